@@ -1,0 +1,240 @@
+/*
+ * mtnlg.h -- C ABI of the MI355X (gfx950) library for one GPU's tensor slice of
+ * an MT-NLG decoder layer and its mixed-precision Adam step.
+ *
+ * What is computed (sources are web pages about MT-NLG 530B; cited by title
+ * and section):
+ *   - A dense left-to-right transformer decoder layer ("Using DeepSpeed and
+ *     Megatron to Train Megatron-Turing NLG 530B", Elamur summary page,
+ *     Summary; jiqizhixin MT-NLG article, model paragraph: 105 layers,
+ *     hidden 20480, 128 heads).
+ *   - Tensor slicing as in the Megatron example of the STRONGHOLD slide deck
+ *     (slides 7-8): the first MLP weight A is split by columns, so slice i
+ *     computes Y_i = GeLU(X A_i) alone; the second weight B is split by rows,
+ *     so slice i produces Z_i = Y_i B_i and the layer output needs the sum of
+ *     the Z_i (operator g: all-reduce forward, identity backward; operator f:
+ *     identity forward, all-reduce backward). Attention is split the same way
+ *     by whole heads: QKV by columns, the output projection by rows.
+ *   - Mixed-precision Adam at about 20 bytes per parameter, with gradients of
+ *     micro-batches accumulated before the step (Elamur summary, Key points).
+ *
+ * Readings where the pages are silent (same as the CPU oracle): pre-LN block,
+ * LayerNorm eps given in the descriptor (1e-5 by default) with biased
+ * variance, exact-erf GeLU, every linear has a bias, row-sliced biases are
+ * added once after the sum, dropout 0, attention scale 1/sqrt(head_dim),
+ * causal mask inside each sequence, QKV columns ordered (q/k/v, local head,
+ * dim).
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers into memory the caller
+ *     allocated (the library never allocates or frees on these paths and keeps
+ *     no mutable global state). Descriptor / config structs and the array of
+ *     partial pointers in mtnlg_reduce_partials are HOST memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; nothing synchronises the host.
+ *   - Layout is row-major. Activations are [batch*seq, width] with rows
+ *     ordered (sequence, position). Weights are in math form [in, out], so a
+ *     linear is Y = X W (+ b).
+ *   - Element type is given by mtnlg_dtype: F32 = IEEE binary32, BF16 =
+ *     bfloat16 bit patterns (uint16). bf16 paths accumulate in fp32 and round
+ *     results to nearest even.
+ *   - Inputs and outputs must not alias. Every device pointer must be 16-byte
+ *     aligned.
+ *   - Errors: arguments are validated on the host BEFORE anything is
+ *     enqueued; a negative mtnlg_status is returned and nothing is launched.
+ *     A failed launch returns MTNLG_ERR_HIP. mtnlg_last_error() gives a
+ *     thread-local text for the last failure. Numerical events (a non-finite
+ *     gradient) are data, not errors.
+ */
+#ifndef MTNLG_H
+#define MTNLG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTNLG_OK = 0,
+  MTNLG_ERR_ARG = -1,          /* null pointer or out-of-range scalar          */
+  MTNLG_ERR_SHAPE = -2,        /* dimensions inconsistent or unsupported        */
+  MTNLG_ERR_DTYPE = -3,        /* unsupported element type                      */
+  MTNLG_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned       */
+  MTNLG_ERR_WORKSPACE = -5,    /* workspace smaller than the size query returns */
+  MTNLG_ERR_HIP = -6,          /* a HIP launch or runtime call failed           */
+  MTNLG_ERR_UNIMPLEMENTED = -7
+} mtnlg_status;
+
+typedef enum { MTNLG_F32 = 0, MTNLG_BF16 = 1 } mtnlg_dtype;
+
+/* The two halves of a layer, each ending in a row-sliced linear whose partial
+ * output feeds an all-reduce (g). */
+typedef enum { MTNLG_ATTN = 0, MTNLG_MLP = 1 } mtnlg_half;
+
+/* Full-layer dimensions plus the slicing factor t (tp_size) and the index of
+ * the slice this call computes (tp_rank). The slice sees heads/tp_size heads
+ * of width hidden/heads and ffn/tp_size MLP columns.
+ * Supported: hidden % heads == 0; heads % tp_size == 0; ffn % tp_size == 0;
+ * 0 <= tp_rank < tp_size; head_dim in {64, 128, 160}; hidden, ffn/tp_size and
+ * batch*seq multiples of 16; seq a multiple of 64; dtype F32 or BF16;
+ * ln_eps > 0. */
+typedef struct {
+  int32_t batch, seq, hidden, heads, ffn;
+  int32_t tp_size, tp_rank;
+  int32_t dtype;       /* mtnlg_dtype */
+  float ln_eps;
+} mtnlg_layer_desc;
+
+/* Parameters of one slice of one half, all in desc->dtype:
+ *   ATTN: ln_g, ln_b = gamma1, beta1 [hidden] (replicated);
+ *         w_in = W_qkv,i [hidden, 3*w] (columns (q/k/v, local head, dim));
+ *         b_in = b_qkv,i [3*w]; w_out = W_o,i [w, hidden]; w = local heads*head_dim
+ *   MLP:  ln_g, ln_b = gamma2, beta2 [hidden]; w_in = A_i [hidden, f];
+ *         b_in = a_i [f]; w_out = B_i [f, hidden]; f = ffn/tp_size
+ * The row-sliced output bias (b_o or b_B) is not here: it is added once, by
+ * the reduction of the partials. */
+typedef struct { const void *ln_g, *ln_b, *w_in, *b_in, *w_out; } mtnlg_half_params;
+
+/* Gradients of one slice of one half, same shapes and dtype as the
+ * parameters; OVERWRITTEN (not accumulated). ln_g and ln_b are this slice's
+ * partial sums (the replicated gamma/beta gradient is their sum over slices);
+ * b_out [hidden] is the gradient of the row-sliced output bias = column sums
+ * of dy, identical on every slice. */
+typedef struct { void *ln_g, *ln_b, *w_in, *b_in, *w_out, *b_out; } mtnlg_half_grads;
+
+/* Size in bytes of the `saved` buffer that layer_fwd fills and layer_bwd
+ * reads for this descriptor and half; 0 if the descriptor is invalid.
+ * Layout (each region starts on a 256-byte boundary, in this order):
+ *   ATTN: ln_out [T, hidden] dtype | mean [T] f32 | rstd [T] f32 |
+ *         qkv [T, 3w] dtype | o [T, w] dtype | lse [local heads, T] f32
+ *   MLP:  ln_out [T, hidden] dtype | mean [T] f32 | rstd [T] f32 |
+ *         u [T, f] dtype (pre-activation) | y [T, f] dtype (GeLU(u))
+ * with T = batch*seq. lse is the natural log of the softmax normaliser of
+ * each query row (scores already scaled by 1/sqrt(head_dim)). */
+size_t mtnlg_saved_bytes(const mtnlg_layer_desc* desc, int32_t half);
+
+/* Size in bytes of the scratch workspace layer_fwd / layer_bwd need for
+ * this descriptor and half (the larger of the two); 0 if invalid. */
+size_t mtnlg_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half);
+
+/* Forward of one slice of one half.
+ *   x          [T, hidden] dtype: the half's input (X for ATTN, X1 for MLP)
+ *   y_partial  [T, hidden] dtype: this slice's row-parallel output WITHOUT
+ *              bias or residual -- ATTN: Attn_i(LN1(x)) W_o,i;
+ *              MLP: GeLU(LN2(x) A_i + a_i) B_i. The caller's reduction adds
+ *              residual + bias + the sum over slices once (on a real
+ *              multi-GPU run this is the g all-reduce).
+ *   saved      mtnlg_saved_bytes(desc, half) bytes, written here.
+ *   ws         mtnlg_workspace_bytes(desc, half) bytes of scratch. */
+int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params,
+                    const void* x, void* y_partial, void* saved, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Backward of one slice of one half for L = <output, dy>.
+ *   x          the same input that was passed to layer_fwd (unchanged)
+ *   saved      what layer_fwd wrote for the same x and params
+ *   dy         [T, hidden] dtype: gradient of the half's output (g's
+ *              backward is the identity, so every slice gets the same dy)
+ *   dx_partial [T, hidden] dtype: this slice's contribution to dL/dx through
+ *              LayerNorm. The caller forms dx = dy + sum of the partials
+ *              (f's backward all-reduce); LayerNorm backward is linear in its
+ *              upstream gradient, so applying it per slice is exact.
+ *   grads      overwritten, see mtnlg_half_grads. */
+int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params,
+                    const void* x, const void* saved, const void* dy, void* dx_partial,
+                    const mtnlg_half_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* out = residual + bias + sum_{j<n} partials[j], summed in fp32 and rounded
+ * once (the g all-reduce, or f's backward, done locally on one device).
+ *   partials   HOST array of n DEVICE pointers, each [rows, cols] dtype; 1 <= n <= 16
+ *   residual   [rows, cols] dtype, nullable (treated as zero)
+ *   bias       [cols] dtype, nullable
+ *   out        [rows, cols] dtype; must not alias the inputs.
+ * cols must be a multiple of 8. */
+int mtnlg_reduce_partials(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials,
+                          int32_t n, const void* residual, const void* bias, void* out,
+                          void* stream);
+
+/* Gradient accumulation over micro-batches (Elamur summary, Key points):
+ * acc[i] = (overwrite ? 0 : acc[i]) + grad[i] for i < n, in fp32.
+ *   grad  [n] dtype (BF16 for the mixed-precision path, F32 allowed)
+ *   acc   [n] f32.  n >= 0 (0 is a no-op). */
+int mtnlg_grad_accumulate(int64_t n, int32_t dtype, const void* grad, float* acc,
+                          int32_t overwrite, void* stream);
+
+/* Adam hyper-parameters of one step. step is the 1-based index of the step
+ * being taken (bias corrections use beta^step). max_grad_norm <= 0 turns
+ * clipping off. inv_loss_scale multiplies the accumulated gradient first. */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay, max_grad_norm, inv_loss_scale;
+  int64_t step;
+} mtnlg_adam_cfg;
+
+/* Scratch bytes mtnlg_adam_step needs for n parameters. */
+size_t mtnlg_adam_workspace_bytes(int64_t n);
+
+/* Fused mixed-precision Adam step over one GPU's flat share of n params:
+ *   g_hat = grad * inv_loss_scale; norm = ||g_hat||_2 over all n;
+ *   found_inf = any non-finite g_hat; coef = max_norm / (norm + 1e-6) if
+ *   that is below 1, else 1. If found_inf, NOTHING is written except
+ *   stats. Otherwise with g = g_hat * coef: p *= (1 - lr*wd) when wd > 0;
+ *   m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ *   p -= lr * (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps);
+ *   w_bf16 = bf16 round-to-nearest-even of p.
+ *   master, m, v [n] f32 (updated in place); grad [n] f32 (the accumulator);
+ *   w_bf16 [n] bf16, nullable (skipped); stats DEVICE f32[3] written with
+ *   {norm, coef, found_inf (0 or 1)}; ws >= mtnlg_adam_workspace_bytes(n).
+ * The whole decision (norm, clip, skip) stays on the device: no host sync. */
+int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v,
+                    const float* grad, void* w_bf16, float* stats, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* ---- Component entry points (the kernels the layer calls, one at a time) ---- */
+
+/* C[M,N] = op(A) op(B) (+ bias[n]) in dtype, fp32 accumulation.
+ *   trans_a = 0: A is [M, K] row-major; 1: A is stored [K, M] (op(A) = A^T).
+ *   trans_b = 0: B is [K, N] row-major; 1: B is stored [N, K] (op(B) = B^T).
+ *   bias nullable. M, N, K >= 1 and multiples of 8. */
+int mtnlg_gemm(int32_t dtype, int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K,
+               const void* A, const void* B, void* C, const void* bias, void* stream);
+
+/* Row LayerNorm of x [rows, cols] (the oracle's layernorm_fwd):
+ * y = gamma*(x-mean)*rstd + beta; mean, rstd [rows] f32. cols multiple of 8. */
+int mtnlg_layernorm_fwd(int32_t dtype, int64_t rows, int64_t cols, const void* x,
+                        const void* gamma, const void* beta, float eps, void* y, float* mean,
+                        float* rstd, void* stream);
+
+/* LayerNorm backward for upstream gradient gy (the oracle's layernorm_bwd):
+ * dx [rows, cols] dtype, dgamma / dbeta [cols] dtype. gy is dtype.
+ * ws >= mtnlg_layernorm_bwd_workspace_bytes(rows, cols). */
+size_t mtnlg_layernorm_bwd_workspace_bytes(int64_t rows, int64_t cols);
+int mtnlg_layernorm_bwd(int32_t dtype, int64_t rows, int64_t cols, const void* gy, const void* x,
+                        const float* mean, const float* rstd, const void* gamma, void* dx,
+                        void* dgamma, void* dbeta, void* ws, size_t ws_bytes, void* stream);
+
+/* Causal attention of `heads` heads of width head_dim over batch sequences
+ * of length seq, reading qkv [batch*seq, 3*heads*head_dim] (columns
+ * (q/k/v, head, dim)) and writing o [batch*seq, heads*head_dim] (columns
+ * (head, dim)) and lse [heads, batch*seq] f32. */
+int mtnlg_attention_fwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads,
+                        int32_t head_dim, const void* qkv, void* o, float* lse, void* stream);
+
+/* Backward of mtnlg_attention_fwd: dqkv [batch*seq, 3*heads*head_dim] from
+ * qkv, o, lse and do_ [batch*seq, heads*head_dim].
+ * ws >= mtnlg_attention_bwd_workspace_bytes(...). */
+size_t mtnlg_attention_bwd_workspace_bytes(int32_t batch, int32_t seq, int32_t heads);
+int mtnlg_attention_bwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads,
+                        int32_t head_dim, const void* qkv, const void* o, const float* lse,
+                        const void* do_, void* dqkv, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* mtnlg_status_str(int32_t status);
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char* mtnlg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTNLG_H */

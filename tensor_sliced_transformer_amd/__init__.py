@@ -1,0 +1,159 @@
+"""MI355X (gfx950) library for one GPU's tensor slice of an MT-NLG decoder layer.
+
+Python binding over the C ABI of ``include/mtnlg.h`` (libmtnlg.so). Every
+function here only marshals arguments: device pointers of torch tensors (torch
+is used for device memory and streams) and the current HIP stream are handed to
+the library, whose hand-written HIP kernels do all the arithmetic. A missing
+library raises on first use; nothing falls back to PyTorch or the CPU.
+
+Tensors: bf16 path -> torch.bfloat16, fp32 path -> torch.float32, all on the
+GPU, contiguous, 16-byte aligned (any fresh torch allocation is).
+"""
+from __future__ import annotations
+
+import ctypes
+from . import _lib
+from ._lib import ATTN, MLP, BF16, F32, AdamCfg, HalfGrads, HalfParams, LayerDesc, MtnlgError, check, load
+
+__all__ = ["ATTN", "MLP", "BF16", "F32", "LayerDesc", "AdamCfg", "MtnlgError", "load", "make_desc",
+           "saved_bytes", "workspace_bytes", "layer_fwd", "layer_bwd", "reduce_partials",
+           "grad_accumulate", "adam_workspace_bytes", "adam_step", "gemm", "layernorm_fwd",
+           "layernorm_bwd_workspace_bytes", "layernorm_bwd", "attention_fwd",
+           "attention_bwd_workspace_bytes", "attention_bwd", "torch_dtype"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype(dtype: int):
+    t = _torch()
+    return t.bfloat16 if dtype == BF16 else t.float32
+
+
+def _code(tensor) -> int:
+    t = _torch()
+    if tensor.dtype == t.bfloat16:
+        return BF16
+    if tensor.dtype == t.float32:
+        return F32
+    raise TypeError(f"unsupported tensor dtype {tensor.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    t = _torch()
+    s = stream if stream is not None else t.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(batch, seq, hidden, heads, ffn, tp_size=1, tp_rank=0, dtype=BF16, ln_eps=1e-5) -> LayerDesc:
+    return LayerDesc(batch, seq, hidden, heads, ffn, tp_size, tp_rank, dtype, ln_eps)
+
+
+def saved_bytes(desc: LayerDesc, half: int) -> int:
+    return int(load().mtnlg_saved_bytes(ctypes.byref(desc), half))
+
+
+def workspace_bytes(desc: LayerDesc, half: int) -> int:
+    return int(load().mtnlg_workspace_bytes(ctypes.byref(desc), half))
+
+
+def _params(p: dict) -> HalfParams:
+    return HalfParams(*(_ptr(p[k]) for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out")))
+
+
+def _grads(g: dict) -> HalfGrads:
+    return HalfGrads(*(_ptr(g[k]) for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out")))
+
+
+def layer_fwd(desc, half, params: dict, x, y_partial, saved, ws=None, stream=None) -> None:
+    """One slice's half forward (mtnlg_layer_fwd); params keys ln_g ln_b w_in b_in w_out."""
+    p = _params(params)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check(load().mtnlg_layer_fwd(ctypes.byref(desc), half, ctypes.byref(p), _ptr(x), _ptr(y_partial),
+                                 _ptr(saved), _ptr(ws), ws_bytes, _stream(stream)), "mtnlg_layer_fwd")
+
+
+def layer_bwd(desc, half, params: dict, x, saved, dy, dx_partial, grads: dict, ws, stream=None) -> None:
+    """One slice's half backward (mtnlg_layer_bwd); grads keys ln_g ln_b w_in b_in w_out b_out."""
+    p = _params(params)
+    g = _grads(grads)
+    check(load().mtnlg_layer_bwd(ctypes.byref(desc), half, ctypes.byref(p), _ptr(x), _ptr(saved), _ptr(dy),
+                                 _ptr(dx_partial), ctypes.byref(g), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "mtnlg_layer_bwd")
+
+
+def reduce_partials(partials, out, residual=None, bias=None, stream=None) -> None:
+    """out = residual + bias + sum(partials) (mtnlg_reduce_partials)."""
+    rows, cols = out.shape
+    arr = (ctypes.c_void_p * len(partials))(*[p.data_ptr() for p in partials])
+    for p in partials:
+        _ptr(p)
+    check(load().mtnlg_reduce_partials(rows, cols, _code(out), arr, len(partials), _ptr(residual), _ptr(bias),
+                                       _ptr(out), _stream(stream)), "mtnlg_reduce_partials")
+
+
+def grad_accumulate(grad, acc, overwrite: bool, stream=None) -> None:
+    check(load().mtnlg_grad_accumulate(grad.numel(), _code(grad), _ptr(grad), _ptr(acc), int(overwrite),
+                                       _stream(stream)), "mtnlg_grad_accumulate")
+
+
+def adam_workspace_bytes(n: int) -> int:
+    return int(load().mtnlg_adam_workspace_bytes(n))
+
+
+def adam_step(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None) -> None:
+    check(load().mtnlg_adam_step(ctypes.byref(cfg), master.numel(), _ptr(master), _ptr(m), _ptr(v), _ptr(grad),
+                                 _ptr(w_bf16), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "mtnlg_adam_step")
+
+
+def gemm(a, b, c, trans_a=False, trans_b=False, bias=None, stream=None) -> None:
+    """c = op(a) op(b) (+ bias) (mtnlg_gemm)."""
+    M, N = c.shape
+    K = a.shape[0] if trans_a else a.shape[1]
+    check(load().mtnlg_gemm(_code(c), int(trans_a), int(trans_b), M, N, K, _ptr(a), _ptr(b), _ptr(c), _ptr(bias),
+                            _stream(stream)), "mtnlg_gemm")
+
+
+def layernorm_fwd(x, gamma, beta, eps, y, mean, rstd, stream=None) -> None:
+    rows, cols = x.shape
+    check(load().mtnlg_layernorm_fwd(_code(x), rows, cols, _ptr(x), _ptr(gamma), _ptr(beta), eps, _ptr(y),
+                                     _ptr(mean), _ptr(rstd), _stream(stream)), "mtnlg_layernorm_fwd")
+
+
+def layernorm_bwd_workspace_bytes(rows: int, cols: int) -> int:
+    return int(load().mtnlg_layernorm_bwd_workspace_bytes(rows, cols))
+
+
+def layernorm_bwd(gy, x, mean, rstd, gamma, dx, dgamma, dbeta, ws, stream=None) -> None:
+    rows, cols = x.shape
+    check(load().mtnlg_layernorm_bwd(_code(x), rows, cols, _ptr(gy), _ptr(x), _ptr(mean), _ptr(rstd), _ptr(gamma),
+                                     _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "mtnlg_layernorm_bwd")
+
+
+def attention_fwd(qkv, o, lse, batch, seq, heads, head_dim, stream=None) -> None:
+    check(load().mtnlg_attention_fwd(_code(qkv), batch, seq, heads, head_dim, _ptr(qkv), _ptr(o), _ptr(lse),
+                                     _stream(stream)), "mtnlg_attention_fwd")
+
+
+def attention_bwd_workspace_bytes(batch, seq, heads) -> int:
+    return int(load().mtnlg_attention_bwd_workspace_bytes(batch, seq, heads))
+
+
+def attention_bwd(qkv, o, lse, do, dqkv, ws, batch, seq, heads, head_dim, stream=None) -> None:
+    check(load().mtnlg_attention_bwd(_code(qkv), batch, seq, heads, head_dim, _ptr(qkv), _ptr(o), _ptr(lse),
+                                     _ptr(do), _ptr(dqkv), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "mtnlg_attention_bwd")

@@ -1,0 +1,508 @@
+// C ABI of the library (include/mtnlg.h): host-side validation, buffer
+// layouts, and the launch sequences of the two halves of a layer slice.
+//
+// The halves follow the tensor-slicing example of the STRONGHOLD slide deck
+// (slides 7-8): the first linear of each half is column-sliced (QKV by whole
+// heads, MLP-up A by columns) and needs no communication; the second is
+// row-sliced (attention output W_o, MLP-down B) and produces a partial that
+// operator g sums across slices. Backward mirrors it: g's backward is the
+// identity (every slice receives the same dy), f's backward sums the slices'
+// input-gradient partials.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/mtnlg.h"
+#include "kernels.hpp"
+
+using namespace mtnlg;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MTNLG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MTNLG_HIP(call, what)                 \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MTNLG_ERR_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MTNLG_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MTNLG_OK;
+}
+
+#define CHECK_PTR(p)                               \
+  do {                                             \
+    int s_ = check_ptr((p), #p);                   \
+    if (s_ != MTNLG_OK) return s_;                 \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dims {
+  int64_t T;      // tokens = batch*seq
+  int64_t h;      // hidden
+  int64_t d;      // head_dim
+  int64_t nhl;    // local heads
+  int64_t w;      // local attention width = nhl*d
+  int64_t fl;     // local MLP width
+  int dtype;
+  size_t eb;      // element bytes
+};
+
+int validate_desc(const mtnlg_layer_desc* desc, int32_t half, Dims* out) {
+  if (!desc) return fail(MTNLG_ERR_ARG, "desc is NULL");
+  if (half != MTNLG_ATTN && half != MTNLG_MLP) return fail(MTNLG_ERR_ARG, "half must be 0 (ATTN) or 1 (MLP)");
+  const mtnlg_layer_desc& D = *desc;
+  if (D.dtype != MTNLG_F32 && D.dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", D.dtype);
+  if (D.batch <= 0 || D.seq <= 0 || D.hidden <= 0 || D.heads <= 0 || D.ffn <= 0 || D.tp_size <= 0)
+    return fail(MTNLG_ERR_SHAPE, "dimensions must be positive");
+  if (D.tp_rank < 0 || D.tp_rank >= D.tp_size)
+    return fail(MTNLG_ERR_ARG, "tp_rank %d outside [0, %d)", D.tp_rank, D.tp_size);
+  if (D.hidden % D.heads) return fail(MTNLG_ERR_SHAPE, "hidden %% heads != 0");
+  if (D.heads % D.tp_size) return fail(MTNLG_ERR_SHAPE, "heads %% tp_size != 0");
+  if (D.ffn % D.tp_size) return fail(MTNLG_ERR_SHAPE, "ffn %% tp_size != 0");
+  const int hd = D.hidden / D.heads;
+  const bool hd_ok = D.dtype == MTNLG_BF16 ? (hd == 64 || hd == 128 || hd == 160) : (hd == 64 || hd == 128);
+  if (!hd_ok) return fail(MTNLG_ERR_SHAPE, "head_dim %d unsupported for this dtype", hd);
+  if (D.hidden % 16 || (D.ffn / D.tp_size) % 16) return fail(MTNLG_ERR_SHAPE, "hidden and ffn/tp must be multiples of 16");
+  if (D.hidden > 32768) return fail(MTNLG_ERR_SHAPE, "hidden > 32768 unsupported");
+  if (D.seq % 128) return fail(MTNLG_ERR_SHAPE, "seq must be a multiple of 128");
+  if (!(D.ln_eps > 0.0f) || !isfinite(D.ln_eps)) return fail(MTNLG_ERR_ARG, "ln_eps must be positive and finite");
+  const int64_t T = (int64_t)D.batch * D.seq;
+  if (T * (int64_t)std::max(D.hidden, D.ffn) > (int64_t)1 << 40) return fail(MTNLG_ERR_SHAPE, "problem too large");
+  if (out) {
+    out->T = T;
+    out->h = D.hidden;
+    out->d = hd;
+    out->nhl = D.heads / D.tp_size;
+    out->w = out->nhl * hd;
+    out->fl = D.ffn / D.tp_size;
+    out->dtype = D.dtype;
+    out->eb = elem_bytes(D.dtype);
+  }
+  return MTNLG_OK;
+}
+
+// ---- saved layout ----
+struct SavedLayout {
+  size_t ln_out, mean, rstd, a, b, c, total;  // ATTN: a=qkv b=o c=lse; MLP: a=u b=y
+};
+
+SavedLayout saved_layout(const Dims& d, int half) {
+  SavedLayout L{};
+  size_t off = 0;
+  L.ln_out = off; off = align256(off + d.T * d.h * d.eb);
+  L.mean = off;   off = align256(off + d.T * sizeof(float));
+  L.rstd = off;   off = align256(off + d.T * sizeof(float));
+  if (half == MTNLG_ATTN) {
+    L.a = off; off = align256(off + d.T * 3 * d.w * d.eb);
+    L.b = off; off = align256(off + d.T * d.w * d.eb);
+    L.c = off; off = align256(off + d.nhl * d.T * sizeof(float));
+  } else {
+    L.a = off; off = align256(off + d.T * d.fl * d.eb);
+    L.b = off; off = align256(off + d.T * d.fl * d.eb);
+    L.c = off;
+  }
+  L.total = off;
+  return L;
+}
+
+// ---- workspace layout (backward; the forward needs none) ----
+struct WsLayout {
+  size_t t1, t2, dln, lnp, cs, split, attn, total;
+  GemmPlan dplan;  // plan of the split-K dgrad (ATTN dO)
+};
+
+WsLayout ws_layout(const Dims& d, int half) {
+  WsLayout L{};
+  size_t off = 0;
+  if (half == MTNLG_ATTN) {
+    L.dplan = plan_gemm(d.dtype, d.T, d.w, d.h, true);
+    L.t1 = off; off = align256(off + d.T * d.w * d.eb);        // dO
+    L.t2 = off; off = align256(off + d.T * 3 * d.w * d.eb);    // dQKV
+    L.split = off; off = align256(off + gemm_workspace_bytes(L.dplan, d.T, d.w));
+    L.attn = off; off = align256(off + attention_bwd_ws(1, (int)d.T, (int)d.nhl));
+  } else {
+    L.t1 = off; off = align256(off + d.T * d.fl * d.eb);       // dU
+    L.t2 = off;
+  }
+  L.dln = off; off = align256(off + d.T * d.h * d.eb);
+  L.lnp = off; off = align256(off + layernorm_bwd_ws(d.T, d.h));
+  L.cs = off;  off = align256(off + colsum_ws(d.T, std::max<int64_t>(d.h, std::max<int64_t>(3 * d.w, d.fl))));
+  L.total = off;
+  return L;
+}
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mtnlg_status_str(int32_t status) {
+  switch (status) {
+    case MTNLG_OK: return "ok";
+    case MTNLG_ERR_ARG: return "invalid argument";
+    case MTNLG_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case MTNLG_ERR_DTYPE: return "unsupported dtype";
+    case MTNLG_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MTNLG_ERR_WORKSPACE: return "workspace too small";
+    case MTNLG_ERR_HIP: return "HIP error";
+    case MTNLG_ERR_UNIMPLEMENTED: return "unimplemented";
+    default: return "unknown status";
+  }
+}
+
+const char* mtnlg_last_error(void) { return g_last_error; }
+
+size_t mtnlg_saved_bytes(const mtnlg_layer_desc* desc, int32_t half) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return saved_layout(d, half).total;
+}
+
+size_t mtnlg_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return ws_layout(d, half).total;
+}
+
+int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
+                    void* y_partial, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  Dims d;
+  int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  (void)ws;
+  (void)ws_bytes;  // the forward needs no scratch
+  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
+  CHECK_PTR(params->ln_g);
+  CHECK_PTR(params->ln_b);
+  CHECK_PTR(params->w_in);
+  CHECK_PTR(params->b_in);
+  CHECK_PTR(params->w_out);
+  CHECK_PTR(x);
+  CHECK_PTR(y_partial);
+  CHECK_PTR(saved);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(d, half);
+  void* ln_out = at(saved, L.ln_out);
+  float* mean = reinterpret_cast<float*>(at(saved, L.mean));
+  float* rstd = reinterpret_cast<float*>(at(saved, L.rstd));
+  MTNLG_HIP(layernorm_fwd(d.dtype, d.T, d.h, x, params->ln_g, params->ln_b, desc->ln_eps, ln_out, mean, rstd, st),
+            "layernorm_fwd");
+  if (half == MTNLG_ATTN) {
+    void* qkv = at(saved, L.a);
+    void* o = at(saved, L.b);
+    float* lse = reinterpret_cast<float*>(at(saved, L.c));
+    const int64_t n3 = 3 * d.w;
+    MTNLG_HIP(gemm(d.dtype, true, false, d.T, n3, d.h, ln_out, d.h, params->w_in, n3, qkv, n3, EPI_BIAS,
+                   params->b_in, nullptr, nullptr, plan_gemm(d.dtype, d.T, n3, d.h, false), nullptr, st),
+              "qkv gemm");
+    MTNLG_HIP(attention_fwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, st),
+              "attention_fwd");
+    MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.w, o, d.w, params->w_out, d.h, y_partial, d.h, EPI_STORE,
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.w, false), nullptr, st),
+              "out-proj gemm");
+  } else {
+    void* u = at(saved, L.a);
+    void* y = at(saved, L.b);
+    MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.fl, d.h, ln_out, d.h, params->w_in, d.fl, u, d.fl, EPI_BIAS_GELU,
+                   params->b_in, y, nullptr, plan_gemm(d.dtype, d.T, d.fl, d.h, false), nullptr, st),
+              "mlp-up gemm");
+    MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.fl, y, d.fl, params->w_out, d.h, y_partial, d.h, EPI_STORE,
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, false), nullptr, st),
+              "mlp-down gemm");
+  }
+  return MTNLG_OK;
+}
+
+int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
+                    const void* saved, const void* dy, void* dx_partial, const mtnlg_half_grads* grads, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  Dims d;
+  int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
+  if (!grads) return fail(MTNLG_ERR_ARG, "grads is NULL");
+  CHECK_PTR(params->ln_g);
+  CHECK_PTR(params->ln_b);
+  CHECK_PTR(params->w_in);
+  CHECK_PTR(params->b_in);
+  CHECK_PTR(params->w_out);
+  CHECK_PTR(grads->ln_g);
+  CHECK_PTR(grads->ln_b);
+  CHECK_PTR(grads->w_in);
+  CHECK_PTR(grads->b_in);
+  CHECK_PTR(grads->w_out);
+  CHECK_PTR(grads->b_out);
+  CHECK_PTR(x);
+  CHECK_PTR(saved);
+  CHECK_PTR(dy);
+  CHECK_PTR(dx_partial);
+  CHECK_PTR(ws);
+  const WsLayout W = ws_layout(d, half);
+  if (ws_bytes < W.total)
+    return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, W.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(d, half);
+  const void* ln_out = at(saved, L.ln_out);
+  const float* mean = reinterpret_cast<const float*>(at(saved, L.mean));
+  const float* rstd = reinterpret_cast<const float*>(at(saved, L.rstd));
+  void* dln = at(ws, W.dln);
+  void* cs = at(ws, W.cs);
+
+  MTNLG_HIP(colsum(d.dtype, d.T, d.h, dy, grads->b_out, cs, st), "b_out colsum");
+  if (half == MTNLG_MLP) {
+    const void* u = at(saved, L.a);
+    const void* y = at(saved, L.b);
+    void* du = at(ws, W.t1);
+    // dU = (dy B^T) * GeLU'(u)
+    MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.fl, d.h, dy, d.h, params->w_out, d.h, du, d.fl, EPI_GELU_GRAD,
+                   nullptr, nullptr, u, plan_gemm(d.dtype, d.T, d.fl, d.h, false), nullptr, st),
+              "mlp dY gemm");
+    // dB = Y^T dy
+    MTNLG_HIP(gemm(d.dtype, false, false, d.fl, d.h, d.T, y, d.fl, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
+                   nullptr, nullptr, plan_gemm(d.dtype, d.fl, d.h, d.T, false), nullptr, st),
+              "mlp dB gemm");
+    MTNLG_HIP(colsum(d.dtype, d.T, d.fl, du, grads->b_in, cs, st), "mlp da colsum");
+    // dA = LN2(x)^T dU
+    MTNLG_HIP(gemm(d.dtype, false, false, d.h, d.fl, d.T, ln_out, d.h, du, d.fl, grads->w_in, d.fl, EPI_STORE,
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, d.fl, d.T, false), nullptr, st),
+              "mlp dA gemm");
+    // dLN = dU A^T
+    MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.h, d.fl, du, d.fl, params->w_in, d.fl, dln, d.h, EPI_STORE, nullptr,
+                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, false), nullptr, st),
+              "mlp dX gemm");
+  } else {
+    const void* qkv = at(saved, L.a);
+    const void* o = at(saved, L.b);
+    const float* lse = reinterpret_cast<const float*>(at(saved, L.c));
+    void* dO = at(ws, W.t1);
+    void* dqkv = at(ws, W.t2);
+    const int64_t n3 = 3 * d.w;
+    // dO = dy W_o^T (short N: split K)
+    MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.w, d.h, dy, d.h, params->w_out, d.h, dO, d.w, EPI_STORE, nullptr,
+                   nullptr, nullptr, W.dplan, at(ws, W.split), st),
+              "attn dO gemm");
+    // dW_o = O^T dy
+    MTNLG_HIP(gemm(d.dtype, false, false, d.w, d.h, d.T, o, d.w, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
+                   nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, d.T, false), nullptr, st),
+              "attn dWo gemm");
+    MTNLG_HIP(attention_bwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, dO, dqkv,
+                            at(ws, W.attn), st),
+              "attention_bwd");
+    MTNLG_HIP(colsum(d.dtype, d.T, n3, dqkv, grads->b_in, cs, st), "attn dbqkv colsum");
+    // dW_qkv = LN1(x)^T dQKV
+    MTNLG_HIP(gemm(d.dtype, false, false, d.h, n3, d.T, ln_out, d.h, dqkv, n3, grads->w_in, n3, EPI_STORE, nullptr,
+                   nullptr, nullptr, plan_gemm(d.dtype, d.h, n3, d.T, false), nullptr, st),
+              "attn dWqkv gemm");
+    // dLN = dQKV W_qkv^T
+    MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.h, n3, dqkv, n3, params->w_in, n3, dln, d.h, EPI_STORE, nullptr,
+                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, n3, false), nullptr, st),
+              "attn dX gemm");
+  }
+  MTNLG_HIP(layernorm_bwd(d.dtype, d.dtype, d.T, d.h, dln, x, mean, rstd, params->ln_g, dx_partial, grads->ln_g,
+                          grads->ln_b, at(ws, W.lnp), st),
+            "layernorm_bwd");
+  return MTNLG_OK;
+}
+
+int mtnlg_reduce_partials(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials, int32_t n,
+                          const void* residual, const void* bias, void* out, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (rows < 0 || cols <= 0 || cols % 8) return fail(MTNLG_ERR_SHAPE, "rows >= 0 and cols a positive multiple of 8");
+  if (n < 1 || n > kMaxPartials) return fail(MTNLG_ERR_ARG, "n must be in [1, %d]", kMaxPartials);
+  if (!partials) return fail(MTNLG_ERR_ARG, "partials is NULL");
+  for (int j = 0; j < n; ++j) {
+    int st = check_ptr(partials[j], "partials[j]");
+    if (st != MTNLG_OK) return st;
+  }
+  if (residual) CHECK_PTR(residual);
+  if (bias) CHECK_PTR(bias);
+  CHECK_PTR(out);
+  MTNLG_HIP(reduce_partials(dtype, rows, cols, partials, n, residual, bias, out, static_cast<hipStream_t>(stream)),
+            "reduce_partials");
+  return MTNLG_OK;
+}
+
+int mtnlg_grad_accumulate(int64_t n, int32_t dtype, const void* grad, float* acc, int32_t overwrite, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (n < 0) return fail(MTNLG_ERR_SHAPE, "n < 0");
+  if (n == 0) return MTNLG_OK;
+  CHECK_PTR(grad);
+  CHECK_PTR(acc);
+  MTNLG_HIP(grad_accumulate(n, dtype, grad, acc, overwrite != 0, static_cast<hipStream_t>(stream)),
+            "grad_accumulate");
+  return MTNLG_OK;
+}
+
+size_t mtnlg_adam_workspace_bytes(int64_t n) { return n < 0 ? 0 : adam_ws(n); }
+
+int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
+                    void* w_bf16, float* stats, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!cfg) return fail(MTNLG_ERR_ARG, "cfg is NULL");
+  if (n < 0) return fail(MTNLG_ERR_SHAPE, "n < 0");
+  if (cfg->step < 1) return fail(MTNLG_ERR_ARG, "step must be >= 1");
+  if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f) || !(cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f))
+    return fail(MTNLG_ERR_ARG, "betas must be in [0, 1)");
+  if (!(cfg->eps > 0.0f) || !(cfg->lr >= 0.0f) || !(cfg->weight_decay >= 0.0f) || !isfinite(cfg->inv_loss_scale))
+    return fail(MTNLG_ERR_ARG, "eps > 0, lr >= 0, weight_decay >= 0 and a finite inv_loss_scale are required");
+  CHECK_PTR(master);
+  CHECK_PTR(m);
+  CHECK_PTR(v);
+  CHECK_PTR(grad);
+  CHECK_PTR(stats);
+  CHECK_PTR(ws);
+  if (w_bf16) CHECK_PTR(w_bf16);
+  if (ws_bytes < adam_ws(n)) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, adam_ws(n));
+  AdamScalars c{};
+  c.lr = cfg->lr;
+  c.beta1 = cfg->beta1;
+  c.beta2 = cfg->beta2;
+  c.eps = cfg->eps;
+  c.weight_decay = cfg->weight_decay;
+  c.max_grad_norm = cfg->max_grad_norm;
+  c.inv_loss_scale = cfg->inv_loss_scale;
+  c.inv_bc1 = (float)(1.0 / (1.0 - pow((double)cfg->beta1, (double)cfg->step)));
+  c.inv_bc2 = (float)(1.0 / (1.0 - pow((double)cfg->beta2, (double)cfg->step)));
+  MTNLG_HIP(adam_step(c, n, master, m, v, grad, w_bf16, stats, ws, static_cast<hipStream_t>(stream)), "adam_step");
+  return MTNLG_OK;
+}
+
+int mtnlg_gemm(int32_t dtype, int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, const void* A,
+               const void* B, void* C, const void* bias, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (M < 8 || N < 8 || K < 8 || M % 8 || N % 8 || K % 8 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
+    return fail(MTNLG_ERR_SHAPE, "M, N, K must be positive multiples of 8");
+  CHECK_PTR(A);
+  CHECK_PTR(B);
+  CHECK_PTR(C);
+  if (bias) CHECK_PTR(bias);
+  const bool a_kc = trans_a == 0, b_kc = trans_b != 0;
+  const int64_t lda = a_kc ? K : M;
+  const int64_t ldb = b_kc ? K : N;
+  MTNLG_HIP(gemm(dtype, a_kc, b_kc, M, N, K, A, lda, B, ldb, C, N, bias ? EPI_BIAS : EPI_STORE, bias, nullptr,
+                 nullptr, plan_gemm(dtype, M, N, K, false), nullptr, static_cast<hipStream_t>(stream)),
+            "gemm");
+  return MTNLG_OK;
+}
+
+int mtnlg_layernorm_fwd(int32_t dtype, int64_t rows, int64_t cols, const void* x, const void* gamma,
+                        const void* beta, float eps, void* y, float* mean, float* rstd, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (rows < 0 || cols < 8 || cols % 8 || cols > 32768) return fail(MTNLG_ERR_SHAPE, "bad rows/cols");
+  if (!(eps > 0.0f)) return fail(MTNLG_ERR_ARG, "eps must be positive");
+  if (rows == 0) return MTNLG_OK;
+  CHECK_PTR(x);
+  CHECK_PTR(gamma);
+  CHECK_PTR(beta);
+  CHECK_PTR(y);
+  CHECK_PTR(mean);
+  CHECK_PTR(rstd);
+  MTNLG_HIP(layernorm_fwd(dtype, rows, cols, x, gamma, beta, eps, y, mean, rstd, static_cast<hipStream_t>(stream)),
+            "layernorm_fwd");
+  return MTNLG_OK;
+}
+
+size_t mtnlg_layernorm_bwd_workspace_bytes(int64_t rows, int64_t cols) {
+  return rows <= 0 || cols <= 0 ? 0 : layernorm_bwd_ws(rows, cols);
+}
+
+int mtnlg_layernorm_bwd(int32_t dtype, int64_t rows, int64_t cols, const void* gy, const void* x, const float* mean,
+                        const float* rstd, const void* gamma, void* dx, void* dgamma, void* dbeta, void* ws,
+                        size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (rows <= 0 || cols < 8 || cols % 8 || cols > 32768) return fail(MTNLG_ERR_SHAPE, "bad rows/cols");
+  CHECK_PTR(gy);
+  CHECK_PTR(x);
+  CHECK_PTR(mean);
+  CHECK_PTR(rstd);
+  CHECK_PTR(gamma);
+  CHECK_PTR(dx);
+  CHECK_PTR(dgamma);
+  CHECK_PTR(dbeta);
+  CHECK_PTR(ws);
+  if (ws_bytes < layernorm_bwd_ws(rows, cols)) return fail(MTNLG_ERR_WORKSPACE, "workspace too small");
+  MTNLG_HIP(layernorm_bwd(dtype, dtype, rows, cols, gy, x, mean, rstd, gamma, dx, dgamma, dbeta, ws,
+                          static_cast<hipStream_t>(stream)),
+            "layernorm_bwd");
+  return MTNLG_OK;
+}
+
+static int validate_attn(int32_t dtype, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim) {
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (batch <= 0 || seq <= 0 || heads <= 0) return fail(MTNLG_ERR_SHAPE, "dimensions must be positive");
+  if (seq % 128) return fail(MTNLG_ERR_SHAPE, "seq must be a multiple of 128");
+  const bool ok = dtype == MTNLG_BF16 ? (head_dim == 64 || head_dim == 128 || head_dim == 160)
+                                      : (head_dim == 64 || head_dim == 128);
+  if (!ok) return fail(MTNLG_ERR_SHAPE, "head_dim %d unsupported", head_dim);
+  return MTNLG_OK;
+}
+
+int mtnlg_attention_fwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim, const void* qkv,
+                        void* o, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  int s = validate_attn(dtype, batch, seq, heads, head_dim);
+  if (s != MTNLG_OK) return s;
+  CHECK_PTR(qkv);
+  CHECK_PTR(o);
+  CHECK_PTR(lse);
+  MTNLG_HIP(attention_fwd(dtype, batch, seq, heads, head_dim, qkv, o, lse, static_cast<hipStream_t>(stream)),
+            "attention_fwd");
+  return MTNLG_OK;
+}
+
+size_t mtnlg_attention_bwd_workspace_bytes(int32_t batch, int32_t seq, int32_t heads) {
+  return batch <= 0 || seq <= 0 || heads <= 0 ? 0 : attention_bwd_ws(batch, seq, heads);
+}
+
+int mtnlg_attention_bwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads, int32_t head_dim, const void* qkv,
+                        const void* o, const float* lse, const void* do_, void* dqkv, void* ws, size_t ws_bytes,
+                        void* stream) {
+  g_last_error[0] = 0;
+  int s = validate_attn(dtype, batch, seq, heads, head_dim);
+  if (s != MTNLG_OK) return s;
+  CHECK_PTR(qkv);
+  CHECK_PTR(o);
+  CHECK_PTR(lse);
+  CHECK_PTR(do_);
+  CHECK_PTR(dqkv);
+  CHECK_PTR(ws);
+  if (ws_bytes < attention_bwd_ws(batch, seq, heads)) return fail(MTNLG_ERR_WORKSPACE, "workspace too small");
+  MTNLG_HIP(attention_bwd(dtype, batch, seq, heads, head_dim, qkv, o, lse, do_, dqkv, ws,
+                          static_cast<hipStream_t>(stream)),
+            "attention_bwd");
+  return MTNLG_OK;
+}
+
+}  // extern "C"

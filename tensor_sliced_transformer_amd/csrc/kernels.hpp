@@ -1,0 +1,87 @@
+// Internal host-side launchers of the gfx950 kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mtnlg {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+inline size_t elem_bytes(int dtype) { return dtype == kBF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- GEMM
+enum GemmEpi {
+  EPI_STORE = 0,       // C = acc
+  EPI_BIAS = 1,        // C = acc + bias[n]
+  EPI_BIAS_GELU = 2,   // C = u = acc + bias[n]; C2 = GeLU(u)
+  EPI_GELU_GRAD = 3,   // C = acc * GeLU'(aux[m, n])
+  EPI_F32_PARTIAL = 4  // fp32 split-K partial (internal)
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  const void* bias;
+  void* C2;
+  const void* aux;
+  int epi;
+  int tiles_m, tiles_n;
+  int splits, k_chunk;
+};
+
+struct GemmPlan {
+  int bm = 256, bn = 256, bk = 64, splits = 1;
+};
+
+GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split);
+size_t gemm_workspace_bytes(const GemmPlan& pl, int64_t M, int64_t N);
+// a_kc: A element (m,k) at A[m*lda+k] (else A[k*lda+m]);
+// b_kc: B element (k,n) at B[n*ldb+k] (else B[k*ldb+n]).
+hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, const void* A,
+                int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int epi,
+                const void* bias, void* C2, const void* aux, const GemmPlan& pl, void* ws,
+                hipStream_t st);
+
+// ---------------------------------------------------------------- LayerNorm
+hipError_t layernorm_fwd(int dtype, int64_t rows, int64_t cols, const void* x, const void* gamma,
+                         const void* beta, float eps, void* y, float* mean, float* rstd,
+                         hipStream_t st);
+size_t layernorm_bwd_ws(int64_t rows, int64_t cols);
+// gy_dtype: element type of gy (may differ from dtype: fp32 upstream in the bf16 path).
+hipError_t layernorm_bwd(int dtype, int gy_dtype, int64_t rows, int64_t cols, const void* gy,
+                         const void* x, const float* mean, const float* rstd, const void* gamma,
+                         void* dx, void* dgamma, void* dbeta, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+hipError_t attention_fwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv,
+                         void* o, float* lse, hipStream_t st);
+size_t attention_bwd_ws(int batch, int seq, int heads);
+hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv,
+                         const void* o, const float* lse, const void* dout, void* dqkv, void* ws,
+                         hipStream_t st);
+
+// ---------------------------------------------------------------- streaming
+constexpr int kMaxPartials = 16;
+hipError_t reduce_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int n,
+                           const void* residual, const void* bias, void* out, hipStream_t st);
+size_t colsum_ws(int64_t rows, int64_t cols);
+// out[c] = sum_r x[r, c] (x dtype, out dtype), two-stage deterministic.
+hipError_t colsum(int dtype, int64_t rows, int64_t cols, const void* x, void* out, void* ws,
+                  hipStream_t st);
+hipError_t grad_accumulate(int64_t n, int dtype, const void* grad, float* acc, bool overwrite,
+                           hipStream_t st);
+size_t adam_ws(int64_t n);
+struct AdamScalars {
+  float lr, beta1, beta2, eps, weight_decay, max_grad_norm, inv_loss_scale;
+  float inv_bc1, inv_bc2;  // 1/(1-beta1^t), 1/(1-beta2^t)
+};
+hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v,
+                     const float* grad, void* w_bf16, float* stats, void* ws, hipStream_t st);
+
+}  // namespace mtnlg

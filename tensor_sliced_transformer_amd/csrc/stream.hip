@@ -1,0 +1,247 @@
+// HBM-streaming kernels (gfx950): the local sum of slice partials, fp32
+// gradient accumulation, and the fused mixed-precision Adam step.
+//
+// * Partial sum (operator g's forward / f's backward of the tensor-slicing
+//   example in the STRONGHOLD slides, done on one device):
+//   out = residual + bias + sum of partials, fp32 sum, one rounding.
+// * Gradient accumulation over micro-batches (Elamur summary of the MT-NLG
+//   paper, Key points): acc = (overwrite ? 0 : acc) + grad.
+// * Adam over the flat share (same page: about 20 bytes per parameter with
+//   mixed precision): (1) per-workgroup partial sums of the squared unscaled
+//   gradient in fp64 plus a non-finite flag, (2) a one-workgroup finish in
+//   fixed order that writes {norm, clip coef, found_inf} to device memory,
+//   (3) the update, which reads those scalars itself and leaves every buffer
+//   untouched when found_inf is set -- the host never waits.
+// Grid-stride loops over 16-byte vectors with a fixed grid; all pointers are
+// 16-byte aligned (checked on the host) and the ragged tail is done per element.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtnlg {
+
+namespace {
+
+constexpr int kStreamThreads = 256;
+
+int stream_grid(int64_t units) {
+  const int64_t max_blocks = 256 * 8;  // 8 workgroups per CU
+  int64_t b = (units + kStreamThreads - 1) / kStreamThreads;
+  return (int)(b < 1 ? 1 : (b > max_blocks ? max_blocks : b));
+}
+
+struct PartialPtrs {
+  const void* p[kMaxPartials];
+};
+
+template <typename T>
+__global__ __launch_bounds__(kStreamThreads) void reduce_partials_kernel(PartialPtrs parts, int n, int64_t total,
+                                                                         int64_t cols, const T* __restrict__ residual,
+                                                                         const T* __restrict__ bias,
+                                                                         T* __restrict__ out) {
+  const int64_t units = total / 8;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = u * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (residual) load8(residual + i, acc);
+    for (int j = 0; j < n; ++j) {
+      float v[8];
+      load8(static_cast<const T*>(parts.p[j]) + i, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    }
+    if (bias) {
+      float b[8];
+      load8(bias + (i % cols), b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += b[e];
+    }
+    store8(out + i, acc);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, const T* __restrict__ g,
+                                                                  float* __restrict__ acc, int overwrite) {
+  const int64_t units = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t u = t0; u < units; u += stride) {
+    const int64_t i = u * 8;
+    float v[8], a[8];
+    load8(g + i, v);
+    if (!overwrite) {
+      load8(acc + i, a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += a[e];
+    }
+    store8(acc + i, v);
+  }
+  for (int64_t i = units * 8 + t0; i < n; i += stride) {
+    const float v = Elem<T>::to_f(g[i]);
+    acc[i] = overwrite ? v : acc[i] + v;
+  }
+}
+
+// (1) partial sums of (grad * s)^2 in fp64 and a non-finite flag per workgroup
+__global__ __launch_bounds__(kStreamThreads) void adam_norm_kernel(int64_t n, const float* __restrict__ grad,
+                                                                   float s, double* __restrict__ part,
+                                                                   int* __restrict__ flag) {
+  __shared__ double red[kStreamThreads / kWave];
+  __shared__ int bad_any;
+  if (threadIdx.x == 0) bad_any = 0;
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = n / 4;
+  double acc = 0.0;
+  int bad = 0;
+  for (int64_t u = t0; u < n4; u += stride) {
+    const float4 g = reinterpret_cast<const float4*>(grad)[u];
+    const float a = g.x * s, b = g.y * s, c = g.z * s, d = g.w * s;
+    bad |= !isfinite(a) | !isfinite(b) | !isfinite(c) | !isfinite(d);
+    acc += (double)a * a + (double)b * b + (double)c * c + (double)d * d;
+  }
+  for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
+    const float a = grad[i] * s;
+    bad |= !isfinite(a);
+    acc += (double)a * a;
+  }
+  if (bad) bad_any = 1;  // benign race: every writer stores 1
+  const double tot = block_sum<kStreamThreads>(acc, red);
+  if (threadIdx.x == 0) {
+    part[blockIdx.x] = tot;
+    flag[blockIdx.x] = bad_any;
+  }
+}
+
+// (2) one workgroup: fixed-order sum of the partials -> stats {norm, coef, found_inf}
+__global__ __launch_bounds__(kStreamThreads) void adam_finish_kernel(const double* __restrict__ part,
+                                                                     const int* __restrict__ flag, int nparts,
+                                                                     float max_norm, float* __restrict__ stats) {
+  __shared__ double red[kStreamThreads / kWave];
+  __shared__ int bad_any;
+  if (threadIdx.x == 0) bad_any = 0;
+  __syncthreads();
+  double acc = 0.0;
+  int bad = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) {
+    acc += part[i];
+    bad |= flag[i];
+  }
+  if (bad) bad_any = 1;
+  const double tot = block_sum<kStreamThreads>(acc, red);
+  if (threadIdx.x == 0) {
+    const int found_inf = bad_any || !isfinite(tot);
+    const double norm = sqrt(tot);
+    double coef = 1.0;
+    if (max_norm > 0.0f) {
+      const double c = (double)max_norm / (norm + 1e-6);
+      if (c < 1.0) coef = c;
+    }
+    stats[0] = found_inf ? __builtin_nanf("") : (float)norm;
+    stats[1] = found_inf ? 1.0f : (float)coef;
+    stats[2] = found_inf ? 1.0f : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void adam_one(float& p, float& m, float& v, float g, const AdamScalars& c) {
+  if (c.weight_decay > 0.0f) p *= 1.0f - c.lr * c.weight_decay;
+  m = c.beta1 * m + (1.0f - c.beta1) * g;
+  v = c.beta2 * v + (1.0f - c.beta2) * g * g;
+  const float mhat = m * c.inv_bc1;
+  const float vhat = v * c.inv_bc2;
+  p -= c.lr * mhat / (sqrtf(vhat) + c.eps);
+}
+
+// (3) the update; reads found_inf and coef written by (2) on the same stream
+__global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars c, int64_t n,
+                                                                     float* __restrict__ master, float* __restrict__ m,
+                                                                     float* __restrict__ v,
+                                                                     const float* __restrict__ grad,
+                                                                     bf16_t* __restrict__ w,
+                                                                     const float* __restrict__ stats) {
+  if (stats[2] != 0.0f) return;
+  const float gs = c.inv_loss_scale * stats[1];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = n / 4;
+  for (int64_t u = t0; u < n4; u += stride) {
+    float4 p = reinterpret_cast<float4*>(master)[u];
+    float4 mm = reinterpret_cast<float4*>(m)[u];
+    float4 vv = reinterpret_cast<float4*>(v)[u];
+    const float4 g = reinterpret_cast<const float4*>(grad)[u];
+    adam_one(p.x, mm.x, vv.x, g.x * gs, c);
+    adam_one(p.y, mm.y, vv.y, g.y * gs, c);
+    adam_one(p.z, mm.z, vv.z, g.z * gs, c);
+    adam_one(p.w, mm.w, vv.w, g.w * gs, c);
+    reinterpret_cast<float4*>(master)[u] = p;
+    reinterpret_cast<float4*>(m)[u] = mm;
+    reinterpret_cast<float4*>(v)[u] = vv;
+    if (w) reinterpret_cast<uint2*>(w)[u] = make_uint2(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w));
+  }
+  for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
+    float p = master[i], mm = m[i], vv = v[i];
+    adam_one(p, mm, vv, grad[i] * gs, c);
+    master[i] = p;
+    m[i] = mm;
+    v[i] = vv;
+    if (w) w[i] = f2bf(p);
+  }
+}
+
+constexpr int kNormBlocks = 2048;
+
+}  // namespace
+
+hipError_t reduce_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int n,
+                           const void* residual, const void* bias, void* out, hipStream_t st) {
+  const int64_t total = rows * cols;
+  if (total == 0) return hipSuccess;
+  PartialPtrs pp{};
+  for (int j = 0; j < n; ++j) pp.p[j] = parts[j];
+  const int grid = stream_grid(total / 8);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, pp, n, total, cols,
+                       static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(bias),
+                       static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(grid), dim3(kStreamThreads), 0, st, pp, n, total, cols,
+                       static_cast<const float*>(residual), static_cast<const float*>(bias),
+                       static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t grad_accumulate(int64_t n, int dtype, const void* grad, float* acc, bool overwrite, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int grid = stream_grid(n / 8 + 1);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(grad_acc_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, n,
+                       static_cast<const bf16_t*>(grad), acc, (int)overwrite);
+  else
+    hipLaunchKernelGGL(grad_acc_kernel<float>, dim3(grid), dim3(kStreamThreads), 0, st, n,
+                       static_cast<const float*>(grad), acc, (int)overwrite);
+  return hipGetLastError();
+}
+
+size_t adam_ws(int64_t) { return (size_t)kNormBlocks * (sizeof(double) + sizeof(int)); }
+
+hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                     void* w_bf16, float* stats, void* ws, hipStream_t st) {
+  double* part = static_cast<double*>(ws);
+  int* flag = reinterpret_cast<int*>(part + kNormBlocks);
+  const int nb = n == 0 ? 1 : std::min<int>(kNormBlocks, stream_grid(n / 4 + 1));
+  hipLaunchKernelGGL(adam_norm_kernel, dim3(nb), dim3(kStreamThreads), 0, st, n, grad, c.inv_loss_scale, part,
+                     flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(adam_finish_kernel, dim3(1), dim3(kStreamThreads), 0, st, part, flag, nb, c.max_grad_norm,
+                     stats);
+  e = hipGetLastError();
+  if (e != hipSuccess || n == 0) return e;
+  const int grid = stream_grid(n / 4 + 1);
+  hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
+                     static_cast<bf16_t*>(w_bf16), stats);
+  return hipGetLastError();
+}
+
+}  // namespace mtnlg

@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI that need no GPU: the built library loads, it
+exports every function include/mtnlg.h declares, size queries follow the
+documented layouts, and invalid arguments are rejected before any launch.
+
+Only validation paths are called here (they return before touching HIP); no
+test passes a fake pointer to a path that would launch a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_sliced_transformer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtnlg.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libmtnlg.so not built (python -m tensor_sliced_transformer_amd.build)")
+
+A = 1 << 20          # a fake, 16-byte aligned, non-null address (never dereferenced)
+ODD = A + 4          # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtnlg_[a-z_0-9]+)\s*\(", text)))
+
+
+def lib():
+    return _lib.load()
+
+
+def desc(**kw):
+    d = dict(batch=1, seq=2048, hidden=20480, heads=128, ffn=81920, tp_size=8, tp_rank=0, dtype=_lib.BF16,
+             ln_eps=1e-5)
+    d.update(kw)
+    return _lib.LayerDesc(**d)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 17
+    missing = [n for n in names if not hasattr(lib(), n)]
+    assert not missing, missing
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    L = lib()
+    for code in _lib.STATUS:
+        assert L.mtnlg_status_str(code)
+    assert L.mtnlg_status_str(12345) == b"unknown status"
+
+
+def align256(x):
+    return (x + 255) & ~255
+
+
+def test_saved_bytes_mtnlg_shard():
+    """ATTN: ln_out | mean | rstd | qkv | o | lse; MLP: ln_out | mean | rstd | u | y (256-byte aligned)."""
+    L = lib()
+    T, h, w, f, nh = 2048, 20480, 2560, 10240, 16
+    d = desc()
+    attn = 0
+    for nbytes in (T * h * 2, T * 4, T * 4, T * 3 * w * 2, T * w * 2, nh * T * 4):
+        attn = align256(attn + nbytes)
+    mlp = 0
+    for nbytes in (T * h * 2, T * 4, T * 4, T * f * 2, T * f * 2):
+        mlp = align256(mlp + nbytes)
+    assert L.mtnlg_saved_bytes(ctypes.byref(d), _lib.ATTN) == attn
+    assert L.mtnlg_saved_bytes(ctypes.byref(d), _lib.MLP) == mlp
+    assert L.mtnlg_workspace_bytes(ctypes.byref(d), _lib.ATTN) > T * h * 2
+    assert L.mtnlg_workspace_bytes(ctypes.byref(d), _lib.MLP) > T * h * 2
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(dtype=7), -3),
+    (dict(tp_rank=8), -1),
+    (dict(tp_rank=-1), -1),
+    (dict(heads=100), -2),           # hidden % heads
+    (dict(heads=128, tp_size=3), -2),
+    (dict(hidden=20480, heads=80), -2),   # head_dim 256 unsupported
+    (dict(seq=100), -2),
+    (dict(ln_eps=0.0), -1),
+    (dict(batch=0), -2),
+])
+def test_invalid_descriptor_rejected(bad, status):
+    L = lib()
+    d = desc(**bad)
+    assert L.mtnlg_saved_bytes(ctypes.byref(d), _lib.ATTN) == 0
+    p = _lib.HalfParams(A, A, A, A, A)
+    st = L.mtnlg_layer_fwd(ctypes.byref(d), _lib.ATTN, ctypes.byref(p), A, A, A, None, 0, None)
+    assert st == status, L.mtnlg_last_error()
+    assert L.mtnlg_last_error()
+
+
+def test_null_and_misaligned_pointers():
+    L = lib()
+    d = desc()
+    p = _lib.HalfParams(A, A, None, A, A)
+    assert L.mtnlg_layer_fwd(ctypes.byref(d), _lib.MLP, ctypes.byref(p), A, A, A, None, 0, None) == -1
+    assert b"w_in" in L.mtnlg_last_error()
+    p = _lib.HalfParams(A, A, ODD, A, A)
+    assert L.mtnlg_layer_fwd(ctypes.byref(d), _lib.MLP, ctypes.byref(p), A, A, A, None, 0, None) == -4
+    assert L.mtnlg_layer_fwd(None, _lib.MLP, ctypes.byref(p), A, A, A, None, 0, None) == -1
+    assert L.mtnlg_layer_fwd(ctypes.byref(d), 2, ctypes.byref(p), A, A, A, None, 0, None) == -1
+
+
+def test_small_workspace_rejected():
+    L = lib()
+    d = desc()
+    p = _lib.HalfParams(A, A, A, A, A)
+    g = _lib.HalfGrads(A, A, A, A, A, A)
+    need = L.mtnlg_workspace_bytes(ctypes.byref(d), _lib.ATTN)
+    st = L.mtnlg_layer_bwd(ctypes.byref(d), _lib.ATTN, ctypes.byref(p), A, A, A, A, ctypes.byref(g), A,
+                           need - 1, None)
+    assert st == -5
+    g2 = _lib.HalfGrads(A, A, A, None, A, A)
+    st = L.mtnlg_layer_bwd(ctypes.byref(d), _lib.ATTN, ctypes.byref(p), A, A, A, A, ctypes.byref(g2), A,
+                           need, None)
+    assert st == -1
+
+
+def test_other_entry_points_validate():
+    L = lib()
+    arr = (ctypes.c_void_p * 2)(A, A)
+    assert L.mtnlg_reduce_partials(4, 12, _lib.BF16, arr, 2, None, None, A, None) == -2      # cols % 8
+    assert L.mtnlg_reduce_partials(4, 16, _lib.BF16, arr, 0, None, None, A, None) == -1      # n
+    assert L.mtnlg_reduce_partials(4, 16, _lib.BF16, arr, 17, None, None, A, None) == -1
+    assert L.mtnlg_reduce_partials(4, 16, 5, arr, 2, None, None, A, None) == -3
+    assert L.mtnlg_grad_accumulate(-1, _lib.BF16, A, A, 1, None) == -2
+    assert L.mtnlg_grad_accumulate(0, _lib.BF16, None, None, 1, None) == 0                   # empty: no-op
+    assert L.mtnlg_grad_accumulate(16, _lib.BF16, ODD, A, 1, None) == -4
+    cfg = _lib.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 0)
+    assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 1 << 20, None) == -1   # step 0
+    cfg = _lib.AdamCfg(1e-4, 1.0, 0.95, 1e-8, 0.0, 1.0, 1.0, 1)
+    assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 1 << 20, None) == -1   # beta1
+    cfg = _lib.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 1)
+    assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 8, None) == -5
+    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 12, 16, 16, A, A, A, None, None) == -2
+    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 16, 16, 16, None, A, A, None, None) == -1
+    assert L.mtnlg_layernorm_fwd(_lib.BF16, 4, 12, A, A, A, 1e-5, A, A, A, None) == -2
+    assert L.mtnlg_attention_fwd(_lib.F32, 1, 128, 2, 160, A, A, A, None) == -2               # f32 hd 160
+    assert L.mtnlg_attention_fwd(_lib.BF16, 1, 96, 2, 128, A, A, A, None) == -2
+    assert L.mtnlg_attention_bwd(_lib.BF16, 1, 128, 2, 128, A, A, A, A, A, A, 0, None) == -5

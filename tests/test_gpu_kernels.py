@@ -1,0 +1,219 @@
+"""GPU parity of the library's component entry points against the CPU oracle.
+
+Each entry point of include/mtnlg.h is called through the C ABI on seeded
+inputs that span several tiles and a ragged tail, and compared element by
+element with the oracle (float64) on the same bf16-exact or fp32 values.
+"""
+import numpy as np
+import pytest
+
+from helpers import TOL, assert_close, empty, empty_bytes, rel_inf, to_gpu, to_np
+from oracle import adam as OA
+from oracle import layer as OL
+from synth.inputs import randn, round_f32_to_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import tensor_sliced_transformer_amd as tst  # noqa: E402
+
+
+def inputs(seed, shape, dtype, std=1.0, mean=0.0):
+    x = randn(seed, shape, std, mean)
+    return round_f32_to_bf16(x) if dtype == "bf16" else x
+
+
+# ------------------------------------------------------------------ GEMM
+GEMM_SHAPES = [(256, 384, 320), (136, 200, 72), (520, 264, 1032), (64, 64, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm(dtype, ta, tb, shape):
+    M, N, K = shape
+    print(f"gemm {dtype} ta={ta} tb={tb} {shape}", flush=True)
+    a = inputs(11, (K, M) if ta else (M, K), dtype)
+    b = inputs(12, (N, K) if tb else (K, N), dtype)
+    bias = inputs(13, (N,), dtype)
+    c = empty((M, N), dtype)
+    tst.gemm(to_gpu(a, dtype), to_gpu(b, dtype), c, bool(ta), bool(tb), bias=to_gpu(bias, dtype))
+    torch.cuda.synchronize()
+    A = a.astype(np.float64).T if ta else a.astype(np.float64)
+    B = b.astype(np.float64).T if tb else b.astype(np.float64)
+    assert_close("C", to_np(c), A @ B + bias.astype(np.float64)[None, :], dtype)
+
+
+def test_gemm_large_tiles_bf16():
+    """256x256 tiles with several XCD groups: M = 2048, N = 2560, K = 1024."""
+    M, N, K = 2048, 2560, 1024
+    a = inputs(14, (M, K), "bf16")
+    b = inputs(15, (K, N), "bf16")
+    c = empty((M, N), "bf16")
+    tst.gemm(to_gpu(a, "bf16"), to_gpu(b, "bf16"), c)
+    torch.cuda.synchronize()
+    assert_close("C", to_np(c), a.astype(np.float64) @ b.astype(np.float64), "bf16")
+
+
+# ------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols", [(64, 256), (37, 4096), (9, 20480), (5, 264)])
+def test_layernorm(dtype, rows, cols):
+    print(f"layernorm {dtype} {rows}x{cols}", flush=True)
+    x = inputs(21, (rows, cols), dtype, 2.0, 0.5)
+    g = inputs(22, (cols,), dtype, 0.1, 1.0)
+    b = inputs(23, (cols,), dtype, 0.1)
+    gy = inputs(24, (rows, cols), dtype)
+    xg, gg, bg, gyg = (to_gpu(v, dtype) for v in (x, g, b, gy))
+    y = empty((rows, cols), dtype)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    tst.layernorm_fwd(xg, gg, bg, 1e-5, y, mean, rstd)
+    dx = empty((rows, cols), dtype)
+    dgam = empty((cols,), dtype)
+    dbet = empty((cols,), dtype)
+    ws = empty_bytes(tst.layernorm_bwd_workspace_bytes(rows, cols))
+    tst.layernorm_bwd(gyg, xg, mean, rstd, gg, dx, dgam, dbet, ws)
+    torch.cuda.synchronize()
+    X = x.astype(np.float64)
+    ry, rmean, rrstd, xhat = OL.layernorm_fwd(X, g.astype(np.float64), b.astype(np.float64), 1e-5)
+    assert_close("y", to_np(y), ry, dtype)
+    assert rel_inf(to_np(mean), rmean) < 1e-5
+    assert rel_inf(to_np(rstd), rrstd) < 1e-5
+    rdx, rdg, rdb = OL.layernorm_bwd(gy.astype(np.float64), xhat, rrstd, g.astype(np.float64))
+    assert_close("dx", to_np(dx), rdx, dtype)
+    assert_close("dgamma", to_np(dgam), rdg, dtype)
+    assert_close("dbeta", to_np(dbet), rdb, dtype)
+
+
+# ------------------------------------------------------------------ attention
+ATTN_CASES = [("f32", 2, 128, 2, 64), ("f32", 1, 256, 2, 128), ("bf16", 2, 128, 2, 64),
+              ("bf16", 1, 256, 3, 128), ("bf16", 1, 384, 2, 160), ("bf16", 2, 256, 1, 160)]
+
+
+@pytest.mark.parametrize("dtype,batch,seq,heads,d", ATTN_CASES)
+def test_attention(dtype, batch, seq, heads, d):
+    print(f"attention {dtype} b={batch} s={seq} h={heads} d={d}", flush=True)
+    T = batch * seq
+    qkv = inputs(31, (T, 3 * heads * d), dtype)
+    go = inputs(32, (T, heads * d), dtype)
+    qg = to_gpu(qkv, dtype)
+    o = empty((T, heads * d), dtype)
+    lse = torch.empty((heads, T), dtype=torch.float32, device="cuda")
+    tst.attention_fwd(qg, o, lse, batch, seq, heads, d)
+    dq = empty((T, 3 * heads * d), dtype)
+    ws = empty_bytes(tst.attention_bwd_workspace_bytes(batch, seq, heads))
+    tst.attention_bwd(qg, o, lse, to_gpu(go, dtype), dq, ws, batch, seq, heads, d)
+    torch.cuda.synchronize()
+    ro, p, rlse = OL.attention_fwd(qkv.astype(np.float64), batch, seq, heads, d)
+    assert_close("o", to_np(o), ro, dtype)
+    # lse [b, nh, s] -> [nh, b*s]
+    rl = rlse.transpose(1, 0, 2).reshape(heads, T)
+    assert np.max(np.abs(to_np(lse) - rl)) < (2e-2 if dtype == "bf16" else 1e-4)
+    # backward from the GPU's own (rounded) O: the oracle uses its P and the given dO
+    rdq = OL.attention_bwd(qkv.astype(np.float64), p, go.astype(np.float64), batch, seq, heads, d)
+    w = heads * d
+    for name, sl in (("dq", slice(0, w)), ("dk", slice(w, 2 * w)), ("dv", slice(2 * w, 3 * w))):
+        assert_close(name, to_np(dq)[:, sl], rdq[:, sl], dtype)
+
+
+# ------------------------------------------------------------------ streaming kernels
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [1, 3])
+def test_reduce_partials(dtype, n):
+    rows, cols = 67, 264
+    parts = [inputs(40 + j, (rows, cols), dtype) for j in range(n)]
+    res = inputs(50, (rows, cols), dtype)
+    bias = inputs(51, (cols,), dtype)
+    out = empty((rows, cols), dtype)
+    tst.reduce_partials([to_gpu(p, dtype) for p in parts], out, to_gpu(res, dtype), to_gpu(bias, dtype))
+    out2 = empty((rows, cols), dtype)
+    tst.reduce_partials([to_gpu(p, dtype) for p in parts], out2)
+    torch.cuda.synchronize()
+    ref = OL.reduce_partials([p.astype(np.float64) for p in parts], res.astype(np.float64), bias.astype(np.float64))
+    assert_close("out", to_np(out), ref, dtype)
+    ref2 = OL.reduce_partials([p.astype(np.float64) for p in parts], np.zeros((rows, cols)), None)
+    assert_close("out_nores", to_np(out2), ref2, dtype)
+
+
+@pytest.mark.parametrize("n", [8, 1000003])
+def test_grad_accumulate(n):
+    gs = [round_f32_to_bf16(randn(60 + k, (n,), 1e-3)) for k in range(4)]
+    acc = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    for k, g in enumerate(gs):
+        tst.grad_accumulate(to_gpu(g, "bf16"), acc, overwrite=(k == 0))
+    torch.cuda.synchronize()
+    ref = OA.accumulate([g.astype(np.float64) for g in gs])
+    assert rel_inf(to_np(acc), ref) < 1e-6
+
+
+def _adam_run(n, cfg, master, m, v, acc):
+    mg, mm, vv, ag = (torch.from_numpy(a.astype(np.float32)).cuda() for a in (master, m, v, acc))
+    w = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    stats = torch.zeros(3, dtype=torch.float32, device="cuda")
+    ws = empty_bytes(tst.adam_workspace_bytes(n))
+    c = tst.AdamCfg(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.max_grad_norm,
+                    cfg.inv_loss_scale, cfg.step)
+    tst.adam_step(c, mg, mm, vv, ag, w, stats, ws)
+    torch.cuda.synchronize()
+    return to_np(mg), to_np(mm), to_np(vv), to_np(w), to_np(stats)
+
+
+@pytest.mark.parametrize("n", [5, 4096, 1000003])
+@pytest.mark.parametrize("max_norm", [1.0, 0.0, 1e6])
+def test_adam_step(n, max_norm):
+    master = randn(70, (n,), 0.02)
+    m = randn(71, (n,), 1e-3)
+    v = randn(72, (n,), 1e-3) ** 2
+    acc = randn(73, (n,), 1e-3) * 4
+    cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, max_grad_norm=max_norm,
+                        inv_loss_scale=2.0 ** -3, step=100)
+    gp, gm, gv, gw, st = _adam_run(n, cfg, master, m, v, acc)
+    rp, rm, rv, rw, (norm, coef, inf) = OA.adam_step(master.astype(np.float64), m.astype(np.float64),
+                                                    v.astype(np.float64), acc.astype(np.float64), cfg)
+    assert not inf and st[2] == 0.0
+    assert abs(st[0] - norm) <= 1e-5 * norm
+    assert abs(st[1] - coef) <= 1e-5
+    # updates (delta p) to 1e-4 relative of the largest step, moments to 1e-5
+    assert rel_inf(gp - master, rp - master) < 1e-4
+    assert rel_inf(gm, rm) < 1e-5
+    assert rel_inf(gv, rv) < 1e-5
+    # bf16 weight copy: within one bf16 ulp of the oracle's rounding
+    ulp = np.abs(rw) * 2.0 ** -7 + 1e-38
+    assert np.all(np.abs(gw - rw) <= ulp)
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_adam_nonfinite_skips(bad):
+    n = 4099
+    master = randn(80, (n,), 0.02)
+    m = randn(81, (n,), 1e-3)
+    v = randn(82, (n,), 1e-3) ** 2
+    acc = randn(83, (n,), 1e-3)
+    acc[n - 2] = bad
+    cfg = OA.AdamConfig(step=3)
+    gp, gm, gv, gw, st = _adam_run(n, cfg, master, m, v, acc)
+    assert st[2] == 1.0
+    assert np.array_equal(gp, master.astype(np.float64))
+    assert np.array_equal(gm, m.astype(np.float64)) and np.array_equal(gv, v.astype(np.float64))
+
+
+def test_adam_constant_gradient_closed_form():
+    """From zero state with constant g, each step moves p by -lr g/(|g|+eps) (Adam closed form)."""
+    n = 1024
+    g = np.where(np.arange(n) % 2 == 0, 3e-3, -5e-4).astype(np.float32)
+    p0 = randn(84, (n,), 0.02)
+    mg = torch.from_numpy(p0.copy()).cuda()
+    mm = torch.zeros(n, device="cuda")
+    vv = torch.zeros(n, device="cuda")
+    ag = torch.from_numpy(g).cuda()
+    stats = torch.zeros(3, device="cuda")
+    ws = empty_bytes(tst.adam_workspace_bytes(n))
+    for t in range(1, 4):
+        tst.adam_step(tst.AdamCfg(1e-3, 0.9, 0.95, 1e-8, 0.0, 0.0, 1.0, t), mg, mm, vv, ag, None, stats, ws)
+    torch.cuda.synchronize()
+    want = p0.astype(np.float64) - 3 * 1e-3 * g / (np.abs(g) + 1e-8)
+    assert rel_inf(to_np(mg) - p0, want - p0) < 1e-5
