@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's 1/8 tensor slice of an MT-NLG decoder layer on MI355X.
+
+One timed step = the forward and backward of the slice (hidden 20480, 16 of 128
+heads x 160, MLP slice 10240, one sequence of 2048 tokens, bf16): LayerNorm,
+QKV, causal attention and output projection, the local partial sum (residual +
+bias), LayerNorm, MLP up + GeLU and down, the local partial sum, then the
+backward of both halves including the input-gradient sums. `value` is the
+algorithmic FLOP count of the step (GEMMs plus causal attention, 2 per
+multiply-add, 7.795e12) divided by the step time.
+
+Also measured in the same run:
+  * the optimizer over one GPU's share of the 530B model (1,887,436,800
+    parameters): fp32 accumulation of 4 bf16 micro-batch gradients, then the
+    fused unscale + global-norm clip + Adam step, as HBM GB/s;
+  * each GEMM launch of the step alone (HIP events on the stream it runs on)
+    for the roofline of the GEMM kernel;
+  * the float64 CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "TFLOP/s per GPU, MT-NLG layer shard fwd+bwd bf16 (% MFMA peak); Adam GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ADAM_N = 1_887_436_800        # 3 layers x 629,145,600 slice parameters
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-adam", action="store_true")
+    ap.add_argument("--adam-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (to scale HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's tensor slice on one GPU; runs on more than one GPU "
+              "are not supported by this build (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_sliced_transformer_amd as tst
+    from synth.inputs import WORKLOADS, make_activation, make_half_params
+
+    tst.load()  # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)    # 512 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 536870912 bytes read and written")
+        del src, dst
+    w = WORKLOADS[3]
+    T, h, wl, fl = w.tokens, w.hidden, w.local_width, w.local_ffn
+    desc = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, 0, tst.BF16, 1e-5)
+
+    log("generating seeded inputs (1/8 shard, h 20480)")
+    t0 = time.time()
+    pa_np = make_half_params(w, "attn", 0)
+    pm_np = make_half_params(w, "mlp", 0)
+    x_np = make_activation(w, 1)
+    g_np = make_activation(w, 2)
+
+    def dev_bf16(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev)
+
+    pa = {k: dev_bf16(v) for k, v in pa_np.items()}
+    pm = {k: dev_bf16(v) for k, v in pm_np.items()}
+    x = dev_bf16(x_np)
+    g = dev_bf16(g_np)
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    def zeros_like_params(p):
+        return {k: torch.empty_like(v) for k, v in p.items()}
+
+    ga, gm = zeros_like_params(pa), zeros_like_params(pm)
+    sav_a = torch.empty(tst.saved_bytes(desc, tst.ATTN), dtype=torch.uint8, device=dev)
+    sav_m = torch.empty(tst.saved_bytes(desc, tst.MLP), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(tst.workspace_bytes(desc, tst.ATTN), tst.workspace_bytes(desc, tst.MLP)),
+                     dtype=torch.uint8, device=dev)
+    part = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    x1 = torch.empty_like(part)
+    out = torch.empty_like(part)
+    dxp = torch.empty_like(part)
+    g1 = torch.empty_like(part)
+    dx = torch.empty_like(part)
+    pa_call = {k: v for k, v in pa.items() if k != "b_out"}
+    pm_call = {k: v for k, v in pm.items() if k != "b_out"}
+
+    def step():
+        tst.layer_fwd(desc, tst.ATTN, pa_call, x, part, sav_a, ws)
+        tst.reduce_partials([part], x1, residual=x, bias=pa["b_out"])
+        tst.layer_fwd(desc, tst.MLP, pm_call, x1, part, sav_m, ws)
+        tst.reduce_partials([part], out, residual=x1, bias=pm["b_out"])
+        tst.layer_bwd(desc, tst.MLP, pm_call, x1, sav_m, g, dxp, gm, ws)
+        tst.reduce_partials([dxp], g1, residual=g)
+        tst.layer_bwd(desc, tst.ATTN, pa_call, x, sav_a, g1, dxp, ga, ws)
+        tst.reduce_partials([dxp], dx, residual=g1)
+
+    flops = 3.0 * shard_fwd_flops(T, h, w.local_heads, w.head_dim, fl, w.seq, w.batch)
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"fwd+bwd step {ms:.3f} ms = {tflops:.1f} TFLOP/s")
+
+    # ---- each GEMM launch of the step alone (same shapes and operand layouts) ----
+    gemm_rows = gemm_breakdown(torch, tst, dev, T, h, wl, fl)
+    g_fl = sum(r["flop"] for r in gemm_rows)
+    g_ms = sum(r["ms"] for r in gemm_rows)
+    gemm_tflops = g_fl / (g_ms * 1e-3) / 1e12
+    log(f"GEMMs alone: {g_ms:.3f} ms of the step, {gemm_tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": "mtnlg-shard-h20480-t8-bf16 fwd+bwd", "tokens": T, "hidden": h,
+                   "local_heads": w.local_heads, "head_dim": w.head_dim, "local_ffn": fl, "causal": True,
+                   "flop_per_step": flops},
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (the 12 GEMM launches of one step)",
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic_bytes(),
+                     "traffic_unit": "bytes per launch (average over the 12 launches)",
+                     "algorithmic_bytes": sum(2 * (r["M"] * r["K"] + r["K"] * r["N"] + r["M"] * r["N"])
+                                              for r in gemm_rows) / len(gemm_rows),
+                     "launches": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                                  for r in gemm_rows]},
+    }
+    del pa, pm, ga, gm, sav_a, sav_m, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_adam:
+        result["adam"] = adam_bench(torch, tst, dev, args.adam_reps)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pa_np, pm_np, x_np, g_np)
+
+    print(json.dumps(result), flush=True)
+
+
+def gemm_traffic_bytes():
+    """HBM bytes per GEMM launch from the committed counter passes, or None when the GEMM
+    source has changed since those counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(root, "profiles", "gemm_traffic.json")))
+        src = open(os.path.join(root, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["avg_bytes_per_launch"]
+
+
+def shard_fwd_flops(tokens, hidden, heads_local, head_dim, ffn_local, seq, batch):
+    wl = heads_local * head_dim
+    gemm = 2.0 * tokens * (hidden * 3 * wl + wl * hidden + hidden * ffn_local + ffn_local * hidden)
+    attn = 4.0 * batch * heads_local * head_dim * seq * (seq + 1) / 2.0
+    return gemm + attn
+
+
+def gemm_breakdown(torch, tst, dev, T, h, wl, fl, reps=10):
+    """Every GEMM of the step, launched alone through mtnlg_gemm with its shape and layout."""
+    # (name, M, N, K, trans_a, trans_b)
+    shapes = [("qkv", T, 3 * wl, h, 0, 0), ("out_proj", T, h, wl, 0, 0), ("mlp_up", T, fl, h, 0, 0),
+              ("mlp_down", T, h, fl, 0, 0), ("mlp_dY", T, fl, h, 0, 1), ("mlp_dB", fl, h, T, 1, 0),
+              ("mlp_dA", h, fl, T, 1, 0), ("mlp_dX", T, h, fl, 0, 1), ("attn_dO", T, wl, h, 0, 1),
+              ("attn_dWo", wl, h, T, 1, 0), ("attn_dWqkv", h, 3 * wl, T, 1, 0), ("attn_dX", T, h, 3 * wl, 0, 1)]
+    rows = []
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    for name, M, N, K, ta, tb in shapes:
+        a = torch.randn((K, M) if ta else (M, K), device=dev, generator=gen).to(torch.bfloat16)
+        b = torch.randn((N, K) if tb else (K, N), device=dev, generator=gen).to(torch.bfloat16)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            tst.gemm(a, b, c, bool(ta), bool(tb))
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            tst.gemm(a, b, c, bool(ta), bool(tb))
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        fl_ = 2.0 * M * N * K
+        rows.append({"name": name, "M": M, "N": N, "K": K, "layout": f"{'T' if ta else 'N'}{'T' if tb else 'N'}",
+                     "ms": ms, "tflops": fl_ / (ms * 1e-3) / 1e12, "flop": fl_})
+        del a, b, c
+    return rows
+
+
+def adam_bench(torch, tst, dev, reps):
+    """Optimizer over 1.887e9 parameters: accumulate 4 bf16 micro-batch grads, then the step."""
+    n = ADAM_N
+    log(f"optimizer workload: {n} parameters")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4000)
+    master = torch.randn(n, device=dev, generator=gen).mul_(0.02)
+    m = torch.randn(n, device=dev, generator=gen).mul_(1e-3)
+    v = torch.randn(n, device=dev, generator=gen).mul_(1e-3).square_()
+    grads = [torch.randn(n, device=dev, generator=gen).mul_(1e-3).to(torch.bfloat16) for _ in range(4)]
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    wbf = master.to(torch.bfloat16)
+    stats = torch.zeros(3, dtype=torch.float32, device=dev)
+    ws = torch.empty(tst.adam_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    cfg = tst.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 100)
+
+    def accumulate():
+        for k, gk in enumerate(grads):
+            tst.grad_accumulate(gk, acc, overwrite=(k == 0))
+
+    def opt_step():
+        tst.adam_step(cfg, master, m, v, acc, wbf, stats, ws)
+
+    accumulate()
+    opt_step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_acc = t_step = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        accumulate()
+        ev[1].record()
+        opt_step()
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_acc += ev[0].elapsed_time(ev[1])
+        t_step += ev[1].elapsed_time(ev[2])
+    t_acc /= reps
+    t_step /= reps
+    st = stats.cpu().tolist()
+    acc_gbs = 36.0 * n / (t_acc * 1e-3) / 1e9
+    step_gbs = 34.0 * n / (t_step * 1e-3) / 1e9
+    log(f"accumulate x4 {t_acc:.2f} ms = {acc_gbs:.0f} GB/s; step {t_step:.2f} ms = {step_gbs:.0f} GB/s; "
+        f"stats {st}")
+    out = {"n_params": n, "micro_batches": 4,
+           "step_ms": round(t_step, 3), "step_GBps": round(step_gbs, 1),
+           "step_hbm_frac": round(step_gbs / PEAK_HBM_GBS, 4), "step_bytes_per_param": 34,
+           "accumulate_ms": round(t_acc, 3), "accumulate_GBps": round(acc_gbs, 1),
+           "accumulate_hbm_frac": round(acc_gbs / PEAK_HBM_GBS, 4), "accumulate_bytes_per_param": 36,
+           "grad_norm": st[0], "clip_coef": st[1], "found_inf": st[2]}
+    del master, m, v, grads, acc, wbf, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=512):
+    """The float64 oracle (as it stands) on the first sequence of 512 tokens of the same slice."""
+    from threadpoolctl import threadpool_info
+    from oracle import layer as OL
+    sh = OL.LayerShape(batch=1, seq=sample_tokens, hidden=20480, heads=128, ffn=81920, tp=8)
+    log(f"cpu baseline: oracle fwd+bwd of the slice on {sample_tokens} tokens")
+    pa = {k: v.astype(np.float64) for k, v in pa_np.items()}
+    pm = {k: v.astype(np.float64) for k, v in pm_np.items()}
+    x = x_np[:sample_tokens].astype(np.float64)
+    g = g_np[:sample_tokens].astype(np.float64)
+    t0 = time.perf_counter()
+    pa_part, sa = OL.attn_half_fwd(sh, x, pa)
+    x1 = OL.reduce_partials([pa_part], x, pa["b_out"])
+    pm_part, sm = OL.mlp_half_fwd(sh, x1, pm)
+    dxm, _, _ = OL.mlp_half_bwd(sh, g, pm, sm)
+    g1 = OL.reduce_partials([dxm], g, None)
+    OL.attn_half_bwd(sh, g1, pa, sa)
+    dt = time.perf_counter() - t0
+    fl = 3.0 * shard_fwd_flops(sample_tokens, 20480, 16, 160, 10240, sample_tokens, 1)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    log(f"cpu baseline {dt:.1f}s, {fl / dt / 1e12:.3f} TFLOP/s on {threads} threads")
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle fwd+bwd of the same 1/8 slice on one sequence of {sample_tokens} "
+                      f"tokens ({fl / 1e12:.3f} TFLOP), {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

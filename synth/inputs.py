@@ -37,19 +37,19 @@ def randn(seed: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest even, NaN kept quiet."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    out = np.empty(u.shape, dtype=np.uint16)
-    flat_u = u.reshape(-1)
-    flat_o = out.reshape(-1)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).reshape(-1)
+    out = np.empty(u.size, dtype=np.uint16)
     step = 1 << 24
-    for s in range(0, flat_u.size, step):
-        c = flat_u[s:s + step].astype(np.uint64)
-        lsb = (c >> np.uint64(16)) & np.uint64(1)
-        r = (c + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-        nan = (c & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
-        r = np.where(nan, (c >> np.uint64(16)) | np.uint64(0x40), r)
-        flat_o[s:s + step] = r.astype(np.uint16)
-    return out
+    for s in range(0, u.size, step):
+        c = u[s:s + step]
+        nan = (c & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        r = (c >> np.uint32(16)) & np.uint32(1)       # lsb of the kept half: ties go to even
+        r += np.uint32(0x7FFF)
+        r += np.where(nan, np.uint32(0), c)            # NaN: no rounding carry into the exponent
+        r >>= np.uint32(16)
+        r = np.where(nan, (c >> np.uint32(16)) | np.uint32(0x40), r)
+        out[s:s + step] = r.astype(np.uint16)
+    return out.reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

@@ -1,0 +1,200 @@
+"""GPU parity of whole layer halves and whole sliced layers against the CPU oracle.
+
+* tiny layer, fp32, t = 2 slices run in turn: forward, backward (both halves,
+  partial sums through mtnlg_reduce_partials) and one Adam step over every
+  parameter, compared in full with the oracle's unsliced layer;
+* GPT-style layer h 4096, t = 1, bf16: each half forward + backward in full;
+* MT-NLG 1/8 shard h 20480, 16 heads x 160, bf16: each half forward + backward
+  in full (the oracle runs the same slice in float64);
+* run-to-run determinism of a backward.
+Tolerance: ||gpu - oracle||_inf / ||oracle||_inf per tensor (1e-4 fp32, 2e-2 bf16).
+"""
+import numpy as np
+import pytest
+
+from helpers import TOL, assert_close, empty, empty_bytes, rel_inf, rel_l2, to_gpu, to_np
+from oracle import adam as OA
+from oracle import layer as OL
+from synth.inputs import WORKLOADS, make_activation, make_half_params
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import tensor_sliced_transformer_amd as tst  # noqa: E402
+
+HALF = {"attn": tst.ATTN, "mlp": tst.MLP}
+
+
+def desc_of(w, rank=0):
+    return tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, rank,
+                         tst.BF16 if w.dtype == "bf16" else tst.F32, 1e-5)
+
+
+def shape_of(w):
+    return OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=w.tp)
+
+
+class GpuHalf:
+    """Device buffers and calls of one slice of one half."""
+
+    def __init__(self, w, half, params_np, rank=0):
+        self.w, self.half, self.dt = w, half, w.dtype
+        self.desc = desc_of(w, rank)
+        self.p = {k: to_gpu(v, self.dt) for k, v in params_np.items() if k != "b_out"}
+        self.saved = empty_bytes(tst.saved_bytes(self.desc, HALF[half]))
+        self.ws = empty_bytes(tst.workspace_bytes(self.desc, HALF[half]))
+        self.g = {k: empty(v.shape, self.dt) for k, v in params_np.items()}
+
+    def fwd(self, x):
+        y = empty((self.w.tokens, self.w.hidden), self.dt)
+        tst.layer_fwd(self.desc, HALF[self.half], self.p, x, y, self.saved, self.ws)
+        return y
+
+    def bwd(self, x, dy):
+        dx = empty((self.w.tokens, self.w.hidden), self.dt)
+        tst.layer_bwd(self.desc, HALF[self.half], self.p, x, self.saved, dy, dx, self.g, self.ws)
+        return dx
+
+
+def oracle_params(p):
+    return {k: v.astype(np.float64) for k, v in p.items()}
+
+
+def check_half(w, half, tag_x, tag_g):
+    """Forward and backward of slice 0 of one half vs the oracle, every output in full."""
+    print(f"{w.name} {half}", flush=True)
+    pn = make_half_params(w, half, 0)
+    x = make_activation(w, tag_x)
+    g = make_activation(w, tag_g)
+    gh = GpuHalf(w, half, pn)
+    xg, gg = to_gpu(x, w.dtype), to_gpu(g, w.dtype)
+    y = gh.fwd(xg)
+    dx = gh.bwd(xg, gg)
+    torch.cuda.synchronize()
+    sh = shape_of(w)
+    po = oracle_params(pn)
+    if half == "attn":
+        part, saved = OL.attn_half_fwd(sh, x.astype(np.float64), po)
+        rdx, rg, _ = OL.attn_half_bwd(sh, g.astype(np.float64), po, saved)
+    else:
+        part, saved = OL.mlp_half_fwd(sh, x.astype(np.float64), po)
+        rdx, rg, _ = OL.mlp_half_bwd(sh, g.astype(np.float64), po, saved)
+    errs = {"y_partial": assert_close("y_partial", to_np(y), part, w.dtype),
+            "dx_partial": assert_close("dx_partial", to_np(dx), rdx, w.dtype)}
+    for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out"):
+        errs[k] = assert_close(k, to_np(gh.g[k]), rg[k], w.dtype)
+    print({k: f"{v:.2e}" for k, v in errs.items()}, "l2(y)", f"{rel_l2(to_np(y), part):.2e}", flush=True)
+
+
+@pytest.mark.parametrize("half", ["attn", "mlp"])
+def test_gpt_layer_h4096_halves(half):
+    check_half(WORKLOADS[2], half, 1, 2)
+
+
+@pytest.mark.parametrize("half", ["attn", "mlp"])
+def test_mtnlg_shard_halves(half):
+    check_half(WORKLOADS[3], half, 1, 2)
+
+
+def test_tiny_layer_two_slices_and_adam():
+    """Whole layer from t = 2 slices (fp32) against the oracle's unsliced layer, then one Adam step."""
+    w = WORKLOADS[1]
+    sh = shape_of(w)
+    ap = [make_half_params(w, "attn", i) for i in range(w.tp)]
+    mp = [make_half_params(w, "mlp", i) for i in range(w.tp)]
+    x = make_activation(w, 1)
+    gout = make_activation(w, 2)
+    # full parameters assembled from the slices (the oracle slices them again)
+    full = {k: np.zeros(s) for k, s in OL.full_param_shapes(sh).items()}
+    full["ln1_g"], full["ln1_b"], full["b_o"] = ap[0]["ln_g"], ap[0]["ln_b"], ap[0]["b_out"]
+    full["ln2_g"], full["ln2_b"], full["b_b"] = mp[0]["ln_g"], mp[0]["ln_b"], mp[0]["b_out"]
+    wl, fl = sh.local_width, sh.local_ffn
+    for i in range(w.tp):
+        cols = OL.qkv_columns(sh, i)
+        full["w_qkv"][:, cols] = ap[i]["w_in"]
+        full["b_qkv"][cols] = ap[i]["b_in"]
+        full["w_o"][i * wl:(i + 1) * wl] = ap[i]["w_out"]
+        full["w_a"][:, i * fl:(i + 1) * fl] = mp[i]["w_in"]
+        full["b_a"][i * fl:(i + 1) * fl] = mp[i]["b_in"]
+        full["w_b"][i * fl:(i + 1) * fl] = mp[i]["w_out"]
+    full = {k: np.asarray(v, dtype=np.float64) for k, v in full.items()}
+
+    dt = w.dtype
+    A = [GpuHalf(w, "attn", ap[i], i) for i in range(w.tp)]
+    M = [GpuHalf(w, "mlp", mp[i], i) for i in range(w.tp)]
+    xg = to_gpu(x, dt)
+    bo, bb = to_gpu(ap[0]["b_out"], dt), to_gpu(mp[0]["b_out"], dt)
+    x1 = empty(x.shape, dt)
+    tst.reduce_partials([a.fwd(xg) for a in A], x1, residual=xg, bias=bo)
+    out = empty(x.shape, dt)
+    tst.reduce_partials([m.fwd(x1) for m in M], out, residual=x1, bias=bb)
+    gg = to_gpu(gout, dt)
+    g1 = empty(x.shape, dt)
+    tst.reduce_partials([m.bwd(x1, gg) for m in M], g1, residual=gg)
+    dx = empty(x.shape, dt)
+    tst.reduce_partials([a.bwd(xg, g1) for a in A], dx, residual=g1)
+    torch.cuda.synchronize()
+
+    rout, st = OL.layer_fwd(sh, x.astype(np.float64), full)
+    rdx, rg = OL.layer_bwd(sh, gout.astype(np.float64), full, st)
+    assert_close("x1", to_np(x1), st["x1"], dt)
+    assert_close("out", to_np(out), rout, dt)
+    assert_close("dx", to_np(dx), rdx, dt)
+    # weight gradients: slices vs the columns/rows of the unsliced gradient
+    for i in range(w.tp):
+        cols = OL.qkv_columns(sh, i)
+        assert_close("dw_qkv", to_np(A[i].g["w_in"]), rg["w_qkv"][:, cols], dt)
+        assert_close("db_qkv", to_np(A[i].g["b_in"]), rg["b_qkv"][cols], dt)
+        assert_close("dw_o", to_np(A[i].g["w_out"]), rg["w_o"][i * wl:(i + 1) * wl], dt)
+        assert_close("dw_a", to_np(M[i].g["w_in"]), rg["w_a"][:, i * fl:(i + 1) * fl], dt)
+        assert_close("db_a", to_np(M[i].g["b_in"]), rg["b_a"][i * fl:(i + 1) * fl], dt)
+        assert_close("dw_b", to_np(M[i].g["w_out"]), rg["w_b"][i * fl:(i + 1) * fl], dt)
+        assert_close("db_o", to_np(A[i].g["b_out"]), rg["b_o"], dt)
+        assert_close("db_b", to_np(M[i].g["b_out"]), rg["b_b"], dt)
+    # replicated LayerNorm parameters: sum of the slice partials
+    for key, halves, name in (("ln_g", A, "ln1_g"), ("ln_b", A, "ln1_b"), ("ln_g", M, "ln2_g"), ("ln_b", M, "ln2_b")):
+        tot = empty(halves[0].g[key].shape, dt)
+        tst.reduce_partials([h.g[key].view(1, -1) for h in halves], tot.view(1, -1))
+        torch.cuda.synchronize()
+        assert_close(name, to_np(tot), rg[name], dt)
+
+    # one Adam step over the flat parameter vector of slice 0's attention half (fp32 grads
+    # accumulated into the fp32 accumulator; lr 1e-4, betas 0.9/0.95, eps 1e-8)
+    flat_p = np.concatenate([ap[0][k].ravel() for k in ("w_in", "b_in", "w_out")]).astype(np.float32)
+    flat_g = torch.cat([A[0].g[k].reshape(-1) for k in ("w_in", "b_in", "w_out")]).contiguous()
+    n = flat_p.size
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    tst.grad_accumulate(flat_g, acc, overwrite=True)
+    mg = torch.from_numpy(flat_p.copy()).cuda()
+    mm = torch.zeros(n, device="cuda")
+    vv = torch.zeros(n, device="cuda")
+    stats = torch.zeros(3, device="cuda")
+    ws = empty_bytes(tst.adam_workspace_bytes(n))
+    tst.adam_step(tst.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 1), mg, mm, vv, acc, None, stats, ws)
+    torch.cuda.synchronize()
+    cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, max_grad_norm=1.0, step=1)
+    ga = to_np(acc)
+    rp, rm, rv, _, (norm, coef, inf) = OA.adam_step(flat_p.astype(np.float64), np.zeros(n), np.zeros(n), ga, cfg)
+    assert not inf
+    assert abs(to_np(stats)[0] - norm) <= 1e-5 * norm
+    assert rel_inf(to_np(mg) - flat_p, rp - flat_p) < 1e-4
+    assert rel_inf(to_np(mm), rm) < 1e-5 and rel_inf(to_np(vv), rv) < 1e-5
+
+
+def test_backward_is_deterministic():
+    w = WORKLOADS[2]
+    pn = make_half_params(w, "mlp", 0)
+    x = to_gpu(make_activation(w, 1), w.dtype)
+    g = to_gpu(make_activation(w, 2), w.dtype)
+    gh = GpuHalf(w, "mlp", pn)
+    gh.fwd(x)
+    dx1 = gh.bwd(x, g).clone()
+    g1 = {k: v.clone() for k, v in gh.g.items()}
+    dx2 = gh.bwd(x, g)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2)
+    for k in g1:
+        assert torch.equal(g1[k], gh.g[k]), k
