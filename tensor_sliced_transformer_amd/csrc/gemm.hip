@@ -11,13 +11,19 @@
 //     sub-tile made of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 for bf16,
 //     v_mfma_f32_32x32x2f32 for fp32).
 //   * LDS holds both operand tiles as rows of K: 8 chunks of 16 bytes per
-//     row (BK = 64 bf16 or 32 fp32), the chunk index XOR-ed with (row & 7)
-//     so that the 32 rows one MFMA operand read touches spread over banks.
+//     row (BK = 64 bf16 or 32 fp32), the chunk index XOR-ed with
+//     ((row >> 1) & 7) so that MFMA operand reads (16 rows per LDS cycle) and
+//     the transposed stores spread over the banks.
 //   * K-contiguous operands are copied chunk by chunk; M/N-contiguous ones
 //     are loaded as VECxVEC micro-blocks and transposed in registers, so the
 //     MFMA loop is the same for all four layouts and HBM is read once.
-//   * Two LDS stages: the global loads of tile k+1 are issued before the
-//     MFMAs of tile k and written to the other stage afterwards.
+//   * Two LDS stages and register staging with prefetch distance 2: at the
+//     top of K tile k the registers (tile k+1) go to the free stage and the
+//     buffer loads of tile k+2 are issued, so a load has a whole tile of MFMAs
+//     to arrive. MFMA fragments are double-buffered across k-substeps, and the
+//     single barrier per tile sits before the last substep so the next tile's
+//     first fragments load under its MFMAs. Out-of-range elements come from
+//     buffer loads past num_records (zero), not from branches.
 //   * Workgroup ids are remapped so that each XCD (ids round-robin over 8
 //     XCDs) gets a contiguous range of tiles, walked in groups of 8 tile rows
 //     so that concurrently running tiles share operand panels in that XCD's L2.
@@ -67,6 +73,23 @@ __device__ __forceinline__ void transpose_block(const uint4* in, uint4* out, flo
     for (int j = 0; j < 4; ++j) o[i * 4 + j] = f[j * 4 + i];
 }
 
+// LDS chunk swizzle: 16-byte chunk c of LDS row `row` lives at slot
+// c ^ ((row >> 1) & 7). With 128-byte rows, 16 consecutive rows reading the
+// same logical chunk then touch 16 distinct 16-byte bank groups (row parity
+// picks the half of a 256-byte bank period, the XOR picks the slot in it).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// 128-bit buffer resource over a whole operand; loads at offsets beyond
+// num_records return zero, which is how ragged tiles are handled without
+// branches (an out-of-range element gets the offset kOob).
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // Loader of one operand tile (R rows of the M or N dimension, BK of K) into
 // LDS rows of K. KC: source is K-contiguous (elem(r,k) = p[r*ld + k]),
 // otherwise R-contiguous (elem(r,k) = p[k*ld + r]).
@@ -80,28 +103,30 @@ struct TileLoader {
   static constexpr int REGS = KC ? PER_T : PER_T * VEC;
   uint4 st[REGS];
 
-  __device__ __forceinline__ void load(const T* __restrict__ p, int64_t ld, int r0, int rmax,
-                                       int k0, int kend, int tid) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int r0, int rmax, int k0, int kend,
+                                       int tid) {
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
       const int id = tid + u * kThreads;
       if (KC) {
         const int row = id / kCH, ch = id % kCH;
         const int r = r0 + row, k = k0 + ch * VEC;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (id < UNITS && r < rmax && k < kend)
-          v = *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + k);
-        st[u] = v;
+        const bool ok = id < UNITS && r < rmax && k < kend;
+        const uint32_t off = ok ? (uint32_t)(((int64_t)r * ld + k) * (int64_t)sizeof(T)) : kOob;
+        st[u] = buf_load16(rs, off);
       } else {
-        const int kb = id / (R / VEC), rb = id % (R / VEC);
+        // chunk index fastest across lanes: a store instruction then covers every
+        // chunk slot of its rows (see store) and a load instruction reads
+        // 8 rows x 8 consecutive 16-byte segments
+        const int kb = id % kCH, rb = id / kCH;
         const int r = r0 + rb * VEC;
+        const bool rok = id < UNITS && r < rmax;
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const int k = k0 + kb * VEC + j;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (id < UNITS && r < rmax && k < kend)
-            v = *reinterpret_cast<const uint4*>(p + (int64_t)k * ld + r);
-          st[u * VEC + j] = v;
+          const uint32_t off =
+              (rok && k < kend) ? (uint32_t)(((int64_t)k * ld + r) * (int64_t)sizeof(T)) : kOob;
+          st[u * VEC + j] = buf_load16(rs, off);
         }
       }
     }
@@ -114,15 +139,15 @@ struct TileLoader {
       if (id >= UNITS) continue;
       if (KC) {
         const int row = id / kCH, ch = id % kCH;
-        s[row * kCH + (ch ^ (row & 7))] = st[u];
+        s[row * kCH + (ch ^ swz(row))] = st[u];
       } else {
-        const int kb = id / (R / VEC), rb = id % (R / VEC);
+        const int kb = id % kCH, rb = id / kCH;
         uint4 t[VEC];
         transpose_block(&st[u * VEC], t, T());
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           const int row = rb * VEC + i;
-          s[row * kCH + (kb ^ (row & 7))] = t[i];
+          s[row * kCH + (kb ^ swz(row))] = t[i];
         }
       }
     }
@@ -205,12 +230,16 @@ template <> struct Mfma<float> {
   }
 };
 
-template <typename T, int BM, int BN, bool A_KC, bool B_KC>
+template <typename T, int BM, int BN, int WM, int WN, bool A_KC, bool B_KC>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+  static_assert(WM * WN == kThreads / kWave, "4 waves");
   using E = Elem<T>;
   constexpr int VEC = E::VEC;
   constexpr int BK = kCH * VEC;
-  constexpr int FM = BM / 64, FN = BN / 64;
+  constexpr int TM = BM / WM, TN = BN / WN;      // wave tile
+  constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA blocks per wave
+  static_assert(FM * 32 == TM && FN * 32 == TN, "wave tile must be a multiple of 32");
+  constexpr int SUB = kCH / 2;                   // MFMA k-substeps per K tile
   __shared__ uint4 smem[2 * (BM + BN) * kCH];
   uint4* const sA0 = smem;                        // two A stages, then two B stages
   uint4* const sB0 = smem + 2 * BM * kCH;
@@ -235,11 +264,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int nk = (kend - kbeg + BK - 1) / BK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane & 31, lg = lane >> 5;
 
-  const T* __restrict__ Ap = static_cast<const T*>(p.A);
-  const T* __restrict__ Bp = static_cast<const T*>(p.B);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)((int64_t)p.M * p.K * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (uint32_t)((int64_t)p.K * p.N * sizeof(T)));
 
   TileLoader<T, BM, A_KC> la;
   TileLoader<T, BN, B_KC> lb;
@@ -252,55 +281,75 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // per-lane LDS row offsets (in chunks) of this wave's fragments
+  int arow[FM], brow[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) arow[i] = (wm * TM + i * 32 + lrow) * kCH;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) brow[j] = (wn * TN + j * 32 + lrow) * kCH;
+  const int sw = swz(lrow);  // the same for every fragment row of this lane (rows start at multiples of 32)
+
+  uint4 af[2][FM], bfr[2][FN];
+  auto load_frags = [&](const uint4* a_s, const uint4* b_s, int s, int buf) {
+    const int ch = (2 * s + lg) ^ sw;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[buf][i] = a_s[arow[i] + ch];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[buf][j] = b_s[brow[j] + ch];
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Mfma<T>::run(af[buf][i], bfr[buf][j], acc[i][j]);
+  };
+
   if (nk > 0) {
-    la.load(Ap, p.lda, m0, p.M, kbeg, kend, tid);
-    lb.load(Bp, p.ldb, n0, p.N, kbeg, kend, tid);
+    la.load(ra, p.lda, m0, p.M, kbeg, kend, tid);
+    lb.load(rb, p.ldb, n0, p.N, kbeg, kend, tid);
     la.store(sA0, tid);
     lb.store(sB0, tid);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(Ap, p.lda, m0, p.M, k0, kend, tid);
-      lb.load(Bp, p.ldb, n0, p.N, k0, kend, tid);
-    }
-    const uint4* a_s = sA0 + cur * BM * kCH;
-    const uint4* b_s = sB0 + cur * BN * kCH;
-#pragma unroll
-    for (int s = 0; s < kCH / 2; ++s) {
-      const int ch = 2 * s + lg;
-      uint4 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * (BM / 2) + i * 32 + lrow;
-        af[i] = a_s[row * kCH + (ch ^ (row & 7))];
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * (BN / 2) + j * 32 + lrow;
-        bfr[j] = b_s[row * kCH + (ch ^ (row & 7))];
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Mfma<T>::run(af[i], bfr[j], acc[i][j]);
-    }
-    if (more) {
-      la.store(sA0 + (cur ^ 1) * BM * kCH, tid);
-      lb.store(sB0 + (cur ^ 1) * BN * kCH, tid);
+    if (nk > 1) {
+      la.load(ra, p.lda, m0, p.M, kbeg + BK, kend, tid);
+      lb.load(rb, p.ldb, n0, p.N, kbeg + BK, kend, tid);
     }
     __syncthreads();
+    load_frags(sA0, sB0, 0, 0);
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const uint4* a_s = sA0 + cur * BM * kCH;
+    const uint4* b_s = sB0 + cur * BN * kCH;
+    uint4* a_n = sA0 + nxt * BM * kCH;
+    uint4* b_n = sB0 + nxt * BN * kCH;
+    // tile kt+1 (loaded during tile kt-1) goes to the other stage; then start tile kt+2
+    if (kt + 1 < nk) {
+      la.store(a_n, tid);
+      lb.store(b_n, tid);
+    }
+    if (kt + 2 < nk) {
+      const int k0 = kbeg + (kt + 2) * BK;
+      la.load(ra, p.lda, m0, p.M, k0, kend, tid);
+      lb.load(rb, p.ldb, n0, p.N, k0, kend, tid);
+    }
+#pragma unroll
+    for (int s = 0; s < SUB - 1; ++s) {
+      load_frags(a_s, b_s, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
+    }
+    // one barrier per K tile: every wave has finished writing stage `nxt` and
+    // reading stage `cur` (its last fragments are in registers)
+    __syncthreads();
+    if (kt + 1 < nk) load_frags(a_n, b_n, 0, SUB & 1);
+    mfmas((SUB - 1) & 1);
   }
 
   // ---- epilogue: stage one 32-row slab of each wave's sub-tile in LDS (now
   // free), then write 8-wide row vectors; the MFMA output layout (lane: column
   // lrow, rows 8*blk + 4*lg + r) is turned into row-contiguous stores here.
-  constexpr int WN = BN / 2;
-  constexpr int SROW = WN + 4;  // padded so the two lane groups' rows hit different banks
+  __syncthreads();
+  constexpr int SROW = TN + 4;  // padded so the two lane groups' rows hit different banks
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -311,7 +360,313 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) stage[(8 * blk + 4 * lg + r) * SROW + j * 32 + lrow] = acc[i][j][blk * 4 + r];
     __syncthreads();
-    epilogue_slab<T, WN, SROW>(p, stage, m0 + wm * (BM / 2) + i * 32, n0 + wn * WN, lane, split);
+    epilogue_slab<T, TN, SROW>(p, stage, m0 + wm * TM + i * 32, n0 + wn * TN, lane, split);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 GEMM with direct-to-LDS loads (the main path on gfx950)
+//
+// * Operand tiles move from HBM/L2 to LDS with buffer_load_dwordx4 ... lds:
+//   no staging registers and no ds_write; lane l of a wave instruction lands
+//   at base + 16*l, so the swizzle is applied to the GLOBAL address each lane
+//   fetches. A ring of kStages K-tiles of 32 (bf16) lets the loads of tile
+//   t+kStages-1 start while tile t is multiplied (three tiles of slack).
+// * K-contiguous operands: LDS rows of 32 k (64 B = 4 chunks); chunk c of
+//   row r sits at slot c ^ ((r >> 2) & 3), so 16 rows read by one MFMA
+//   operand fetch (ds_read_b128) hit 16 distinct 16-byte bank groups.
+// * M/N-contiguous operands stay in their natural layout in LDS (rows of k,
+//   R elements each, chunk c of row k at slot c ^ (4 * (k & 3))) and MFMA
+//   fragments are read with ds_read_b64_tr_b16: within 16 lanes, lane i
+//   supplies the 8 bytes at (row k0 + i/4, elements 4*(i%4)..+3) and lane j
+//   receives element j%4.. i.e. 4 consecutive k of element j -- exactly half
+//   of a 32x32x16 operand fragment; two reads make the 8 k of a lane.
+// * One barrier per K-tile, between its two k-substeps: it publishes tile
+//   t+1 (loads waited with vmcnt) and frees the stage of tile t-1 for the next
+//   prefetch, while the fragments of the next substep are read ahead.
+// ---------------------------------------------------------------------------
+#ifndef MTNLG_GEMM_STAGES
+#define MTNLG_GEMM_STAGES 4
+#endif
+constexpr int kStages = MTNLG_GEMM_STAGES;  // K-tiles in the LDS ring
+constexpr int kBKd = 32;                    // bf16 K per stage
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#define MTNLG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource as four words: 48-bit base, stride 0, num_records bytes,
+// and the raw-buffer format word used for make_rsrc above.
+__device__ __forceinline__ i32x4_t rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  i32x4_t r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)((a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer into LDS at m0 + 16*lane. Written as inline
+// asm on purpose: the compiler cannot tell which LDS bytes such a load writes
+// and would otherwise wait for ALL outstanding loads before every LDS read,
+// defeating the prefetch ring; the kernel waits on vmcnt itself (wait_tiles)
+// before the barrier that publishes a stage.
+__device__ __forceinline__ void dtl16(i32x4_t rsrc, const void* lds_base, uint32_t off) {
+  // the stage base is the same for every lane; make that explicit for the SGPR operand
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MTNLG_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint2 ds_read_tr(const char* p) {
+  s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, t);
+}
+
+// One operand of the direct-to-LDS GEMM: R rows of M (or N) per tile.
+template <int R, bool KC>
+struct DtlOperand {
+  static constexpr int STAGE_BYTES = R * kBKd * 2;
+  static constexpr int INSTR = STAGE_BYTES / 1024;     // 1 KiB per wave-wide load
+  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int RB = R * 2;                     // bytes per LDS row (MN layout)
+  static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile too small");
+  // per-lane, per-instruction (row/col) of the element this lane fetches
+  int r_[PER_WAVE];      // M/N index within the tile (KC) or k within the tile (MN)
+  int c_[PER_WAVE];      // k within the tile (KC) or M/N index within the tile (MN)
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int q = wave * PER_WAVE + u;
+      if (KC) {
+        const int r = q * 16 + lane / 4;                 // 16 rows of 64 B per KiB
+        const int slot = lane & 3;
+        r_[u] = r;
+        c_[u] = 8 * (slot ^ ((r >> 2) & 3));
+      } else {
+        const int rows_per = 1024 / RB;                  // 2 (R=256) or 4 (R=128)
+        const int k = q * rows_per + (16 * lane) / RB;
+        const int slot = ((16 * lane) % RB) / 16;
+        r_[u] = k;
+        c_[u] = 8 * (slot ^ (4 * (k & 3)));
+      }
+    }
+  }
+
+  // issue this wave's u-th load of the K-tile starting at k0 into stage `dst`
+  __device__ __forceinline__ void load_one(int u, i32x4_t rs, int64_t ld, int r0, int rmax, int k0, int kend,
+                                           char* dst, int wave) const {
+    const int q = wave * PER_WAVE + u;
+    uint32_t off;
+    if (KC) {
+      const int m = r0 + r_[u], k = k0 + c_[u];
+      off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)m * ld + k) * 2) : kOob;
+    } else {
+      const int k = k0 + r_[u], m = r0 + c_[u];
+      off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)k * ld + m) * 2) : kOob;
+    }
+    dtl16(rs, dst + q * 1024, off);
+  }
+};
+
+// Byte offset (within a stage) of this lane's fragment of the 32-row block
+// starting at tile row `rb32*32`, k-substep s (16 k): KC operand via b128.
+__device__ __forceinline__ int kc_frag_off(int rb32, int s, int lane) {
+  const int fr = lane & 31, g = lane >> 5;
+  const int r = rb32 * 32 + fr;
+  return r * 64 + (((2 * s + g) ^ ((fr >> 2) & 3)) * 16);
+}
+// MN operand via two transposing reads; returns the offset of read h = 0 (h = 1 adds 4 rows).
+template <int RB>
+__device__ __forceinline__ int mn_frag_off(int rb32, int s, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int k = s * 16 + 8 * (G >> 1) + (i >> 2);
+  const int c = 4 * (rb32 ^ (i >> 2)) + 2 * (G & 1) + ((i >> 1) & 1);
+  return k * RB + c * 16 + 8 * (i & 1);
+}
+
+template <int BM, int BN, bool A_KC, bool B_KC>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_dtl_kernel(GemmArgs p) {
+  constexpr int WM = 2, WN = 2;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  using OA = DtlOperand<BM, A_KC>;
+  using OB = DtlOperand<BN, B_KC>;
+  constexpr int SA = OA::STAGE_BYTES, SB = OB::STAGE_BYTES, SS = SA + SB;
+  __shared__ __align__(1024) char smem[kStages * SS];
+
+  // ---- tile id: XCD-contiguous ranges, grouped by 8 tile rows ----
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int w = blockIdx.x;
+  const int xcd = w & 7, idx = w >> 3;
+  const int base = tiles >> 3, rem = tiles & 7;
+  const int L = xcd * base + min(xcd, rem) + idx;
+  const int group = kGroupM * p.tiles_n;
+  const int gq = L / group;
+  const int first_m = gq * kGroupM;
+  const int gm = min(p.tiles_m - first_m, kGroupM);
+  const int tm = first_m + (L % group) % gm;
+  const int tn = (L % group) / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int split = blockIdx.y;
+  const int kbeg = split * p.k_chunk;
+  const int kend = min(p.K, kbeg + p.k_chunk);
+  const int nk = (kend - kbeg + kBKd - 1) / kBKd;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const i32x4_t ra = rsrc_words(p.A, (uint32_t)((int64_t)p.M * p.K * 2));
+  const i32x4_t rb = rsrc_words(p.B, (uint32_t)((int64_t)p.K * p.N * 2));
+  OA oa;
+  OB ob;
+  oa.init(wave, lane);
+  ob.init(wave, lane);
+
+  // fragment offsets within a stage (substep 0; substep 1 adds a constant)
+  int aoff[FM], boff[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    aoff[i] = A_KC ? kc_frag_off(wm * FM + i, 0, lane) : mn_frag_off<OA::RB>(wm * FM + i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    boff[j] = SA + (B_KC ? kc_frag_off(wn * FN + j, 0, lane) : mn_frag_off<OB::RB>(wn * FN + j, 0, lane));
+  // substep 1 offset: KC: chunk 2s+g -> the XOR with a lane constant of (2 + ...) ; handled by recomputing
+  int aoff1[FM], boff1[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    aoff1[i] = A_KC ? kc_frag_off(wm * FM + i, 1, lane) : mn_frag_off<OA::RB>(wm * FM + i, 1, lane);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    boff1[j] = SA + (B_KC ? kc_frag_off(wn * FN + j, 1, lane) : mn_frag_off<OB::RB>(wn * FN + j, 1, lane));
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  uint4 af[2][FM], bfr[2][FN];
+  auto read_frags = [&](const char* st, int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const char* q = st + (s ? aoff1[i] : aoff[i]);
+      if (A_KC) {
+        af[buf][i] = *reinterpret_cast<const uint4*>(q);
+      } else {
+        const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OA::RB);
+        af[buf][i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const char* q = st + (s ? boff1[j] : boff[j]);
+      if (B_KC) {
+        bfr[buf][j] = *reinterpret_cast<const uint4*>(q);
+      } else {
+        const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OB::RB);
+        bfr[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+  };
+  // Loads of K-tile t: its A half is issued during substep 1 of tile t-(S-1),
+  // its B half during substep 0 of tile t-(S-2), one load after every few
+  // MFMAs so the issue cost hides under the matrix core. Stage t % S is free
+  // once every wave has passed the barrier of tile t-(S-1) (they have all
+  // finished tile t-S by then).
+  constexpr int S = kStages;
+  static_assert(OA::PER_WAVE == OB::PER_WAVE, "square tiles");
+  constexpr int ND = OA::PER_WAVE;          // loads per half tile per lane
+  constexpr int NM = FM * FN;               // MFMAs per substep
+  static_assert(NM % ND == 0, "interleave");
+  auto load_a = [&](int t, int u) {
+    char* st = smem + (t % S) * SS;
+    oa.load_one(u, ra, p.lda, m0, p.M, kbeg + t * kBKd, kend, st, wave);
+  };
+  auto load_b = [&](int t, int u) {
+    char* st = smem + (t % S) * SS;
+    ob.load_one(u, rb, p.ldb, n0, p.N, kbeg + t * kBKd, kend, st + SA, wave);
+  };
+  // the MFMAs of one substep with the loads of one half tile (t < 0: none) woven in
+  auto mfmas_with = [&](int buf, int t, bool half_a) {
+#pragma unroll
+    for (int idx = 0; idx < NM; ++idx) {
+      Mfma<bf16_t>::run(af[buf][idx / FN], bfr[buf][idx % FN], acc[idx / FN][idx % FN]);
+      if ((idx + 1) % (NM / ND) == 0 && t >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (half_a) load_a(t, (idx + 1) / (NM / ND) - 1);
+        else load_b(t, (idx + 1) / (NM / ND) - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  // s_waitcnt immediate for vmcnt(n) alone (expcnt and lgkmcnt at their maxima);
+  // vmcnt is 6 bits, low 4 in [3:0], high 2 in [15:14]
+  constexpr int W0 = 0x0F70;
+  static_assert((2 * (S - 3) + 1) * ND < 64, "vmcnt is 6 bits");
+  // wait until at most h half-tiles of this lane's loads are outstanding
+  auto wait_halves = [&](int h) {
+#define MTNLG_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+    switch (h) {
+      case 0: MTNLG_VM(0); break;
+      case 1: MTNLG_VM(ND); break;
+      case 2: MTNLG_VM(2 * ND); break;
+      case 3: MTNLG_VM(3 * ND); break;
+      case 4: MTNLG_VM(4 * ND); break;
+      default: MTNLG_VM(5 * ND); break;
+    }
+#undef MTNLG_VM
+  };
+  static_assert(2 * (S - 3) + 1 <= 5, "extend wait_halves");
+
+  // prologue: tiles 0 .. S-3 whole and the A half of tile S-2; then tile 0 must be complete
+  for (int t = 0; t < S - 2 && t < nk; ++t)
+    for (int u = 0; u < ND; ++u) { load_a(t, u); load_b(t, u); }
+  if (S - 2 < nk)
+    for (int u = 0; u < ND; ++u) load_a(S - 2, u);
+  if (nk > 0) {
+    const int whole = min(nk - 1, S - 3);                 // tiles 1 .. S-3 that exist
+    wait_halves(2 * whole + (S - 2 < nk ? 1 : 0));
+    __syncthreads();
+    read_frags(smem, 0, 0);
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* st = smem + (kt % S) * SS;
+    read_frags(st, 1, 1);
+    mfmas_with(0, kt + S - 2 < nk ? kt + S - 2 : -1, false);   // B half of tile kt+S-2
+    // publish tile kt+1: tiles kt+2 .. kt+S-2 may still be in flight
+    if (kt + 1 < nk) wait_halves(2 * min(nk - 2 - kt, S - 3));
+    __syncthreads();
+    if (kt + 1 < nk) read_frags(smem + ((kt + 1) % S) * SS, 0, 0);
+    mfmas_with(1, kt + S - 1 < nk ? kt + S - 1 : -1, true);    // A half of tile kt+S-1
+  }
+
+  // ---- epilogue (as in the register-staged kernel) ----
+  __builtin_amdgcn_s_waitcnt(W0);  // no load may still be writing LDS (all waited above)
+  __syncthreads();
+  constexpr int SROW = TN + 4;
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
+  const int lrow = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stage[(8 * blk + 4 * lg + r) * SROW + j * 32 + lrow] = acc[i][j][blk * 4 + r];
+    __syncthreads();
+    epilogue_slab<bf16_t, TN, SROW>(p, stage, m0 + wm * TM + i * 32, n0 + wn * TN, lane, split);
     __syncthreads();
   }
 }
@@ -341,19 +696,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   store8(C + i8, s);
 }
 
-template <typename T, int BM, int BN, bool AK, bool BKc>
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKc>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
   dim3 grid(a.tiles_m * a.tiles_n, a.splits);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AK, BKc>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKc>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN>
+template <int BM, int BN, bool AK, bool BKc>
+hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
+  dim3 grid(a.tiles_m * a.tiles_n, a.splits);
+  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_dtl_layout(const GemmArgs& a, bool a_kc, bool b_kc, hipStream_t st) {
+  if (a_kc && !b_kc) return launch_dtl<BM, BN, true, false>(a, st);
+  if (a_kc && b_kc) return launch_dtl<BM, BN, true, true>(a, st);
+  if (!a_kc && !b_kc) return launch_dtl<BM, BN, false, false>(a, st);
+  return launch_dtl<BM, BN, false, true>(a, st);
+}
+
+template <typename T, int BM, int BN, int WM, int WN>
 hipError_t launch_layout(const GemmArgs& a, bool a_kc, bool b_kc, hipStream_t st) {
-  if (a_kc && !b_kc) return launch_tile<T, BM, BN, true, false>(a, st);
-  if (a_kc && b_kc) return launch_tile<T, BM, BN, true, true>(a, st);
-  if (!a_kc && !b_kc) return launch_tile<T, BM, BN, false, false>(a, st);
-  return launch_tile<T, BM, BN, false, true>(a, st);
+  if (a_kc && !b_kc) return launch_tile<T, BM, BN, WM, WN, true, false>(a, st);
+  if (a_kc && b_kc) return launch_tile<T, BM, BN, WM, WN, true, true>(a, st);
+  if (!a_kc && !b_kc) return launch_tile<T, BM, BN, WM, WN, false, false>(a, st);
+  return launch_tile<T, BM, BN, WM, WN, false, true>(a, st);
 }
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -370,7 +740,7 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split)
     } else {
       pl.bm = pl.bn = 128;
     }
-    pl.bk = 64;
+    pl.bk = kBKd;
   } else {
     pl.bm = pl.bn = (M >= 1024 && N >= 1024) ? 128 : 64;
     pl.bk = 32;
@@ -415,11 +785,11 @@ hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K
   }
   hipError_t e;
   if (dtype == kBF16) {
-    if (pl.bm == 256) e = launch_layout<bf16_t, 256, 256>(a, a_kc, b_kc, st);
-    else e = launch_layout<bf16_t, 128, 128>(a, a_kc, b_kc, st);
+    if (pl.bm == 256) e = launch_dtl_layout<256, 256>(a, a_kc, b_kc, st);
+    else e = launch_dtl_layout<128, 128>(a, a_kc, b_kc, st);
   } else {
-    if (pl.bm == 128) e = launch_layout<float, 128, 128>(a, a_kc, b_kc, st);
-    else e = launch_layout<float, 64, 64>(a, a_kc, b_kc, st);
+    if (pl.bm == 128) e = launch_layout<float, 128, 128, 2, 2>(a, a_kc, b_kc, st);
+    else e = launch_layout<float, 64, 64, 2, 2>(a, a_kc, b_kc, st);
   }
   if (e != hipSuccess || !split) return e;
   const int64_t MN = M * N;
