@@ -220,20 +220,21 @@ def gemm_breakdown(torch, tst, dev, T, h, wl, fl, reps=10):
         a = torch.randn((K, M) if ta else (M, K), device=dev, generator=gen).to(torch.bfloat16)
         b = torch.randn((N, K) if tb else (K, N), device=dev, generator=gen).to(torch.bfloat16)
         c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(tst.gemm_workspace_bytes(tst.BF16, M, N, K), 16), dtype=torch.uint8, device=dev)
         for _ in range(2):
-            tst.gemm(a, b, c, bool(ta), bool(tb))
+            tst.gemm(a, b, c, bool(ta), bool(tb), ws=ws)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s.record()
         for _ in range(reps):
-            tst.gemm(a, b, c, bool(ta), bool(tb))
+            tst.gemm(a, b, c, bool(ta), bool(tb), ws=ws)
         e.record()
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / reps
         fl_ = 2.0 * M * N * K
         rows.append({"name": name, "M": M, "N": N, "K": K, "layout": f"{'T' if ta else 'N'}{'T' if tb else 'N'}",
                      "ms": ms, "tflops": fl_ / (ms * 1e-3) / 1e12, "flop": fl_})
-        del a, b, c
+        del a, b, c, ws
     return rows
 
 

@@ -116,7 +116,7 @@ typedef struct { void *ln_g, *ln_b, *w_in, *b_in, *w_out, *b_out; } mtnlg_half_g
 size_t mtnlg_saved_bytes(const mtnlg_layer_desc* desc, int32_t half);
 
 /* Size in bytes of the scratch workspace layer_fwd / layer_bwd need for
- * this descriptor and half (the larger of the two); 0 if invalid. */
+ * this descriptor and half (one size serves both); 0 if invalid. */
 size_t mtnlg_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half);
 
 /* Forward of one slice of one half.
@@ -193,12 +193,18 @@ int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* 
 
 /* ---- Component entry points (the kernels the layer calls, one at a time) ---- */
 
-/* C[M,N] = op(A) op(B) (+ bias[n]) in dtype, fp32 accumulation.
+/* C[M,N] = op(A) op(B) (+ bias[n]) in dtype, fp32 accumulation -- the GEMM
+ * every linear of the layer runs on.
  *   trans_a = 0: A is [M, K] row-major; 1: A is stored [K, M] (op(A) = A^T).
  *   trans_b = 0: B is [K, N] row-major; 1: B is stored [N, K] (op(B) = B^T).
- *   bias nullable. M, N, K >= 1 and multiples of 8. */
+ *   bias nullable. M, N, K multiples of 8, each operand below 2 GiB.
+ *   ws: mtnlg_gemm_workspace_bytes(...) bytes (fp32 partials of the tiles
+ *   that are split along K to fill the last round of workgroups); may be NULL
+ *   when that size is 0. */
+size_t mtnlg_gemm_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K);
 int mtnlg_gemm(int32_t dtype, int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K,
-               const void* A, const void* B, void* C, const void* bias, void* stream);
+               const void* A, const void* B, void* C, const void* bias, void* ws, size_t ws_bytes,
+               void* stream);
 
 /* Row LayerNorm of x [rows, cols] (the oracle's layernorm_fwd):
  * y = gamma*(x-mean)*rstd + beta; mean, rstd [rows] f32. cols multiple of 8. */

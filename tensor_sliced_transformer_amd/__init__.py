@@ -17,7 +17,7 @@ from ._lib import ATTN, MLP, BF16, F32, AdamCfg, HalfGrads, HalfParams, LayerDes
 
 __all__ = ["ATTN", "MLP", "BF16", "F32", "LayerDesc", "AdamCfg", "MtnlgError", "load", "make_desc",
            "saved_bytes", "workspace_bytes", "layer_fwd", "layer_bwd", "reduce_partials",
-           "grad_accumulate", "adam_workspace_bytes", "adam_step", "gemm", "layernorm_fwd",
+           "grad_accumulate", "adam_workspace_bytes", "adam_step", "gemm", "gemm_workspace_bytes", "layernorm_fwd",
            "layernorm_bwd_workspace_bytes", "layernorm_bwd", "attention_fwd",
            "attention_bwd_workspace_bytes", "attention_bwd", "torch_dtype"]
 
@@ -119,12 +119,18 @@ def adam_step(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None) 
                                  _stream(stream)), "mtnlg_adam_step")
 
 
-def gemm(a, b, c, trans_a=False, trans_b=False, bias=None, stream=None) -> None:
-    """c = op(a) op(b) (+ bias) (mtnlg_gemm)."""
+def gemm_workspace_bytes(dtype: int, M: int, N: int, K: int) -> int:
+    return int(load().mtnlg_gemm_workspace_bytes(dtype, M, N, K))
+
+
+def gemm(a, b, c, trans_a=False, trans_b=False, bias=None, ws=None, stream=None) -> None:
+    """c = op(a) op(b) (+ bias) (mtnlg_gemm). ws: a uint8 tensor of at least
+    gemm_workspace_bytes(...) bytes, or None when that is 0."""
     M, N = c.shape
     K = a.shape[0] if trans_a else a.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(load().mtnlg_gemm(_code(c), int(trans_a), int(trans_b), M, N, K, _ptr(a), _ptr(b), _ptr(c), _ptr(bias),
-                            _stream(stream)), "mtnlg_gemm")
+                            _ptr(ws), ws_bytes, _stream(stream)), "mtnlg_gemm")
 
 
 def layernorm_fwd(x, gamma, beta, eps, y, mean, rstd, stream=None) -> None:

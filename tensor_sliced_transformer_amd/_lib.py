@@ -54,8 +54,9 @@ SIGNATURES = {
     "mtnlg_adam_workspace_bytes": (c_size_t, [c_int64]),
     "mtnlg_adam_step": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mtnlg_gemm_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, c_int64]),
     "mtnlg_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
-                             c_void_p, c_void_p, c_void_p]),
+                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mtnlg_layernorm_fwd": (c_int32, [c_int32, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_float,
                                       c_void_p, c_void_p, c_void_p, c_void_p]),
     "mtnlg_layernorm_bwd_workspace_bytes": (c_size_t, [c_int64, c_int64]),

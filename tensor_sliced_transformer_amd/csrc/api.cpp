@@ -128,20 +128,41 @@ SavedLayout saved_layout(const Dims& d, int half) {
   return L;
 }
 
-// ---- workspace layout (backward; the forward needs none) ----
+// ---- GEMMs of each half: (M, N, K) of the forward and backward products ----
+struct Shape3 { int64_t M, N, K; };
+int half_gemms(const Dims& d, int half, Shape3* out) {
+  if (half == MTNLG_ATTN) {
+    const int64_t n3 = 3 * d.w;
+    const Shape3 g[6] = {{d.T, n3, d.h}, {d.T, d.h, d.w}, {d.T, d.w, d.h},
+                         {d.w, d.h, d.T}, {d.h, n3, d.T}, {d.T, d.h, n3}};
+    for (int i = 0; i < 6; ++i) out[i] = g[i];
+    return 6;
+  }
+  const Shape3 g[6] = {{d.T, d.fl, d.h}, {d.T, d.h, d.fl}, {d.T, d.fl, d.h},
+                       {d.fl, d.h, d.T}, {d.h, d.fl, d.T}, {d.T, d.h, d.fl}};
+  for (int i = 0; i < 6; ++i) out[i] = g[i];
+  return 6;
+}
+
+// ---- workspace layout ----
+// gemm: fp32 partials of a GEMM's tail tiles (one GEMM at a time; forward and
+// backward); the rest is backward-only scratch.
 struct WsLayout {
-  size_t t1, t2, dln, lnp, cs, split, attn, total;
-  GemmPlan dplan;  // plan of the split-K dgrad (ATTN dO)
+  size_t gemm, t1, t2, dln, lnp, cs, attn, total;
 };
 
 WsLayout ws_layout(const Dims& d, int half) {
   WsLayout L{};
   size_t off = 0;
+  Shape3 g[6];
+  const int ng = half_gemms(d, half, g);
+  size_t gws = 0;
+  for (int i = 0; i < ng; ++i)
+    gws = std::max(gws, gemm_workspace_bytes(plan_gemm(d.dtype, g[i].M, g[i].N, g[i].K, true), g[i].M, g[i].N));
+  L.gemm = off; off = align256(off + gws);
   if (half == MTNLG_ATTN) {
-    L.dplan = plan_gemm(d.dtype, d.T, d.w, d.h, true);
     L.t1 = off; off = align256(off + d.T * d.w * d.eb);        // dO
     L.t2 = off; off = align256(off + d.T * 3 * d.w * d.eb);    // dQKV
-    L.split = off; off = align256(off + gemm_workspace_bytes(L.dplan, d.T, d.w));
     L.attn = off; off = align256(off + attention_bwd_ws(1, (int)d.T, (int)d.nhl));
   } else {
     L.t1 = off; off = align256(off + d.T * d.fl * d.eb);       // dU
@@ -195,8 +216,6 @@ int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
   Dims d;
   int s = validate_desc(desc, half, &d);
   if (s != MTNLG_OK) return s;
-  (void)ws;
-  (void)ws_bytes;  // the forward needs no scratch
   if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
   CHECK_PTR(params->ln_g);
   CHECK_PTR(params->ln_b);
@@ -206,6 +225,13 @@ int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
   CHECK_PTR(x);
   CHECK_PTR(y_partial);
   CHECK_PTR(saved);
+  const WsLayout W = ws_layout(d, half);
+  const size_t need = W.t1;  // the forward uses only the GEMM partial region, which comes first
+  if (need > 0) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  }
+  void* gws = need > 0 ? at(ws, W.gemm) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const SavedLayout L = saved_layout(d, half);
   void* ln_out = at(saved, L.ln_out);
@@ -219,21 +245,21 @@ int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
     float* lse = reinterpret_cast<float*>(at(saved, L.c));
     const int64_t n3 = 3 * d.w;
     MTNLG_HIP(gemm(d.dtype, true, false, d.T, n3, d.h, ln_out, d.h, params->w_in, n3, qkv, n3, EPI_BIAS,
-                   params->b_in, nullptr, nullptr, plan_gemm(d.dtype, d.T, n3, d.h, false), nullptr, st),
+                   params->b_in, nullptr, nullptr, plan_gemm(d.dtype, d.T, n3, d.h, true), gws, st),
               "qkv gemm");
     MTNLG_HIP(attention_fwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, st),
               "attention_fwd");
     MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.w, o, d.w, params->w_out, d.h, y_partial, d.h, EPI_STORE,
-                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.w, false), nullptr, st),
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.w, true), gws, st),
               "out-proj gemm");
   } else {
     void* u = at(saved, L.a);
     void* y = at(saved, L.b);
     MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.fl, d.h, ln_out, d.h, params->w_in, d.fl, u, d.fl, EPI_BIAS_GELU,
-                   params->b_in, y, nullptr, plan_gemm(d.dtype, d.T, d.fl, d.h, false), nullptr, st),
+                   params->b_in, y, nullptr, plan_gemm(d.dtype, d.T, d.fl, d.h, true), gws, st),
               "mlp-up gemm");
     MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.fl, y, d.fl, params->w_out, d.h, y_partial, d.h, EPI_STORE,
-                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, false), nullptr, st),
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, true), gws, st),
               "mlp-down gemm");
   }
   return MTNLG_OK;
@@ -274,6 +300,7 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
   const float* rstd = reinterpret_cast<const float*>(at(saved, L.rstd));
   void* dln = at(ws, W.dln);
   void* cs = at(ws, W.cs);
+  void* gws = at(ws, W.gemm);
 
   MTNLG_HIP(colsum(d.dtype, d.T, d.h, dy, grads->b_out, cs, st), "b_out colsum");
   if (half == MTNLG_MLP) {
@@ -282,20 +309,20 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
     void* du = at(ws, W.t1);
     // dU = (dy B^T) * GeLU'(u)
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.fl, d.h, dy, d.h, params->w_out, d.h, du, d.fl, EPI_GELU_GRAD,
-                   nullptr, nullptr, u, plan_gemm(d.dtype, d.T, d.fl, d.h, false), nullptr, st),
+                   nullptr, nullptr, u, plan_gemm(d.dtype, d.T, d.fl, d.h, true), gws, st),
               "mlp dY gemm");
     // dB = Y^T dy
     MTNLG_HIP(gemm(d.dtype, false, false, d.fl, d.h, d.T, y, d.fl, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.fl, d.h, d.T, false), nullptr, st),
+                   nullptr, nullptr, plan_gemm(d.dtype, d.fl, d.h, d.T, true), gws, st),
               "mlp dB gemm");
     MTNLG_HIP(colsum(d.dtype, d.T, d.fl, du, grads->b_in, cs, st), "mlp da colsum");
     // dA = LN2(x)^T dU
     MTNLG_HIP(gemm(d.dtype, false, false, d.h, d.fl, d.T, ln_out, d.h, du, d.fl, grads->w_in, d.fl, EPI_STORE,
-                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, d.fl, d.T, false), nullptr, st),
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, d.fl, d.T, true), gws, st),
               "mlp dA gemm");
     // dLN = dU A^T
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.h, d.fl, du, d.fl, params->w_in, d.fl, dln, d.h, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, false), nullptr, st),
+                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, true), gws, st),
               "mlp dX gemm");
   } else {
     const void* qkv = at(saved, L.a);
@@ -306,11 +333,11 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
     const int64_t n3 = 3 * d.w;
     // dO = dy W_o^T (short N: split K)
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.w, d.h, dy, d.h, params->w_out, d.h, dO, d.w, EPI_STORE, nullptr,
-                   nullptr, nullptr, W.dplan, at(ws, W.split), st),
+                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.w, d.h, true), gws, st),
               "attn dO gemm");
     // dW_o = O^T dy
     MTNLG_HIP(gemm(d.dtype, false, false, d.w, d.h, d.T, o, d.w, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, d.T, false), nullptr, st),
+                   nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, d.T, true), gws, st),
               "attn dWo gemm");
     MTNLG_HIP(attention_bwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, dO, dqkv,
                             at(ws, W.attn), st),
@@ -318,11 +345,11 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
     MTNLG_HIP(colsum(d.dtype, d.T, n3, dqkv, grads->b_in, cs, st), "attn dbqkv colsum");
     // dW_qkv = LN1(x)^T dQKV
     MTNLG_HIP(gemm(d.dtype, false, false, d.h, n3, d.T, ln_out, d.h, dqkv, n3, grads->w_in, n3, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.h, n3, d.T, false), nullptr, st),
+                   nullptr, nullptr, plan_gemm(d.dtype, d.h, n3, d.T, true), gws, st),
               "attn dWqkv gemm");
     // dLN = dQKV W_qkv^T
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.h, n3, dqkv, n3, params->w_in, n3, dln, d.h, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, n3, false), nullptr, st),
+                   nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, n3, true), gws, st),
               "attn dX gemm");
   }
   MTNLG_HIP(layernorm_bwd(d.dtype, d.dtype, d.T, d.h, dln, x, mean, rstd, params->ln_g, dx_partial, grads->ln_g,
@@ -396,21 +423,38 @@ int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* 
   return MTNLG_OK;
 }
 
+static bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+  // every operand must stay below 2 GiB (32-bit buffer offsets)
+  return M >= 8 && N >= 8 && K >= 8 && M % 8 == 0 && N % 8 == 0 && K % 8 == 0 && M * K < (1LL << 30) &&
+         K * N < (1LL << 30) && M * N < (1LL << 30);
+}
+
+size_t mtnlg_gemm_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K) {
+  if ((dtype != MTNLG_F32 && dtype != MTNLG_BF16) || !gemm_shape_ok(M, N, K)) return 0;
+  return gemm_workspace_bytes(plan_gemm(dtype, M, N, K, true), M, N);
+}
+
 int mtnlg_gemm(int32_t dtype, int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, const void* A,
-               const void* B, void* C, const void* bias, void* stream) {
+               const void* B, void* C, const void* bias, void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
-  if (M < 8 || N < 8 || K < 8 || M % 8 || N % 8 || K % 8 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
-    return fail(MTNLG_ERR_SHAPE, "M, N, K must be positive multiples of 8");
+  if (!gemm_shape_ok(M, N, K))
+    return fail(MTNLG_ERR_SHAPE, "M, N, K must be positive multiples of 8 with operands below 2 GiB");
   CHECK_PTR(A);
   CHECK_PTR(B);
   CHECK_PTR(C);
   if (bias) CHECK_PTR(bias);
+  const GemmPlan pl = plan_gemm(dtype, M, N, K, true);
+  const size_t need = gemm_workspace_bytes(pl, M, N);
+  if (need > 0) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  }
   const bool a_kc = trans_a == 0, b_kc = trans_b != 0;
   const int64_t lda = a_kc ? K : M;
   const int64_t ldb = b_kc ? K : N;
   MTNLG_HIP(gemm(dtype, a_kc, b_kc, M, N, K, A, lda, B, ldb, C, N, bias ? EPI_BIAS : EPI_STORE, bias, nullptr,
-                 nullptr, plan_gemm(dtype, M, N, K, false), nullptr, static_cast<hipStream_t>(stream)),
+                 nullptr, pl, need > 0 ? ws : nullptr, static_cast<hipStream_t>(stream)),
             "gemm");
   return MTNLG_OK;
 }

@@ -154,61 +154,104 @@ struct TileLoader {
   }
 };
 
-// Epilogue over a staged 32 x WN fp32 slab (row stride SROW floats): each lane
-// takes 8-wide row vectors, applies the epilogue and stores 16 bytes (bf16) or
-// 32 bytes (fp32). Not unrolled: it touches no register arrays.
-template <typename T, int WN, int SROW>
-__device__ __forceinline__ void epilogue_slab(const GemmArgs& p, const float* stage, int row0, int col0, int lane,
-                                              int split) {
-  using E = Elem<T>;
+// Applies the epilogue to the 8 consecutive fp32 values v of row `row`,
+// columns col..col+7 (in range), and stores them.
+template <typename T>
+__device__ __forceinline__ void apply_epi_store(const GemmArgs& p, int row, int col, float* v) {
+  const int64_t off = (int64_t)row * p.ldc + col;
+  switch (p.epi) {
+    case EPI_GELU_GRAD: {
+      float u8[8];
+      load8(static_cast<const T*>(p.aux) + off, u8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_f(u8[e]);
+      store8(static_cast<T*>(p.C) + off, v);
+      break;
+    }
+    case EPI_BIAS_GELU: {
+      float b8[8], y8[8];
+      load8(static_cast<const T*>(p.bias) + col, b8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] += b8[e];
+        y8[e] = gelu_f(v[e]);
+      }
+      store8(static_cast<T*>(p.C) + off, v);
+      store8(static_cast<T*>(p.C2) + off, y8);
+      break;
+    }
+    case EPI_BIAS: {
+      float b8[8];
+      load8(static_cast<const T*>(p.bias) + col, b8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += b8[e];
+      store8(static_cast<T*>(p.C) + off, v);
+      break;
+    }
+    default:
+      store8(static_cast<T*>(p.C) + off, v);
+  }
+}
+
+// Epilogue over a staged 32 x WN fp32 slab (row stride SROW floats) whose
+// first element is tile-local (rl0, cl0) of the tile at (m0, n0): each lane
+// takes 8-wide row vectors and either applies the epilogue (whole tile) or
+// stores the raw fp32 values into the tile-major partial `pt` (BN wide) of a
+// tail piece. Not unrolled: it touches no register arrays.
+template <typename T, int WN, int SROW, int BN>
+__device__ __forceinline__ void epilogue_slab(const GemmArgs& p, const float* stage, int m0, int n0, int rl0,
+                                              int cl0, int lane, float* pt) {
   constexpr int VPR = WN / 8;  // vectors per slab row
 #pragma unroll 1
   for (int u = lane; u < 32 * VPR; u += kWave) {
     const int rr = u / VPR, cc = (u % VPR) * 8;
-    const int row = row0 + rr, col = col0 + cc;
-    if (row >= p.M || col >= p.N) continue;
     float v[8];
     const float4 a = *reinterpret_cast<const float4*>(stage + rr * SROW + cc);
     const float4 b = *reinterpret_cast<const float4*>(stage + rr * SROW + cc + 4);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    const int64_t off = (int64_t)row * p.ldc + col;
-    switch (p.epi) {
-      case EPI_F32_PARTIAL:
-        store8(static_cast<float*>(p.C) + (int64_t)split * p.M * p.N + (int64_t)row * p.N + col, v);
-        break;
-      case EPI_GELU_GRAD: {
-        float u8[8];
-        load8(static_cast<const T*>(p.aux) + off, u8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_f(u8[e]);
-        store8(static_cast<T*>(p.C) + off, v);
-        break;
-      }
-      case EPI_BIAS_GELU: {
-        float b8[8], y8[8];
-        load8(static_cast<const T*>(p.bias) + col, b8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[e] += b8[e];
-          y8[e] = gelu_f(v[e]);
-        }
-        store8(static_cast<T*>(p.C) + off, v);
-        store8(static_cast<T*>(p.C2) + off, y8);
-        break;
-      }
-      case EPI_BIAS: {
-        float b8[8];
-        load8(static_cast<const T*>(p.bias) + col, b8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += b8[e];
-        store8(static_cast<T*>(p.C) + off, v);
-        break;
-      }
-      default:
-        store8(static_cast<T*>(p.C) + off, v);
+    if (pt) {
+      store8(pt + (int64_t)(rl0 + rr) * BN + cl0 + cc, v);
+      continue;
     }
+    const int row = m0 + rl0 + rr, col = n0 + cl0 + cc;
+    if (row >= p.M || col >= p.N) continue;
+    apply_epi_store<T>(p, row, col, v);
   }
+}
+
+// Tile index L, K range and tail piece (split < 0: whole tile) of workgroup w.
+struct TileWork {
+  int tm, tn, split, tl, kbeg, kend;
+};
+__device__ __forceinline__ TileWork tile_work(const GemmArgs& p, int w) {
+  TileWork t;
+  int L;
+  if (w < p.nfull) {
+    // XCD-contiguous ranges: consecutive ids go round-robin over 8 XCDs
+    const int xcd = w & 7, idx = w >> 3;
+    const int base = p.nfull >> 3, rem = p.nfull & 7;
+    L = xcd * base + min(xcd, rem) + idx;
+    t.split = -1;
+    t.tl = 0;
+    t.kbeg = 0;
+    t.kend = p.K;
+  } else {
+    const int u = w - p.nfull;
+    t.tl = u % p.tail_tiles;
+    t.split = u / p.tail_tiles;
+    L = p.nfull + t.tl;
+    t.kbeg = t.split * p.k_chunk;
+    t.kend = min(p.K, t.kbeg + p.k_chunk);
+  }
+  // groups of kGroupM tile rows, walked column by column
+  const int group = kGroupM * p.tiles_n;
+  const int gq = L / group;
+  const int first_m = gq * kGroupM;
+  const int gm = min(p.tiles_m - first_m, kGroupM);
+  t.tm = first_m + (L % group) % gm;
+  t.tn = (L % group) / gm;
+  return t;
 }
 
 template <typename T> struct Mfma;
@@ -244,24 +287,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   uint4* const sA0 = smem;                        // two A stages, then two B stages
   uint4* const sB0 = smem + 2 * BM * kCH;
 
-  // ---- tile id: XCD-contiguous ranges, grouped by 8 tile rows ----
-  const int tiles = p.tiles_m * p.tiles_n;
-  const int w = blockIdx.x;
-  const int xcd = w & 7, idx = w >> 3;
-  const int base = tiles >> 3, rem = tiles & 7;
-  const int L = xcd * base + min(xcd, rem) + idx;
-  const int group = kGroupM * p.tiles_n;
-  const int g = L / group;
-  const int first_m = g * kGroupM;
-  const int gm = min(p.tiles_m - first_m, kGroupM);
-  const int tm = first_m + (L % group) % gm;
-  const int tn = (L % group) / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const int split = blockIdx.y;
-  const int kbeg = split * p.k_chunk;
-  const int kend = min(p.K, kbeg + p.k_chunk);
+  const TileWork tw = tile_work(p, blockIdx.x);
+  const int m0 = tw.tm * BM, n0 = tw.tn * BN;
+  const int kbeg = tw.kbeg, kend = tw.kend;
   const int nk = (kend - kbeg + BK - 1) / BK;
+  float* const pt = tw.split >= 0 ? p.part + ((int64_t)tw.split * p.tail_tiles + tw.tl) * BM * BN : nullptr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -360,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) stage[(8 * blk + 4 * lg + r) * SROW + j * 32 + lrow] = acc[i][j][blk * 4 + r];
     __syncthreads();
-    epilogue_slab<T, TN, SROW>(p, stage, m0 + wm * TM + i * 32, n0 + wn * TN, lane, split);
+    epilogue_slab<T, TN, SROW, BN>(p, stage, m0, n0, wm * TM + i * 32, wn * TN, lane, pt);
     __syncthreads();
   }
 }
@@ -501,24 +531,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dtl_kernel(GemmArgs p) {
   constexpr int SA = OA::STAGE_BYTES, SB = OB::STAGE_BYTES, SS = SA + SB;
   __shared__ __align__(1024) char smem[kStages * SS];
 
-  // ---- tile id: XCD-contiguous ranges, grouped by 8 tile rows ----
-  const int tiles = p.tiles_m * p.tiles_n;
-  const int w = blockIdx.x;
-  const int xcd = w & 7, idx = w >> 3;
-  const int base = tiles >> 3, rem = tiles & 7;
-  const int L = xcd * base + min(xcd, rem) + idx;
-  const int group = kGroupM * p.tiles_n;
-  const int gq = L / group;
-  const int first_m = gq * kGroupM;
-  const int gm = min(p.tiles_m - first_m, kGroupM);
-  const int tm = first_m + (L % group) % gm;
-  const int tn = (L % group) / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const int split = blockIdx.y;
-  const int kbeg = split * p.k_chunk;
-  const int kend = min(p.K, kbeg + p.k_chunk);
+  const TileWork tw = tile_work(p, blockIdx.x);
+  const int m0 = tw.tm * BM, n0 = tw.tn * BN;
+  const int kbeg = tw.kbeg, kend = tw.kend;
   const int nk = (kend - kbeg + kBKd - 1) / kBKd;
+  float* const pt = tw.split >= 0 ? p.part + ((int64_t)tw.split * p.tail_tiles + tw.tl) * BM * BN : nullptr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -666,46 +683,45 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dtl_kernel(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) stage[(8 * blk + 4 * lg + r) * SROW + j * 32 + lrow] = acc[i][j][blk * 4 + r];
     __syncthreads();
-    epilogue_slab<bf16_t, TN, SROW>(p, stage, m0 + wm * TM + i * 32, n0 + wn * TN, lane, split);
+    epilogue_slab<bf16_t, TN, SROW, BN>(p, stage, m0, n0, wm * TM + i * 32, wn * TN, lane, pt);
     __syncthreads();
   }
 }
 
-// Sum of split-K partials [splits][M][N] f32 -> C (dtype), with optional bias.
-template <typename T>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            int64_t MN, int N, const T* __restrict__ bias,
-                                                            T* __restrict__ C) {
-  const int64_t i8 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  if (i8 >= MN) return;
+// Sums the tail pieces of each tail tile (fixed order over the splits) and
+// applies the epilogue: one thread per 8-wide row vector of a tail tile.
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
+  constexpr int VPT = BM * BN / 8;  // vectors per tile
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)p.tail_tiles * VPT) return;
+  const int tl = (int)(gid / VPT), v = (int)(gid % VPT);
+  const int rl = v / (BN / 8), cl = (v % (BN / 8)) * 8;
+  const TileWork tw = tile_work(p, p.nfull + tl);  // split 0 of tail tile tl
+  const int row = tw.tm * BM + rl, col = tw.tn * BN + cl;
+  if (row >= p.M || col >= p.N) return;
   float s[8];
-  load8(part + i8, s);
-  for (int z = 1; z < splits; ++z) {
+  const float* base = p.part + (int64_t)tl * BM * BN + (int64_t)rl * BN + cl;
+  load8(base, s);
+  for (int z = 1; z < p.tail_split; ++z) {
     float t[8];
-    load8(part + (int64_t)z * MN + i8, t);
+    load8(base + (int64_t)z * p.tail_tiles * BM * BN, t);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] += t[e];
   }
-  if (bias) {
-    const int col = (int)(i8 % N);
-    float b[8];
-    load8(bias + col, b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += b[e];
-  }
-  store8(C + i8, s);
+  apply_epi_store<T>(p, row, col, s);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKc>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
-  dim3 grid(a.tiles_m * a.tiles_n, a.splits);
+  dim3 grid(a.nfull + a.tail_tiles * a.tail_split);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKc>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 template <int BM, int BN, bool AK, bool BKc>
 hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
-  dim3 grid(a.tiles_m * a.tiles_n, a.splits);
+  dim3 grid(a.nfull + a.tail_tiles * a.tail_split);
   hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -745,20 +761,25 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split)
     pl.bm = pl.bn = (M >= 1024 && N >= 1024) ? 128 : 64;
     pl.bk = 32;
   }
-  const int64_t tiles = (int64_t)ceil_div(M, pl.bm) * ceil_div(N, pl.bn);
-  pl.splits = 1;
-  if (allow_split && tiles < num_cu) {
-    // split K so that roughly one full wave of workgroups runs, keeping >= 8 K tiles each
-    int s = (int)(num_cu / tiles);
+  pl.tiles = ceil_div(M, pl.bm) * ceil_div(N, pl.bn);
+  // Wave quantisation: one workgroup per CU (the LDS ring fills a CU), so the
+  // last round of tiles may leave most CUs idle. When at most half a round is
+  // left over, those tiles are split along K across the idle CUs.
+  const int tail = pl.tiles % num_cu;
+  if (allow_split && dtype == kBF16 && tail > 0 && tail <= num_cu / 2) {
     const int ktiles = ceil_div(K, pl.bk);
-    while (s > 1 && ktiles / s < 8) --s;
-    pl.splits = s < 1 ? 1 : s;
+    int s = num_cu / tail;
+    while (s > 1 && ktiles / s < 8) --s;  // keep >= 8 K-tiles per piece
+    if (s > 1) {
+      pl.tail_tiles = tail;
+      pl.tail_split = s;
+    }
   }
   return pl;
 }
 
-size_t gemm_workspace_bytes(const GemmPlan& pl, int64_t M, int64_t N) {
-  return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+size_t gemm_workspace_bytes(const GemmPlan& pl, int64_t, int64_t) {
+  return pl.tail_split > 1 ? (size_t)pl.tail_tiles * pl.tail_split * pl.bm * pl.bn * sizeof(float) : 0;
 }
 
 hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, const void* A,
@@ -773,16 +794,14 @@ hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K
   a.epi = epi;
   a.tiles_m = ceil_div(M, pl.bm);
   a.tiles_n = ceil_div(N, pl.bn);
-  a.splits = pl.splits;
+  const bool tail = pl.tail_split > 1 && ws != nullptr;
+  a.tail_tiles = tail ? pl.tail_tiles : 0;
+  a.tail_split = tail ? pl.tail_split : 1;
+  a.nfull = pl.tiles - a.tail_tiles;
   const int ktiles = ceil_div(K, pl.bk);
-  a.k_chunk = ceil_div(ktiles, pl.splits) * pl.bk;
-  const bool split = pl.splits > 1;
-  if (split) {
-    // real number of non-empty splits
-    a.splits = ceil_div(K, a.k_chunk);
-    a.epi = EPI_F32_PARTIAL;
-    a.C = ws;
-  }
+  a.k_chunk = ceil_div(ktiles, a.tail_split) * pl.bk;
+  if (tail) a.tail_split = ceil_div(K, a.k_chunk);   // non-empty pieces only
+  a.part = static_cast<float*>(ws);
   hipError_t e;
   if (dtype == kBF16) {
     if (pl.bm == 256) e = launch_dtl_layout<256, 256>(a, a_kc, b_kc, st);
@@ -791,18 +810,13 @@ hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K
     if (pl.bm == 128) e = launch_layout<float, 128, 128, 2, 2>(a, a_kc, b_kc, st);
     else e = launch_layout<float, 64, 64, 2, 2>(a, a_kc, b_kc, st);
   }
-  if (e != hipSuccess || !split) return e;
-  const int64_t MN = M * N;
-  const int blocks = ceil_div(MN / 8, 256);
-  const bool with_bias = epi == EPI_BIAS;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(splitk_reduce_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const float*>(ws), a.splits, MN, (int)N,
-                       with_bias ? static_cast<const bf16_t*>(bias) : nullptr, static_cast<bf16_t*>(C));
+  if (e != hipSuccess || !tail) return e;
+  const int64_t vec = (int64_t)a.tail_tiles * pl.bm * pl.bn / 8;
+  const int blocks = (int)((vec + 255) / 256);
+  if (pl.bm == 256)
+    hipLaunchKernelGGL((tail_reduce_kernel<bf16_t, 256, 256>), dim3(blocks), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const float*>(ws), a.splits, MN, (int)N,
-                       with_bias ? static_cast<const float*>(bias) : nullptr, static_cast<float*>(C));
+    hipLaunchKernelGGL((tail_reduce_kernel<bf16_t, 128, 128>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

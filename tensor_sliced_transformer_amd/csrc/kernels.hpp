@@ -17,8 +17,7 @@ enum GemmEpi {
   EPI_STORE = 0,       // C = acc
   EPI_BIAS = 1,        // C = acc + bias[n]
   EPI_BIAS_GELU = 2,   // C = u = acc + bias[n]; C2 = GeLU(u)
-  EPI_GELU_GRAD = 3,   // C = acc * GeLU'(aux[m, n])
-  EPI_F32_PARTIAL = 4  // fp32 split-K partial (internal)
+  EPI_GELU_GRAD = 3    // C = acc * GeLU'(aux[m, n])
 };
 
 struct GemmArgs {
@@ -32,11 +31,18 @@ struct GemmArgs {
   const void* aux;
   int epi;
   int tiles_m, tiles_n;
-  int splits, k_chunk;
+  // Tail split: tiles [0, nfull) (in the XCD/grouped order) are computed whole
+  // by the first nfull workgroups; the last tail_tiles tiles are each split
+  // tail_split ways along K (k_chunk per piece) into fp32 partials `part`
+  // (tile-major, [split][tail tile][BM][BN]) that a reduce kernel sums and
+  // passes through the epilogue.
+  int nfull, tail_tiles, tail_split, k_chunk;
+  float* part;
 };
 
 struct GemmPlan {
-  int bm = 256, bn = 256, bk = 64, splits = 1;
+  int bm = 256, bn = 256, bk = 32;
+  int tiles = 0, tail_tiles = 0, tail_split = 1;
 };
 
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split);

@@ -140,8 +140,13 @@ def test_other_entry_points_validate():
     assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 1 << 20, None) == -1   # beta1
     cfg = _lib.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 1)
     assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 8, None) == -5
-    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 12, 16, 16, A, A, A, None, None) == -2
-    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 16, 16, 16, None, A, A, None, None) == -1
+    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 12, 16, 16, A, A, A, None, None, 0, None) == -2
+    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 16, 16, 16, None, A, A, None, None, 0, None) == -1
+    # 2048 x 10240 tiles: the leftover round is split along K, so a workspace is required
+    need = L.mtnlg_gemm_workspace_bytes(_lib.BF16, 2048, 10240, 20480)
+    assert need == 64 * 4 * 256 * 256 * 4
+    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 2048, 10240, 20480, A, A, A, None, A, need - 1, None) == -5
+    assert L.mtnlg_gemm_workspace_bytes(_lib.BF16, 2048, 7680, 20480) == 0     # 240 tiles: one round
     assert L.mtnlg_layernorm_fwd(_lib.BF16, 4, 12, A, A, A, 1e-5, A, A, A, None) == -2
     assert L.mtnlg_attention_fwd(_lib.F32, 1, 128, 2, 160, A, A, A, None) == -2               # f32 hd 160
     assert L.mtnlg_attention_fwd(_lib.BF16, 1, 96, 2, 128, A, A, A, None) == -2

@@ -40,22 +40,26 @@ def test_gemm(dtype, ta, tb, shape):
     b = inputs(12, (N, K) if tb else (K, N), dtype)
     bias = inputs(13, (N,), dtype)
     c = empty((M, N), dtype)
-    tst.gemm(to_gpu(a, dtype), to_gpu(b, dtype), c, bool(ta), bool(tb), bias=to_gpu(bias, dtype))
+    ws = empty_bytes(tst.gemm_workspace_bytes(tst.BF16 if dtype == "bf16" else tst.F32, M, N, K))
+    tst.gemm(to_gpu(a, dtype), to_gpu(b, dtype), c, bool(ta), bool(tb), bias=to_gpu(bias, dtype), ws=ws)
     torch.cuda.synchronize()
     A = a.astype(np.float64).T if ta else a.astype(np.float64)
     B = b.astype(np.float64).T if tb else b.astype(np.float64)
     assert_close("C", to_np(c), A @ B + bias.astype(np.float64)[None, :], dtype)
 
 
-def test_gemm_large_tiles_bf16():
-    """256x256 tiles with several XCD groups: M = 2048, N = 2560, K = 1024."""
-    M, N, K = 2048, 2560, 1024
+@pytest.mark.parametrize("M,N,K", [(2048, 2560, 1024), (2048, 10240, 2048), (4096, 4096, 512)])
+def test_gemm_large_tiles_bf16(M, N, K):
+    """256x256 tiles with several XCD groups; 320 tiles (2048 x 10240) exercise the K-split
+    of the tiles left over after one round of 256 workgroups."""
     a = inputs(14, (M, K), "bf16")
     b = inputs(15, (K, N), "bf16")
+    bias = inputs(16, (N,), "bf16")
     c = empty((M, N), "bf16")
-    tst.gemm(to_gpu(a, "bf16"), to_gpu(b, "bf16"), c)
+    ws = empty_bytes(tst.gemm_workspace_bytes(tst.BF16, M, N, K))
+    tst.gemm(to_gpu(a, "bf16"), to_gpu(b, "bf16"), c, bias=to_gpu(bias, "bf16"), ws=ws)
     torch.cuda.synchronize()
-    assert_close("C", to_np(c), a.astype(np.float64) @ b.astype(np.float64), "bf16")
+    assert_close("C", to_np(c), a.astype(np.float64) @ b.astype(np.float64) + bias[None, :], "bf16")
 
 
 # ------------------------------------------------------------------ LayerNorm
