@@ -5,7 +5,7 @@ Usage: python -m tensor_sliced_transformer_amd.build [--jobs N]
 Every call recompiles all sources (the build check must compile each time);
 objects go to tensor_sliced_transformer_amd/_build/, the shared library next to
 this file. Device code is built for gfx950 only, with packed-fp32 instruction
-selection turned off.
+selection turned off (see EXTRA for per-file flags).
 """
 from __future__ import annotations
 
@@ -22,7 +22,12 @@ BUILD = os.path.join(HERE, "_build")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmtnlg.so")
 
-SOURCES = ["api.cpp", "gemm.hip", "layernorm.hip", "attention.hip", "stream.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "layernorm.hip", "attention.hip", "attention_bf16.hip",
+           "attention_bf16_dkdv.hip", "stream.hip"]
+# Per-source extra flags. The forward and dQ attention kernels keep their MFMA
+# accumulators in VGPRs, so that the softmax arithmetic on them needs no copies
+# between register files.
+EXTRA = {"attention_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -39,7 +44,7 @@ def hipcc() -> str:
 def _compile(src: str) -> tuple[str, str]:
     out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *lang, *COMMON, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [hipcc(), *lang, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -88,6 +88,8 @@ int validate_desc(const mtnlg_layer_desc* desc, int32_t half, Dims* out) {
   if (D.hidden % 16 || (D.ffn / D.tp_size) % 16) return fail(MTNLG_ERR_SHAPE, "hidden and ffn/tp must be multiples of 16");
   if (D.hidden > 32768) return fail(MTNLG_ERR_SHAPE, "hidden > 32768 unsupported");
   if (D.seq % 128) return fail(MTNLG_ERR_SHAPE, "seq must be a multiple of 128");
+  if ((int64_t)D.seq * 3 * D.hidden / D.tp_size * (int64_t)elem_bytes(D.dtype) >= ((int64_t)1 << 31))
+    return fail(MTNLG_ERR_SHAPE, "one sequence of the QKV activations must stay below 2 GiB");
   if (!(D.ln_eps > 0.0f) || !isfinite(D.ln_eps)) return fail(MTNLG_ERR_ARG, "ln_eps must be positive and finite");
   const int64_t T = (int64_t)D.batch * D.seq;
   if (T * (int64_t)std::max(D.hidden, D.ffn) > (int64_t)1 << 40) return fail(MTNLG_ERR_SHAPE, "problem too large");
@@ -510,6 +512,8 @@ static int validate_attn(int32_t dtype, int32_t batch, int32_t seq, int32_t head
   const bool ok = dtype == MTNLG_BF16 ? (head_dim == 64 || head_dim == 128 || head_dim == 160)
                                       : (head_dim == 64 || head_dim == 128);
   if (!ok) return fail(MTNLG_ERR_SHAPE, "head_dim %d unsupported", head_dim);
+  if ((int64_t)seq * 3 * heads * head_dim * (int64_t)elem_bytes(dtype) >= ((int64_t)1 << 31))
+    return fail(MTNLG_ERR_SHAPE, "one sequence of qkv must stay below 2 GiB");
   return MTNLG_OK;
 }
 

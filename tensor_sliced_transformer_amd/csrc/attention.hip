@@ -1,4 +1,6 @@
-// Causal multi-head attention, forward and backward, on MFMA (gfx950).
+// Causal multi-head attention, forward and backward, on MFMA (gfx950): the
+// fp32 kernels, and the dispatch of both dtypes (bf16 runs the kernels of
+// attention_bf16.hip).
 //
 // Per sequence and head: S = Q K^T / sqrt(d), keys after the query masked,
 // P = softmax(S) row-wise, O = P V (the left-to-right decoder of the MT-NLG
@@ -477,16 +479,14 @@ hipError_t attention_fwd(int dtype, int batch, int seq, int heads, int head_dim,
   if (batch == 0) return hipSuccess;
 #define MTNLG_AF(T, D) \
   if (head_dim == D) return fwd_launch<T, D>(batch, seq, heads, qkv, o, lse, st);
-  if (dtype == kBF16) {
-    MTNLG_AF(bf16_t, 64) MTNLG_AF(bf16_t, 128) MTNLG_AF(bf16_t, 160)
-  } else {
-    MTNLG_AF(float, 64) MTNLG_AF(float, 128)
-  }
+  if (dtype == kBF16) return attention_fwd_bf16(batch, seq, heads, head_dim, qkv, o, lse, st);
+  MTNLG_AF(float, 64) MTNLG_AF(float, 128)
 #undef MTNLG_AF
   return hipErrorInvalidValue;
 }
 
-size_t attention_bwd_ws(int batch, int seq, int heads) { return (size_t)batch * seq * heads * sizeof(float); }
+// bf16: one (lse * log2 e, rowsum(dO * O)) float pair per (token, head); fp32: the rowsum only.
+size_t attention_bwd_ws(int batch, int seq, int heads) { return (size_t)batch * seq * heads * 2 * sizeof(float); }
 
 hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv, const void* o,
                          const float* lse, const void* dout, void* dqkv, void* ws, hipStream_t st) {
@@ -494,11 +494,8 @@ hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim,
   float* dd = static_cast<float*>(ws);
 #define MTNLG_AB(T, D) \
   if (head_dim == D) return bwd_launch<T, D>(batch, seq, heads, qkv, o, lse, dout, dqkv, dd, st);
-  if (dtype == kBF16) {
-    MTNLG_AB(bf16_t, 64) MTNLG_AB(bf16_t, 128) MTNLG_AB(bf16_t, 160)
-  } else {
-    MTNLG_AB(float, 64) MTNLG_AB(float, 128)
-  }
+  if (dtype == kBF16) return attention_bwd_bf16(batch, seq, heads, head_dim, qkv, o, lse, dout, dqkv, ws, st);
+  MTNLG_AB(float, 64) MTNLG_AB(float, 128)
 #undef MTNLG_AB
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,139 @@
+// Shared pieces of the bf16 attention kernels (gfx950): tile layout in LDS,
+// direct-to-LDS tile loads, MFMA fragment reads and the LDS ring walk.
+// The kernels themselves and what they compute are described in
+// attention_bf16.hip.
+#pragma once
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mtnlg {
+namespace attn {
+
+constexpr int kRows = 64;      // rows per workgroup block and per streamed tile
+constexpr int kRing = 3;       // LDS ring depth (tiles in flight)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D>
+struct Tile {
+  static constexpr int EB = D / 32;               // 32-column blocks of head_dim
+  static constexpr int SUB = D / 16;              // 16-wide reduction steps over head_dim
+  static constexpr int BYTES = kRows * D * 2;     // one 64-row tile
+  static constexpr int IPW = BYTES / 1024 / 4;    // 1 KiB loads per wave per tile (= EB)
+};
+
+__device__ __forceinline__ int chunk_off(int e, int r, int c) {
+  return e * 4096 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
+
+// Per-lane byte offset, relative to the tile's first row and head column, of
+// this wave's u-th 1 KiB load: load q = wave*IPW + u covers 32-column block
+// q/4 and rows 16*(q%4) .. +15; lane l fills row 16*(q%4) + l/4, LDS slot l%4.
+template <int D>
+__device__ __forceinline__ uint32_t tile_voff(int wave, int u, int lane, int64_t ld) {
+  const int q = wave * Tile<D>::IPW + u;
+  const int r = 16 * (q & 3) + (lane >> 2);
+  const int c = (lane & 3) ^ ((r >> 2) & 3);
+  return (uint32_t)(((int64_t)r * ld + (q >> 2) * 32 + c * 8) * 2);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(i32x4_t rs, const uint32_t* voff, uint32_t soff, char* dst, int wave) {
+#pragma unroll
+  for (int u = 0; u < Tile<D>::IPW; ++u) dtl16_so(rs, dst + (wave * Tile<D>::IPW + u) * 1024, voff[u], soff);
+}
+
+// 16-byte row fragment: row r, head_dim columns 16*s + 8*g .. +7.
+__device__ __forceinline__ bf16x8_t frag_row(const char* tile, int r, int s, int g) {
+  const int ch = 2 * s + g;
+  return *reinterpret_cast<const bf16x8_t*>(tile + chunk_off(ch >> 2, r, ch & 3));
+}
+
+// Transposed fragment of a tile X for the MFMA A operand of X^T Y: lane l
+// holds column 32*e + l%32 and, in its 8 reduction slots, rows
+// rb + 16*t + 4*g + {0..3} then rb + 16*t + 8 + 4*g + {0..3} (g = l/32): the
+// order in which a 32x32 MFMA accumulator holds its rows.
+__device__ __forceinline__ bf16x8_t frag_tr(const char* tile, int e, int rb, int t, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int r = rb + 16 * t + 4 * (G >> 1) + (i >> 2);
+  const int c = 2 * (G & 1) + ((i & 3) >> 1);
+  const uint2 lo = ds_read_tr(tile + chunk_off(e, r, c) + 8 * (i & 1));
+  const uint2 hi = ds_read_tr(tile + chunk_off(e, r + 8, c) + 8 * (i & 1));
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Accumulator entries 8t .. 8t+7 as the bf16 B operand matching frag_tr(.., t, ..).
+__device__ __forceinline__ bf16x8_t pack_slots(const f32x16_t& a, int t) {
+  uint4 u;
+  u.x = pack_bf16x2(a[8 * t + 0], a[8 * t + 1]);
+  u.y = pack_bf16x2(a[8 * t + 2], a[8 * t + 3]);
+  u.z = pack_bf16x2(a[8 * t + 4], a[8 * t + 5]);
+  u.w = pack_bf16x2(a[8 * t + 6], a[8 * t + 7]);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ f32x16_t mma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero(f32x16_t& a) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = 0.0f;
+}
+
+// Wait until at most k tiles' worth (n loads each) of this wave's loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_tiles(int k) {
+  static_assert(2 * N < 64, "vmcnt is 6 bits");
+  if (k >= 2) {
+    MTNLG_VMCNT(2 * N);
+  } else if (k == 1) {
+    MTNLG_VMCNT(N);
+  } else {
+    MTNLG_VMCNT(0);
+  }
+}
+
+// An empty asm that reads x: the compiler must complete the load of x before
+// it. Used on the register-resident operands before the tile loop, so that
+// none of their loads is still pending (from the compiler's view) inside the
+// loop, where waiting for it would also wait for every prefetch.
+__device__ __forceinline__ void settle(const bf16x8_t& x) { asm volatile("" : : "v"(x)); }
+
+// 2^x by the hardware instruction (results below 2^-126 flush to zero, which
+// is immaterial next to the softmax row sum of at least 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The walk over `count` streamed tiles through the LDS ring. issue(t, stage)
+// starts the loads of tile t into a ring stage; body(it, stage) computes on
+// tile it. The loop is unrolled by the ring depth so that each stage index,
+// and with it every LDS address of the body, is a compile-time offset.
+template <int NLD, typename Issue, typename Body>
+__device__ __forceinline__ void ring_walk(int count, Issue&& issue, Body&& body) {
+#pragma unroll
+  for (int t = 0; t < kRing - 1; ++t)
+    if (t < count) issue(t, t);
+  for (int it0 = 0; it0 < count; it0 += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      const int it = it0 + j;
+      if (it < count) {
+        wait_tiles<NLD>(min(kRing - 2, count - 1 - it));
+        __syncthreads();
+        if (it + kRing - 1 < count) issue(it + kRing - 1, (j + kRing - 1) % kRing);
+        body(it, j);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+// dK and dV given the (L, D) pairs the dQ kernel stores (attention_bf16_dkdv.hip).
+hipError_t dkdv_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, const void* dout,
+                     const float2* ldw, void* dqkv, hipStream_t st);
+
+}  // namespace attn
+}  // namespace mtnlg

@@ -22,9 +22,13 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
-// Two floats -> packed bf16x2 in one dword (lo in bits 0-15).
+// Two floats -> packed bf16x2 in one dword (lo in bits 0-15), round to
+// nearest even: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Element traits: VEC = elements per 16-byte vector.
@@ -101,5 +105,59 @@ __device__ __forceinline__ F block_sum(F v, F* red) {
   __syncthreads();
   return s;
 }
+
+// ---- direct-to-LDS loads and transposing LDS reads (gfx950) ----
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#define MTNLG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// A buffer-load offset past any num_records used here: the load returns zeros.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// Buffer resource as four words: 48-bit base, stride 0, num_records bytes,
+// and the raw-buffer format word.
+__device__ __forceinline__ i32x4_t rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  i32x4_t r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)((a >> 32) & 0xffffu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer into LDS at m0 + 16*lane. Written as inline
+// asm on purpose: the compiler cannot tell which LDS bytes such a load writes
+// and would otherwise wait for ALL outstanding loads before every LDS read,
+// defeating a prefetch ring; callers wait on vmcnt themselves before the
+// barrier that publishes what was loaded.
+__device__ __forceinline__ void dtl16(i32x4_t rsrc, const void* lds_base, uint32_t off) {
+  // the stage base is the same for every lane; make that explicit for the SGPR operand
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MTNLG_LDS(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
+// As dtl16, with a wave-uniform byte offset `soff` added to every lane's `off`.
+__device__ __forceinline__ void dtl16_so(i32x4_t rsrc, const void* lds_base, uint32_t off, uint32_t soff) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MTNLG_LDS(lds_base));
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds), "s"(so)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint2 ds_read_tr(const char* p) {
+  s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, t);
+}
+
+// s_waitcnt for at most n outstanding vector-memory loads (vmcnt: bits [3:0] and [15:14]).
+#define MTNLG_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 }  // namespace mtnlg

@@ -422,42 +422,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 constexpr int kStages = MTNLG_GEMM_STAGES;  // K-tiles in the LDS ring
 constexpr int kBKd = 32;                    // bf16 K per stage
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-#define MTNLG_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer resource as four words: 48-bit base, stride 0, num_records bytes,
-// and the raw-buffer format word used for make_rsrc above.
-__device__ __forceinline__ i32x4_t rsrc_words(const void* p, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)p;
-  i32x4_t r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)(uint32_t)((a >> 32) & 0xffffu);
-  r[2] = (int)bytes;
-  r[3] = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from a buffer into LDS at m0 + 16*lane. Written as inline
-// asm on purpose: the compiler cannot tell which LDS bytes such a load writes
-// and would otherwise wait for ALL outstanding loads before every LDS read,
-// defeating the prefetch ring; the kernel waits on vmcnt itself (wait_tiles)
-// before the barrier that publishes a stage.
-__device__ __forceinline__ void dtl16(i32x4_t rsrc, const void* lds_base, uint32_t off) {
-  // the stage base is the same for every lane; make that explicit for the SGPR operand
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MTNLG_LDS(lds_base));
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(off), "s"(rsrc), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint2 ds_read_tr(const char* p) {
-  s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(uint2, t);
-}
-
 // One operand of the direct-to-LDS GEMM: R rows of M (or N) per tile.
 template <int R, bool KC>
 struct DtlOperand {

@@ -68,6 +68,10 @@ hipError_t layernorm_bwd(int dtype, int gy_dtype, int64_t rows, int64_t cols, co
 hipError_t attention_fwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv,
                          void* o, float* lse, hipStream_t st);
 size_t attention_bwd_ws(int batch, int seq, int heads);
+hipError_t attention_fwd_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, void* o, float* lse,
+                              hipStream_t st);
+hipError_t attention_bwd_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, const void* o,
+                              const float* lse, const void* dout, void* dqkv, void* ws, hipStream_t st);
 hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv,
                          const void* o, const float* lse, const void* dout, void* dqkv, void* ws,
                          hipStream_t st);
