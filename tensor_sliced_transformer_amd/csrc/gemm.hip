@@ -6,28 +6,31 @@
 // products (dY W^T: both K-contiguous) and the weight-gradient products
 // (X^T dY: both M/N-contiguous), see the layer driver.
 //
-// Design (CDNA4, wave64):
-//   * 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2)x(BN/2)
-//     sub-tile made of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16 for bf16,
-//     v_mfma_f32_32x32x2f32 for fp32).
-//   * LDS holds both operand tiles as rows of K: 8 chunks of 16 bytes per
-//     row (BK = 64 bf16 or 32 fp32), the chunk index XOR-ed with
-//     ((row >> 1) & 7) so that MFMA operand reads (16 rows per LDS cycle) and
-//     the transposed stores spread over the banks.
-//   * K-contiguous operands are copied chunk by chunk; M/N-contiguous ones
-//     are loaded as VECxVEC micro-blocks and transposed in registers, so the
-//     MFMA loop is the same for all four layouts and HBM is read once.
-//   * Two LDS stages and register staging with prefetch distance 2: at the
-//     top of K tile k the registers (tile k+1) go to the free stage and the
-//     buffer loads of tile k+2 are issued, so a load has a whole tile of MFMAs
-//     to arrive. MFMA fragments are double-buffered across k-substeps, and the
-//     single barrier per tile sits before the last substep so the next tile's
-//     first fragments load under its MFMAs. Out-of-range elements come from
-//     buffer loads past num_records (zero), not from branches.
+// Design (CDNA4, wave64). Two code paths share the tile scheduling and the
+// epilogue:
+//   * bf16 (the layer's path): operand tiles move from memory straight into
+//     LDS with buffer_load_dwordx4 ... lds; M/N-contiguous operands stay in
+//     their natural layout and MFMA fragments are read with the transposing
+//     ds_read_b64_tr_b16, so all four layouts share one MFMA loop.
+//       - 256x256 tiles: K tiles 64 deep (a k-contiguous operand row is one
+//         128-byte line per tile), a 2-stage LDS ring, 8 waves in a 2x4 grid
+//         (128x64 each, two waves per SIMD so one wave's MFMAs cover the
+//         other's LDS reads and barrier waits).
+//       - 128x128 tiles (small problems): K tiles 32 deep, a 4-stage ring,
+//         4 waves in a 2x2 grid.
+//   * fp32 (the small checked configuration): register-staged copies into
+//     LDS rows of 32 k, M/N-contiguous operands transposed in registers as
+//     4x4 micro-blocks; two stages, prefetch distance 2; 4 waves in a 2x2 grid
+//     on v_mfma_f32_32x32x2f32.
+//   * MFMA blocks are 32x32 (v_mfma_f32_32x32x16_bf16); fragments are
+//     double-buffered across 16-deep k-substeps. Out-of-range elements come
+//     from buffer loads past num_records (zeros), not from branches.
 //   * Workgroup ids are remapped so that each XCD (ids round-robin over 8
 //     XCDs) gets a contiguous range of tiles, walked in groups of 8 tile rows
 //     so that concurrently running tiles share operand panels in that XCD's L2.
-//   * Optional split-K (grid.y) writes fp32 partials that a second kernel sums.
+//   * Wave quantisation: when the last round of tiles would leave at least
+//     half the CUs idle, only those leftover tiles are split along K into
+//     fp32 partials that a second kernel sums before the epilogue.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 GEMM with direct-to-LDS loads (the main path on gfx950)
+// bf16 GEMM with direct-to-LDS loads, 32-deep K tiles (128x128 tiles)
 //
 // * Operand tiles move from HBM/L2 to LDS with buffer_load_dwordx4 ... lds:
 //   no staging registers and no ds_write; lane l of a wave instruction lands
@@ -423,13 +426,13 @@ constexpr int kStages = MTNLG_GEMM_STAGES;  // K-tiles in the LDS ring
 constexpr int kBKd = 32;                    // bf16 K per stage
 
 // One operand of the direct-to-LDS GEMM: R rows of M (or N) per tile.
-template <int R, bool KC>
+template <int R, bool KC, int NW>
 struct DtlOperand {
   static constexpr int STAGE_BYTES = R * kBKd * 2;
   static constexpr int INSTR = STAGE_BYTES / 1024;     // 1 KiB per wave-wide load
-  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int PER_WAVE = INSTR / NW;
   static constexpr int RB = R * 2;                     // bytes per LDS row (MN layout)
-  static_assert(PER_WAVE >= 1 && INSTR % 4 == 0, "tile too small");
+  static_assert(PER_WAVE >= 1 && INSTR % NW == 0, "tile too small");
   // per-lane, per-instruction (row/col) of the element this lane fetches
   int r_[PER_WAVE];      // M/N index within the tile (KC) or k within the tile (MN)
   int c_[PER_WAVE];      // k within the tile (KC) or M/N index within the tile (MN)
@@ -485,13 +488,13 @@ __device__ __forceinline__ int mn_frag_off(int rb32, int s, int lane) {
   return k * RB + c * 16 + 8 * (i & 1);
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_dtl_kernel(GemmArgs p) {
-  constexpr int WM = 2, WN = 2;
+template <int BM, int BN, bool A_KC, bool B_KC, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl_kernel(GemmArgs p) {
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  using OA = DtlOperand<BM, A_KC>;
-  using OB = DtlOperand<BN, B_KC>;
+  using OA = DtlOperand<BM, A_KC, NW>;
+  using OB = DtlOperand<BN, B_KC, NW>;
   constexpr int SA = OA::STAGE_BYTES, SB = OB::STAGE_BYTES, SS = SA + SB;
   __shared__ __align__(1024) char smem[kStages * SS];
 
@@ -632,10 +635,195 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dtl_kernel(GemmArgs p) {
     mfmas_with(1, kt + S - 1 < nk ? kt + S - 1 : -1, true);    // A half of tile kt+S-1
   }
 
-  // ---- epilogue (as in the register-staged kernel) ----
+  // ---- epilogue: through LDS, one 32-row slab of the wave's sub-tile at a time ----
   __builtin_amdgcn_s_waitcnt(W0);  // no load may still be writing LDS (all waited above)
   __syncthreads();
   constexpr int SROW = TN + 4;
+  static_assert(NW * 32 * SROW * 4 <= kStages * SS, "epilogue staging exceeds the ring");
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
+  const int lrow = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stage[(8 * blk + 4 * lg + r) * SROW + j * 32 + lrow] = acc[i][j][blk * 4 + r];
+    __syncthreads();
+    epilogue_slab<bf16_t, TN, SROW, BN>(p, stage, m0, n0, wm * TM + i * 32, wn * TN, lane, pt);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 GEMM with direct-to-LDS loads, 64-deep K tiles (256x256 tiles)
+//
+// * k-contiguous operands: LDS rows of 64 k (128 B = 8 chunks), chunk c of
+//   row r at slot c ^ ((r >> 1) & 7): the 8 rows that one 16-byte operand
+//   read serves at a time land in 8 distinct bank groups, and each row of a
+//   tile is one whole 128-byte line in memory.
+// * M/N-contiguous operands: as in the 32-deep kernel, 64 rows of k.
+// * A 2-stage ring (2 x 64 KiB): right after the barrier that publishes tile
+//   t (and so frees the stage of tile t-1) the loads of tile t+1 are issued
+//   in one burst; they are waited for (vmcnt) just before the next barrier.
+// ---------------------------------------------------------------------------
+constexpr int kBK64 = 64;
+
+template <int R, bool KC, int NW>
+struct Dtl64 {
+  static constexpr int STAGE_BYTES = R * kBK64 * 2;
+  static constexpr int INSTR = STAGE_BYTES / 1024;
+  static constexpr int PER_WAVE = INSTR / NW;
+  static constexpr int RB = R * 2;  // MN layout: bytes per k row
+  static_assert(PER_WAVE >= 1 && INSTR % NW == 0, "tile too small");
+  int r_[PER_WAVE], c_[PER_WAVE];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int q = wave * PER_WAVE + u;
+      if (KC) {
+        const int r = q * 8 + lane / 8;       // 8 rows of 128 B per KiB
+        const int slot = lane & 7;
+        r_[u] = r;
+        c_[u] = 8 * (slot ^ ((r >> 1) & 7));
+      } else {
+        const int rows_per = 1024 / RB;
+        const int k = q * rows_per + (16 * lane) / RB;
+        const int slot = ((16 * lane) % RB) / 16;
+        r_[u] = k;
+        c_[u] = 8 * (slot ^ (4 * (k & 3)));
+      }
+    }
+  }
+  __device__ __forceinline__ void load_one(int u, i32x4_t rs, int64_t ld, int r0, int rmax, int k0, int kend,
+                                           char* dst, int wave) const {
+    const int q = wave * PER_WAVE + u;
+    uint32_t off;
+    if (KC) {
+      const int m = r0 + r_[u], k = k0 + c_[u];
+      off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)m * ld + k) * 2) : kOob;
+    } else {
+      const int k = k0 + r_[u], m = r0 + c_[u];
+      off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)k * ld + m) * 2) : kOob;
+    }
+    dtl16(rs, dst + q * 1024, off);
+  }
+};
+
+__device__ __forceinline__ int kc64_frag_off(int rb32, int s, int lane) {
+  const int r = rb32 * 32 + (lane & 31);
+  const int c = 2 * s + (lane >> 5);
+  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+template <int BM, int BN, bool A_KC, bool B_KC, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  using OA = Dtl64<BM, A_KC, NW>;
+  using OB = Dtl64<BN, B_KC, NW>;
+  constexpr int SA = OA::STAGE_BYTES, SB = OB::STAGE_BYTES, SS = SA + SB;
+  __shared__ __align__(1024) char smem[2 * SS];
+
+  const TileWork tw = tile_work(p, blockIdx.x);
+  const int m0 = tw.tm * BM, n0 = tw.tn * BN;
+  const int kbeg = tw.kbeg, kend = tw.kend;
+  const int nk = (kend - kbeg + kBK64 - 1) / kBK64;
+  float* const pt = tw.split >= 0 ? p.part + ((int64_t)tw.split * p.tail_tiles + tw.tl) * BM * BN : nullptr;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const i32x4_t ra = rsrc_words(p.A, (uint32_t)((int64_t)p.M * p.K * 2));
+  const i32x4_t rb = rsrc_words(p.B, (uint32_t)((int64_t)p.K * p.N * 2));
+  OA oa;
+  OB ob;
+  oa.init(wave, lane);
+  ob.init(wave, lane);
+
+  int aoff[4][FM], boff[4][FN];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      aoff[s][i] = A_KC ? kc64_frag_off(wm * FM + i, s, lane) : mn_frag_off<OA::RB>(wm * FM + i, s, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      boff[s][j] = SA + (B_KC ? kc64_frag_off(wn * FN + j, s, lane) : mn_frag_off<OB::RB>(wn * FN + j, s, lane));
+  }
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  uint4 af[2][FM], bfr[2][FN];
+  auto read_frags = [&](const char* st, int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const char* q = st + aoff[s][i];
+      if (A_KC) {
+        af[buf][i] = *reinterpret_cast<const uint4*>(q);
+      } else {
+        const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OA::RB);
+        af[buf][i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const char* q = st + boff[s][j];
+      if (B_KC) {
+        bfr[buf][j] = *reinterpret_cast<const uint4*>(q);
+      } else {
+        const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OB::RB);
+        bfr[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+  };
+  auto issue = [&](int t) {
+    char* st = smem + (t & 1) * SS;
+#pragma unroll
+    for (int u = 0; u < OA::PER_WAVE; ++u) oa.load_one(u, ra, p.lda, m0, p.M, kbeg + t * kBK64, kend, st, wave);
+#pragma unroll
+    for (int u = 0; u < OB::PER_WAVE; ++u) ob.load_one(u, rb, p.ldb, n0, p.N, kbeg + t * kBK64, kend, st + SA, wave);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        Mfma<bf16_t>::run(af[buf][i], bfr[buf][j], acc[i][j]);
+      }
+  };
+
+  if (nk > 0) {
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    read_frags(smem, 0, 0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* st = smem + (kt & 1) * SS;
+    // stage (kt+1)&1 held tile kt-1, which every wave finished before the barrier above
+    if (kt + 1 < nk) issue(kt + 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) read_frags(st, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // tile kt+1 has landed (this wave's part)
+    __syncthreads();
+    if (kt + 1 < nk) read_frags(smem + ((kt + 1) & 1) * SS, 0, 0);
+  }
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  constexpr int SROW = TN + 4;
+  static_assert(NW * 32 * SROW * 4 <= 2 * SS, "epilogue staging exceeds the ring");
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
   const int lrow = lane & 31, lg = lane >> 5;
 #pragma unroll
@@ -686,7 +874,11 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
 template <int BM, int BN, bool AK, bool BKc>
 hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
   dim3 grid(a.nfull + a.tail_tiles * a.tail_split);
-  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc>), grid, dim3(kThreads), 0, st, a);
+    if (BM >= 256) {  // 64-deep K tiles, 8 waves (2 x 4, 128 x 64 each)
+    hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<BM, BN, AK, BKc, 2, 4>), grid, dim3(512), 0, st, a);
+  } else {           // 32-deep K tiles, 4 waves (2 x 2)
+    hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc, 2, 2>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -720,7 +912,7 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split)
     } else {
       pl.bm = pl.bn = 128;
     }
-    pl.bk = kBKd;
+    pl.bk = pl.bm == 256 ? kBK64 : kBKd;
   } else {
     pl.bm = pl.bn = (M >= 1024 && N >= 1024) ? 128 : 64;
     pl.bk = 32;
