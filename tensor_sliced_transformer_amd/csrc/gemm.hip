@@ -907,12 +907,18 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split)
   const int num_cu = 256;
   if (dtype == kBF16) {
     const int64_t big = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
-    if (big >= num_cu || (M >= 256 && N >= 256 && big * 4 >= 3 * num_cu)) {
+    const int kt_big = ceil_div(K, kBK64);
+    // 256x256 tiles whenever they fill the chip, or can be made to by
+    // splitting every tile along K (at least 8 K-tiles per piece); 128x128
+    // tiles only for problems too small for either.
+    const bool split_fill = allow_split && big * 2 <= num_cu && kt_big / 2 >= 8;
+    if (M >= 256 && N >= 256 && (big >= num_cu || big * 4 >= 3 * num_cu || split_fill)) {
       pl.bm = pl.bn = 256;
+      pl.bk = kBK64;
     } else {
       pl.bm = pl.bn = 128;
+      pl.bk = kBKd;
     }
-    pl.bk = pl.bm == 256 ? kBK64 : kBKd;
   } else {
     pl.bm = pl.bn = (M >= 1024 && N >= 1024) ? 128 : 64;
     pl.bk = 32;
@@ -920,7 +926,8 @@ GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split)
   pl.tiles = ceil_div(M, pl.bm) * ceil_div(N, pl.bn);
   // Wave quantisation: one workgroup per CU (the LDS ring fills a CU), so the
   // last round of tiles may leave most CUs idle. When at most half a round is
-  // left over, those tiles are split along K across the idle CUs.
+  // left over, those tiles are split along K across the idle CUs; a problem
+  // of at most half a round is split whole.
   const int tail = pl.tiles % num_cu;
   if (allow_split && dtype == kBF16 && tail > 0 && tail <= num_cu / 2) {
     const int ktiles = ceil_div(K, pl.bk);
