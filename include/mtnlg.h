@@ -77,9 +77,12 @@ typedef enum { MTNLG_ATTN = 0, MTNLG_MLP = 1 } mtnlg_half;
  * the slice this call computes (tp_rank). The slice sees heads/tp_size heads
  * of width hidden/heads and ffn/tp_size MLP columns.
  * Supported: hidden % heads == 0; heads % tp_size == 0; ffn % tp_size == 0;
- * 0 <= tp_rank < tp_size; head_dim in {64, 128, 160}; hidden, ffn/tp_size and
- * batch*seq multiples of 16; seq a multiple of 64; dtype F32 or BF16;
- * ln_eps > 0. */
+ * 0 <= tp_rank < tp_size; head_dim in {64, 128, 160} (bf16) or {64, 128}
+ * (f32); hidden and ffn/tp_size multiples of 16; hidden <= 32768; seq a
+ * multiple of 128; one sequence of the slice's QKV activations
+ * (seq * 3 * hidden/tp_size elements) below 2 GiB; dtype F32 or BF16;
+ * ln_eps > 0 and finite. Violations return MTNLG_ERR_SHAPE, MTNLG_ERR_DTYPE
+ * or MTNLG_ERR_ARG before any launch. */
 typedef struct {
   int32_t batch, seq, hidden, heads, ffn;
   int32_t tp_size, tp_rank;
@@ -223,13 +226,20 @@ int mtnlg_layernorm_bwd(int32_t dtype, int64_t rows, int64_t cols, const void* g
 /* Causal attention of `heads` heads of width head_dim over batch sequences
  * of length seq, reading qkv [batch*seq, 3*heads*head_dim] (columns
  * (q/k/v, head, dim)) and writing o [batch*seq, heads*head_dim] (columns
- * (head, dim)) and lse [heads, batch*seq] f32. */
+ * (head, dim)) and lse [heads, batch*seq] f32 (natural log of each query's
+ * softmax normaliser). Scores are scaled by 1/sqrt(head_dim); query r sees
+ * keys 0..r of its own sequence (the left-to-right decoder of the MT-NLG
+ * paper summary, Summary, and of the STRONGHOLD slides, slide 8).
+ * Requires seq % 128 == 0, head_dim in {64, 128, 160} (bf16) or {64, 128}
+ * (f32), and seq*3*heads*head_dim elements below 2 GiB. */
 int mtnlg_attention_fwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads,
                         int32_t head_dim, const void* qkv, void* o, float* lse, void* stream);
 
 /* Backward of mtnlg_attention_fwd: dqkv [batch*seq, 3*heads*head_dim] from
- * qkv, o, lse and do_ [batch*seq, heads*head_dim].
- * ws >= mtnlg_attention_bwd_workspace_bytes(...). */
+ * qkv, o, lse and do_ [batch*seq, heads*head_dim]. Every element of dqkv is
+ * written (no accumulation); the result is deterministic.
+ * ws >= mtnlg_attention_bwd_workspace_bytes(...) (two floats per token and
+ * head: lse*log2(e) and rowsum(dO*O)). */
 size_t mtnlg_attention_bwd_workspace_bytes(int32_t batch, int32_t seq, int32_t heads);
 int mtnlg_attention_bwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads,
                         int32_t head_dim, const void* qkv, const void* o, const float* lse,
