@@ -3,7 +3,8 @@
 // Forward: y = gamma * (x - mean) * rstd + beta with mean and biased variance
 // over the row, statistics in fp32 (mean, rstd saved for backward). One row
 // per workgroup; each thread keeps its 8-element chunks in registers, so x is
-// read once and y written once.
+// read once and y written once; the row's mean and variance come from one
+// workgroup reduction of per-thread (count, mean, squared deviations).
 //
 // Backward on an upstream gradient gy (linear in gy, so a tensor slice may
 // apply it to its own partial): with gh = gy * gamma and xhat recomputed from
@@ -21,52 +22,119 @@ namespace mtnlg {
 
 namespace {
 
+// Eight consecutive elements kept in their storage type (one 16-byte vector
+// of bf16, two of fp32) until they are used, to keep register use low.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float operator[](int e) const {
+    const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    const float4& v = e < 4 ? a : b;
+    const int k = e & 3;
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
+
+// Count, mean and sum of squared deviations of a set of values; two sets
+// combine exactly (up to rounding) by the pairwise update of Chan, Golub and
+// LeVeque, so a row's variance comes out of one reduction without the
+// cancellation of E[x^2] - E[x]^2.
+struct Moments {
+  float n, mean, m2;
+};
+__device__ __forceinline__ Moments combine(const Moments& a, const Moments& b) {
+  const float n = a.n + b.n;
+  if (n == 0.0f) return a;
+  const float d = b.mean - a.mean;
+  const float wb = b.n / n;
+  return {n, a.mean + d * wb, a.m2 + b.m2 + d * d * a.n * wb};
+}
+// Combined moments of the whole workgroup; every thread gets the same value
+// (lanes combine in lane order, waves in wave order).
+template <int NT>
+__device__ __forceinline__ Moments block_moments(Moments m, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    Moments o;
+    o.n = __shfl_xor(m.n, off, kWave);
+    o.mean = __shfl_xor(m.mean, off, kWave);
+    o.m2 = __shfl_xor(m.m2, off, kWave);
+    m = (lane & off) ? combine(o, m) : combine(m, o);
+  }
+  if (lane == 0) {
+    red[3 * w] = m.n;
+    red[3 * w + 1] = m.mean;
+    red[3 * w + 2] = m.m2;
+  }
+  __syncthreads();
+  Moments t = {red[0], red[1], red[2]};
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) t = combine(t, Moments{red[3 * i], red[3 * i + 1], red[3 * i + 2]});
+  return t;
+}
+
 template <int NT, typename T, int CPT>
 __global__ __launch_bounds__(NT) void ln_fwd_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                                                     const T* __restrict__ beta, float eps, T* __restrict__ y,
                                                     float* __restrict__ mean_out, float* __restrict__ rstd_out,
                                                     int cols) {
-  __shared__ float red[NT / kWave];
+  __shared__ float red[3 * (NT / kWave)];
   const int64_t row = blockIdx.x;
   const T* xr = x + row * cols;
   const int nch = cols / 8;
   const int tid = threadIdx.x;
-  float v[CPT][8];
-  float s = 0.0f;
+  Raw8<T> xv[CPT], gv[CPT], bv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * NT;
     if (ch < nch) {
-      load8(xr + ch * 8, v[c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[c][e];
+      xv[c].load(xr + ch * 8);
+      gv[c].load(gamma + ch * 8);  // issued before the reduction so its latency hides under it
+      bv[c].load(beta + ch * 8);
     }
   }
-  const float mu = block_sum<NT>(s, red) / (float)cols;
-  float q = 0.0f;
+  float n = 0.0f, s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * NT;
-    if (ch < nch) {
+  for (int c = 0; c < CPT; ++c)
+    if (tid + c * NT < nch) {
+      n += 8.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += xv[c][e];
+    }
+  const float mt = n > 0.0f ? s / n : 0.0f;
+  float m2 = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+    if (tid + c * NT < nch) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = v[c][e] - mu;
-        q += d * d;
+        const float d = xv[c][e] - mt;
+        m2 += d * d;
       }
     }
-  }
-  const float var = block_sum<NT>(q, red) / (float)cols;
-  const float rs = 1.0f / sqrtf(var + eps);
+  const Moments t = block_moments<NT>(Moments{n, mt, m2}, red);
+  const float mu = t.mean;
+  const float rs = 1.0f / sqrtf(t.m2 / (float)cols + eps);
   T* yr = y + row * cols;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * NT;
     if (ch < nch) {
-      float g[8], b[8], o[8];
-      load8(gamma + ch * 8, g);
-      load8(beta + ch * 8, b);
+      float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = g[e] * ((v[c][e] - mu) * rs) + b[e];
+      for (int e = 0; e < 8; ++e) o[e] = gv[c][e] * ((xv[c][e] - mu) * rs) + bv[c][e];
       store8(yr + ch * 8, o);
     }
   }
@@ -76,41 +144,72 @@ __global__ __launch_bounds__(NT) void ln_fwd_kernel(const T* __restrict__ x, con
   }
 }
 
+// One workgroup per block of consecutive rows. gamma sits in LDS (each thread
+// reads back only its own chunks), which leaves registers for loading the next
+// row's gy and x while the current row is reduced; the two row sums of a row
+// share one barrier (the LDS slots alternate between rows, so no second
+// barrier is needed before they are reused).
 template <int NT, typename T, typename G, int CPT>
 __global__ __launch_bounds__(NT) void ln_bwd_kernel(const G* __restrict__ gy, const T* __restrict__ x,
                                                     const float* __restrict__ mean, const float* __restrict__ rstd,
                                                     const T* __restrict__ gamma, T* __restrict__ dx,
                                                     float* __restrict__ part, int64_t rows, int cols,
                                                     int rows_per_block) {
-  __shared__ float red[NT / kWave];
-  const int tid = threadIdx.x;
+  constexpr int NW = NT / kWave;
+  __shared__ float red[2][2 * NW];
+  extern __shared__ __align__(16) char gam_lds[];  // cols elements of T
+  T* sg = reinterpret_cast<T*>(gam_lds);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int nch = cols / 8;
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
   const int64_t r1 = min(rows, r0 + rows_per_block);
-  float gam[CPT][8];
   float dg[CPT][8], db[CPT][8];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * NT;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { dg[c][e] = 0.0f; db[c][e] = 0.0f; gam[c][e] = 0.0f; }
-    if (ch < nch) load8(gamma + ch * 8, gam[c]);
+    for (int e = 0; e < 8; ++e) { dg[c][e] = 0.0f; db[c][e] = 0.0f; }
+    if (ch < nch) {
+      Raw8<T> g;
+      g.load(gamma + ch * 8);
+      *reinterpret_cast<Raw8<T>*>(sg + ch * 8) = g;
+    }
   }
   const float inv_cols = 1.0f / (float)cols;
+  Raw8<G> ng[CPT];
+  Raw8<T> nx[CPT];
+  auto load_row = [&](int64_t row) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < nch) {
+        ng[c].load(gy + row * cols + ch * 8);
+        nx[c].load(x + row * cols + ch * 8);
+      }
+    }
+  };
+  if (r0 < r1) load_row(r0);
+  int parity = 0;
   for (int64_t row = r0; row < r1; ++row) {
     const float mu = mean[row], rs = rstd[row];
     float gv[CPT][8], xh[CPT][8];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gv[c][e] = ng[c][e];
+        xh[c][e] = (nx[c][e] - mu) * rs;
+      }
+    if (row + 1 < r1) load_row(row + 1);
     float sa = 0.0f, sb = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * NT;
       if (ch < nch) {
-        load8(gy + row * cols + ch * 8, gv[c]);
-        load8(x + row * cols + ch * 8, xh[c]);
+        const Raw8<T> g = *reinterpret_cast<const Raw8<T>*>(sg + ch * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xh[c][e] = (xh[c][e] - mu) * rs;
-          const float gh = gv[c][e] * gam[c][e];
+          const float gh = gv[c][e] * g[e];
           sa += gh;
           sb += gh * xh[c][e];
           dg[c][e] += gv[c][e] * xh[c][e];
@@ -118,15 +217,29 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(const G* __restrict__ gy, co
         }
       }
     }
-    const float a = block_sum<NT>(sa, red) * inv_cols;
-    const float b = block_sum<NT>(sb, red) * inv_cols;
+    sa = wave_sum(sa);
+    sb = wave_sum(sb);
+    if (lane == 0) {
+      red[parity][w] = sa;
+      red[parity][NW + w] = sb;
+    }
+    __syncthreads();
+    float ta = 0.0f, tb = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      ta += red[parity][i];
+      tb += red[parity][NW + i];
+    }
+    parity ^= 1;
+    const float a = ta * inv_cols, b = tb * inv_cols;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * NT;
       if (ch < nch) {
+        const Raw8<T> g = *reinterpret_cast<const Raw8<T>*>(sg + ch * 8);
         float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = rs * (gv[c][e] * gam[c][e] - a - xh[c][e] * b);
+        for (int e = 0; e < 8; ++e) o[e] = rs * (gv[c][e] * g[e] - a - xh[c][e] * b);
         store8(dx + row * cols + ch * 8, o);
       }
     }
@@ -144,19 +257,62 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(const G* __restrict__ gy, co
   }
 }
 
-// out[j][c] = sum_p part[p][j][c] for j < nout (fixed order over p), rounded to T.
+// out[j][c] = sum_p part[p][j][c] for j < nout, rounded to T. A workgroup
+// owns 128 columns (32 float4 quads) of one output row j; its 8 thread groups
+// take the partials p = g, g+8, g+16, ... with independent loads, and the 8
+// group sums are added in fixed order through LDS (deterministic).
+constexpr int kCrQuads = 32, kCrGroups = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void col_reduce_kernel(const float* __restrict__ part, int P, int nout,
                                                          int cols, T* __restrict__ out0, T* __restrict__ out1) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ float4 red[kCrGroups][kCrQuads];
+  const int q = threadIdx.x % kCrQuads, g = threadIdx.x / kCrQuads;
   const int j = blockIdx.y;
-  if (c >= cols || j >= nout) return;
-  float s = 0.0f;
-  for (int p = 0; p < P; ++p) s += part[((int64_t)p * nout + j) * cols + c];
-  (j == 0 ? out0 : out1)[c] = Elem<T>::from_f(s);
+  const int c4 = (blockIdx.x * kCrQuads + q) * 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c4 < cols) {
+    const float* base = part + (int64_t)j * cols + c4;
+    const int64_t stride = (int64_t)nout * cols;
+    int p = g;
+    for (; p + 3 * kCrGroups < P; p += 4 * kCrGroups) {  // four loads in flight per thread
+      const float4 a = *reinterpret_cast<const float4*>(base + p * stride);
+      const float4 b = *reinterpret_cast<const float4*>(base + (p + kCrGroups) * stride);
+      const float4 d = *reinterpret_cast<const float4*>(base + (p + 2 * kCrGroups) * stride);
+      const float4 e = *reinterpret_cast<const float4*>(base + (p + 3 * kCrGroups) * stride);
+      s.x += a.x + b.x + d.x + e.x;
+      s.y += a.y + b.y + d.y + e.y;
+      s.z += a.z + b.z + d.z + e.z;
+      s.w += a.w + b.w + d.w + e.w;
+    }
+    for (; p < P; p += kCrGroups) {
+      const float4 a = *reinterpret_cast<const float4*>(base + p * stride);
+      s.x += a.x;
+      s.y += a.y;
+      s.z += a.z;
+      s.w += a.w;
+    }
+  }
+  red[g][q] = s;
+  __syncthreads();
+  if (g == 0 && c4 < cols) {
+#pragma unroll
+    for (int h = 1; h < kCrGroups; ++h) {
+      const float4 a = red[h][q];
+      s.x += a.x;
+      s.y += a.y;
+      s.z += a.z;
+      s.w += a.w;
+    }
+    T* o = (j == 0 ? out0 : out1) + c4;
+    o[0] = Elem<T>::from_f(s.x);
+    o[1] = Elem<T>::from_f(s.y);
+    o[2] = Elem<T>::from_f(s.z);
+    o[3] = Elem<T>::from_f(s.w);
+  }
 }
 
-// part[p][c] = sum of x[r][c] over rows r in block p (8 columns per thread).
+// part[p][c] = sum of x[r][c] over rows r in block p (8 columns per thread,
+// four independent accumulators so several rows' loads are in flight).
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ x, int64_t rows, int cols,
                                                              int rows_per_block, float* __restrict__ part) {
@@ -164,14 +320,31 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
   if (c8 >= cols) return;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(rows, r0 + rows_per_block);
-  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t r = r0; r < r1; ++r) {
+  float s[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[u][e] = 0.0f;
+  int64_t r = r0;
+  for (; r + 3 < r1; r += 4) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8(x + (r + u) * cols + c8, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[u][e] += v[u][e];
+  }
+  for (; r < r1; ++r) {
     float v[8];
     load8(x + r * cols + c8, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += v[e];
+    for (int e = 0; e < 8; ++e) s[0][e] += v[e];
   }
-  store8(part + (int64_t)blockIdx.y * cols + c8, s);
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (s[0][e] + s[1][e]) + (s[2][e] + s[3][e]);
+  store8(part + (int64_t)blockIdx.y * cols + c8, o);
 }
 
 int ln_cpt(int nch, int nt) { return (nch + nt - 1) / nt; }
@@ -186,17 +359,14 @@ hipError_t ln_fwd_launch(int64_t rows, int cols, const void* x, const void* g, c
                      rstd, cols)
   if (cpt <= 1) MTNLG_LNF(1);
   else if (cpt <= 2) MTNLG_LNF(2);
+  else if (cpt <= 3) MTNLG_LNF(3);
   else if (cpt <= 4) MTNLG_LNF(4);
-  else if (cpt <= 6) MTNLG_LNF(6);
+  else if (cpt <= 5) MTNLG_LNF(5);
   else if (cpt <= 8) MTNLG_LNF(8);
-  else if (cpt <= 10) MTNLG_LNF(10);
-  else if (cpt <= 16) MTNLG_LNF(16);
   else return hipErrorInvalidValue;
 #undef MTNLG_LNF
   return hipGetLastError();
 }
-
-constexpr int kLnBwdThreads = 512;
 
 int ln_bwd_blocks(int64_t rows) {
   // about one workgroup per CU; each walks a contiguous range of rows
@@ -209,10 +379,10 @@ template <typename T, typename G>
 hipError_t ln_bwd_launch(int64_t rows, int cols, const void* gy, const void* x, const float* mean,
                          const float* rstd, const void* gamma, void* dx, float* part, int blocks,
                          int rpb, hipStream_t st) {
-  constexpr int NT = kLnBwdThreads;
+  constexpr int NT = 512;
   const int cpt = ln_cpt(cols / 8, NT);
 #define MTNLG_LNB(C)                                                                                  \
-  hipLaunchKernelGGL((ln_bwd_kernel<NT, T, G, C>), dim3(blocks), dim3(NT), 0, st,                    \
+  hipLaunchKernelGGL((ln_bwd_kernel<NT, T, G, C>), dim3(blocks), dim3(NT), (size_t)cols * sizeof(T), st, \
                      static_cast<const G*>(gy), static_cast<const T*>(x), mean, rstd,                \
                      static_cast<const T*>(gamma), static_cast<T*>(dx), part, rows, cols, rpb)
   if (cpt <= 1) MTNLG_LNB(1);
@@ -227,7 +397,7 @@ hipError_t ln_bwd_launch(int64_t rows, int cols, const void* gy, const void* x, 
 
 template <typename T>
 hipError_t col_reduce_launch(const float* part, int P, int nout, int cols, void* o0, void* o1, hipStream_t st) {
-  dim3 grid((cols + 255) / 256, nout);
+  dim3 grid((cols + 4 * kCrQuads - 1) / (4 * kCrQuads), nout);
   hipLaunchKernelGGL(col_reduce_kernel<T>, grid, dim3(256), 0, st, part, P, nout, cols, static_cast<T*>(o0),
                      static_cast<T*>(o1));
   return hipGetLastError();
@@ -242,10 +412,12 @@ hipError_t layernorm_fwd(int dtype, int64_t rows, int64_t cols, const void* x, c
   if (rows == 0) return hipSuccess;
   const int c = (int)cols;
   if (dtype == kBF16) {
-    if (c >= 8192) return ln_fwd_launch<256, bf16_t>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
+    if (c > 8192) return ln_fwd_launch<512, bf16_t>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
+    if (c > 2048) return ln_fwd_launch<256, bf16_t>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
     return ln_fwd_launch<128, bf16_t>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
   }
-  if (c >= 8192) return ln_fwd_launch<256, float>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
+  if (c > 8192) return ln_fwd_launch<512, float>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
+  if (c > 2048) return ln_fwd_launch<256, float>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
   return ln_fwd_launch<128, float>(rows, c, x, gamma, beta, eps, y, mean, rstd, st);
 }
 
