@@ -12,8 +12,8 @@
 //   fixed order that writes {norm, clip coef, found_inf} to device memory,
 //   (3) the update, which reads those scalars itself and leaves every buffer
 //   untouched when found_inf is set -- the host never waits.
-// Grid-stride loops over 16-byte vectors with a fixed grid; all pointers are
-// 16-byte aligned (checked on the host) and the ragged tail is done per element.
+// Grid-stride loops over 16-byte vectors; all pointers are 16-byte aligned
+// (checked on the host) and the ragged tail is done per element.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,10 +23,29 @@ namespace {
 
 constexpr int kStreamThreads = 256;
 
-int stream_grid(int64_t units) {
-  const int64_t max_blocks = 256 * 8;  // 8 workgroups per CU
+int stream_grid(int64_t units, int64_t max_blocks = 256 * 8) {
   int64_t b = (units + kStreamThreads - 1) / kStreamThreads;
   return (int)(b < 1 ? 1 : (b > max_blocks ? max_blocks : b));
+}
+
+// The optimizer streams (accumulation, norm, update) touch every byte once:
+// two vectors per thread per iteration and up to 128 workgroups per CU keep
+// more bytes in flight; the norm and update passes use non-temporal accesses
+// (measured faster there, slower for the accumulation).
+constexpr int64_t kOptBlocks = 256 * 128;
+typedef float nf4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_nt(const float4* p) {
+  const nf4_t v = __builtin_nontemporal_load(reinterpret_cast<const nf4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(float4* p, const float4& v) {
+  const nf4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nf4_t*>(p));
+}
+__device__ __forceinline__ void st_nt(uint2* p, const uint2& v) {
+  typedef unsigned int nu2_t __attribute__((ext_vector_type(2)));
+  const nu2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<nu2_t*>(p));
 }
 
 struct PartialPtrs {
@@ -63,20 +82,32 @@ template <typename T>
 __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, const T* __restrict__ g,
                                                                   float* __restrict__ acc, int overwrite) {
   const int64_t units = n / 8;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int64_t u = t0; u < units; u += stride) {
-    const int64_t i = u * 8;
-    float v[8], a[8];
-    load8(g + i, v);
-    if (!overwrite) {
-      load8(acc + i, a);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 2;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x;
+  for (int64_t u0 = t0; u0 < units; u0 += stride) {
+    float v[2][8], a[2][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += a[e];
+    for (int k = 0; k < 2; ++k) {
+      const int64_t u = u0 + (int64_t)k * blockDim.x;
+      if (u < units) {
+        load8(g + u * 8, v[k]);  // plain loads: non-temporal ones measured slower here
+        if (!overwrite) load8(acc + u * 8, a[k]);
+      }
     }
-    store8(acc + i, v);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t u = u0 + (int64_t)k * blockDim.x;
+      if (u < units) {
+        if (!overwrite) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[k][e] += a[k][e];
+        }
+        store8(acc + u * 8, v[k]);
+      }
+    }
   }
-  for (int64_t i = units * 8 + t0; i < n; i += stride) {
+  const int64_t s1 = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = units * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += s1) {
     const float v = Elem<T>::to_f(g[i]);
     acc[i] = overwrite ? v : acc[i] + v;
   }
@@ -95,11 +126,19 @@ __global__ __launch_bounds__(kStreamThreads) void adam_norm_kernel(int64_t n, co
   const int64_t n4 = n / 4;
   double acc = 0.0;
   int bad = 0;
-  for (int64_t u = t0; u < n4; u += stride) {
-    const float4 g = reinterpret_cast<const float4*>(grad)[u];
-    const float a = g.x * s, b = g.y * s, c = g.z * s, d = g.w * s;
-    bad |= !isfinite(a) | !isfinite(b) | !isfinite(c) | !isfinite(d);
-    acc += (double)a * a + (double)b * b + (double)c * c + (double)d * d;
+  for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x; u0 < n4; u0 += 2 * stride) {
+    float4 g[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t u = u0 + (int64_t)k * blockDim.x;
+      g[k] = u < n4 ? ld_nt(reinterpret_cast<const float4*>(grad) + u) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float a = g[k].x * s, b = g[k].y * s, c = g[k].z * s, d = g[k].w * s;
+      bad |= !isfinite(a) | !isfinite(b) | !isfinite(c) | !isfinite(d);
+      acc += (double)a * a + (double)b * b + (double)c * c + (double)d * d;
+    }
   }
   for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
     const float a = grad[i] * s;
@@ -165,19 +204,34 @@ __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n4 = n / 4;
-  for (int64_t u = t0; u < n4; u += stride) {
-    float4 p = reinterpret_cast<float4*>(master)[u];
-    float4 mm = reinterpret_cast<float4*>(m)[u];
-    float4 vv = reinterpret_cast<float4*>(v)[u];
-    const float4 g = reinterpret_cast<const float4*>(grad)[u];
-    adam_one(p.x, mm.x, vv.x, g.x * gs, c);
-    adam_one(p.y, mm.y, vv.y, g.y * gs, c);
-    adam_one(p.z, mm.z, vv.z, g.z * gs, c);
-    adam_one(p.w, mm.w, vv.w, g.w * gs, c);
-    reinterpret_cast<float4*>(master)[u] = p;
-    reinterpret_cast<float4*>(m)[u] = mm;
-    reinterpret_cast<float4*>(v)[u] = vv;
-    if (w) reinterpret_cast<uint2*>(w)[u] = make_uint2(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w));
+  for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x; u0 < n4; u0 += 2 * stride) {
+    float4 p[2], mm[2], vv[2], g[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t u = u0 + (int64_t)k * blockDim.x;
+      if (u < n4) {
+        p[k] = ld_nt(reinterpret_cast<const float4*>(master) + u);
+        mm[k] = ld_nt(reinterpret_cast<const float4*>(m) + u);
+        vv[k] = ld_nt(reinterpret_cast<const float4*>(v) + u);
+        g[k] = ld_nt(reinterpret_cast<const float4*>(grad) + u);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t u = u0 + (int64_t)k * blockDim.x;
+      if (u < n4) {
+        adam_one(p[k].x, mm[k].x, vv[k].x, g[k].x * gs, c);
+        adam_one(p[k].y, mm[k].y, vv[k].y, g[k].y * gs, c);
+        adam_one(p[k].z, mm[k].z, vv[k].z, g[k].z * gs, c);
+        adam_one(p[k].w, mm[k].w, vv[k].w, g[k].w * gs, c);
+        st_nt(reinterpret_cast<float4*>(master) + u, p[k]);
+        st_nt(reinterpret_cast<float4*>(m) + u, mm[k]);
+        st_nt(reinterpret_cast<float4*>(v) + u, vv[k]);
+        if (w)
+          st_nt(reinterpret_cast<uint2*>(w) + u,
+                make_uint2(pack_bf16x2(p[k].x, p[k].y), pack_bf16x2(p[k].z, p[k].w)));
+      }
+    }
   }
   for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
     float p = master[i], mm = m[i], vv = v[i];
@@ -189,7 +243,7 @@ __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars
   }
 }
 
-constexpr int kNormBlocks = 2048;
+constexpr int kNormBlocks = 8192;
 
 }  // namespace
 
@@ -213,7 +267,7 @@ hipError_t reduce_partials(int dtype, int64_t rows, int64_t cols, const void* co
 
 hipError_t grad_accumulate(int64_t n, int dtype, const void* grad, float* acc, bool overwrite, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  const int grid = stream_grid(n / 8 + 1);
+  const int grid = stream_grid(n / 16 + 1, kOptBlocks);
   if (dtype == kBF16)
     hipLaunchKernelGGL(grad_acc_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, n,
                        static_cast<const bf16_t*>(grad), acc, (int)overwrite);
@@ -229,7 +283,7 @@ hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, f
                      void* w_bf16, float* stats, void* ws, hipStream_t st) {
   double* part = static_cast<double*>(ws);
   int* flag = reinterpret_cast<int*>(part + kNormBlocks);
-  const int nb = n == 0 ? 1 : std::min<int>(kNormBlocks, stream_grid(n / 4 + 1));
+  const int nb = n == 0 ? 1 : std::min<int>(kNormBlocks, stream_grid(n / 8 + 1, kNormBlocks));
   hipLaunchKernelGGL(adam_norm_kernel, dim3(nb), dim3(kStreamThreads), 0, st, n, grad, c.inv_loss_scale, part,
                      flag);
   hipError_t e = hipGetLastError();
@@ -238,7 +292,7 @@ hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, f
                      stats);
   e = hipGetLastError();
   if (e != hipSuccess || n == 0) return e;
-  const int grid = stream_grid(n / 4 + 1);
+  const int grid = stream_grid(n / 8 + 1, kOptBlocks);
   hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
                      static_cast<bf16_t*>(w_bf16), stats);
   return hipGetLastError();
