@@ -342,6 +342,42 @@ def layer_fwd(sh: LayerShape, x: np.ndarray, full: dict):
     return out, state
 
 
+def layer_fwd_rows(sh: LayerShape, x_seq: np.ndarray, full: dict, rows) -> np.ndarray:
+    """Output rows of the unsliced layer for some positions of ONE sequence.
+
+    x_seq is one sequence [seq, h]; `rows` are positions in it. The same
+    definition as layer_fwd with one slice (pre-LN block, causal attention of
+    all heads, GeLU MLP, biases and residuals), computed only where the
+    requested rows need it: keys and values for every position up to the last
+    requested row, everything else for the requested rows alone. Used to check
+    layers too large for the full oracle on sampled rows.
+    """
+    h, nh, d = sh.hidden, sh.heads, sh.head_dim
+    rows = np.asarray(rows, dtype=np.int64)
+    last = int(rows.max()) + 1
+    x_seq = np.asarray(x_seq, dtype=np.float64)
+    y, _, _, _ = layernorm_fwd(x_seq[:last], full["ln1_g"], full["ln1_b"], sh.eps)
+    w_qkv = full["w_qkv"]
+    b_qkv = np.asarray(full["b_qkv"], dtype=np.float64)
+    k = y @ np.asarray(w_qkv[:, h:2 * h], dtype=np.float64) + b_qkv[h:2 * h]
+    v = y @ np.asarray(w_qkv[:, 2 * h:], dtype=np.float64) + b_qkv[2 * h:]
+    q = y[rows] @ np.asarray(w_qkv[:, :h], dtype=np.float64) + b_qkv[:h]
+    k = k.reshape(last, nh, d)
+    v = v.reshape(last, nh, d)
+    o = np.empty((len(rows), h))
+    for j, r in enumerate(rows):
+        qr = q[j].reshape(nh, d)
+        s = np.einsum("chd,hd->hc", k[:r + 1], qr) / np.sqrt(d)    # [heads, visible keys]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        o[j] = np.einsum("hc,chd->hd", p, v[:r + 1]).reshape(h)
+    x1 = x_seq[rows] + o @ np.asarray(full["w_o"], dtype=np.float64) + full["b_o"]
+    y2, _, _, _ = layernorm_fwd(x1, full["ln2_g"], full["ln2_b"], sh.eps)
+    u = y2 @ np.asarray(full["w_a"], dtype=np.float64) + full["b_a"]
+    return x1 + gelu(u) @ np.asarray(full["w_b"], dtype=np.float64) + full["b_b"]
+
+
 def layer_bwd(sh: LayerShape, g: np.ndarray, full: dict, state: dict):
     """Gradients of L = <Out, g> for the full layer, assembled from t slices.
 

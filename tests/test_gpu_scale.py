@@ -1,0 +1,176 @@
+"""GPU parity at the full measured sizes, on sampled outputs the oracle computes.
+
+* Adam over one GPU's parameter share (1,887,436,800 parameters, four bf16
+  micro-batch gradients, step 100, clipping active): the GPU runs the whole
+  accumulation and step; the oracle checks the accumulator and the update on
+  seeded chunks of 2^20 elements (always the first and the last chunk) and the
+  global norm and clip coefficient from an exact float64 pass over the GPU's
+  float32 accumulator, streamed to the host in pieces.
+  Tolerances: accumulator 1e-6, norm and clip coefficient 1e-6, delta p, m, v
+  1e-4 (||gpu - oracle||_inf / ||oracle||_inf per chunk), bf16 weights within
+  one bf16 ulp of the oracle's rounded master weights.
+
+* The whole layer as 8 slices (h 20480, 128 heads x 160, MLP 81920, batch 4
+  x seq 2048): the GPU runs the 8 attention halves, the partial sum, the 8
+  MLP halves and the partial sum; the unsliced oracle computes 32 seeded rows
+  of every sequence (always its first and last position) in float64.
+  Tolerance 2e-2 (||gpu - oracle||_inf / ||oracle||_inf over the rows).
+
+Inputs at these sizes are drawn with torch's seeded generator on the GPU
+(numpy would need minutes for 1.9e9 or 5e9 values), with the distributions of
+the other workloads: activations N(0,1), weights and biases N(0,0.02),
+LayerNorm gains 1 + N(0,0.02); the oracle receives the same values.
+"""
+import numpy as np
+import pytest
+
+from oracle import adam as OA
+from oracle import layer as OL
+from synth.inputs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import tensor_sliced_transformer_amd as tst  # noqa: E402
+
+CHUNK = 1 << 20
+
+
+def _bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().astype(np.int64) & 0xFFFF
+
+
+def test_adam_full_share():
+    w = WORKLOADS[4]
+    n = w.extra["n"]
+    print(f"adam full share n={n}", flush=True)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4000 + 17)
+    master = torch.randn(n, device=dev, generator=gen).mul_(0.02)
+    m = torch.randn(n, device=dev, generator=gen).mul_(1e-3)
+    v = torch.randn(n, device=dev, generator=gen).mul_(1e-3).square_()
+    grads = [torch.randn(n, device=dev, generator=gen).mul_(1e-3).to(torch.bfloat16) for _ in range(4)]
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    wbf = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    stats = torch.zeros(3, dtype=torch.float32, device=dev)
+    ws = torch.empty(tst.adam_workspace_bytes(n), dtype=torch.uint8, device=dev)
+
+    rng = np.random.Generator(np.random.PCG64(4004))
+    starts = sorted({0, n - CHUNK, *[int(s) for s in rng.integers(0, n - CHUNK, size=2)]})
+    sl = [slice(s, s + CHUNK) for s in starts]
+    pre = [(master[s].double().cpu().numpy(), m[s].double().cpu().numpy(), v[s].double().cpu().numpy())
+           for s in sl]
+    gchunks = [[g[s].float().cpu().numpy().astype(np.float64) for g in grads] for s in sl]
+
+    for k, g in enumerate(grads):
+        tst.grad_accumulate(g, acc, overwrite=(k == 0))
+    torch.cuda.synchronize()
+    acc_chunks = [acc[s].double().cpu().numpy() for s in sl]
+    for a, gs in zip(acc_chunks, gchunks):
+        ref = OA.accumulate(gs)
+        assert np.max(np.abs(a - ref)) / np.max(np.abs(ref)) < 1e-6
+
+    # exact float64 norm of the GPU's float32 accumulator, on the host
+    sq = 0.0
+    piece = 1 << 26
+    for s0 in range(0, n, piece):
+        x = acc[s0:s0 + piece].cpu().numpy().astype(np.float64)
+        sq += float(np.dot(x, x))
+    cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, max_grad_norm=1.0,
+                        inv_loss_scale=1.0, step=100)
+    norm = float(np.sqrt(sq))
+    coef = min(1.0, cfg.max_grad_norm / (norm + OA.CLIP_EPS))
+    assert coef < 1.0, "the share's gradient norm should be clipped"
+
+    c = tst.AdamCfg(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.max_grad_norm,
+                    cfg.inv_loss_scale, cfg.step)
+    tst.adam_step(c, master, m, v, acc, wbf, stats, ws)
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy()
+    print(f"norm gpu {st[0]:.7g} oracle {norm:.7g}; coef gpu {st[1]:.7g} oracle {coef:.7g}", flush=True)
+    assert st[2] == 0.0
+    assert abs(st[0] - norm) / norm < 1e-6
+    assert abs(st[1] - coef) / coef < 1e-6
+
+    for s, (p0, m0, v0), a in zip(sl, pre, acc_chunks):
+        rp, rm, rv, rw = OA.adam_update(p0, m0, v0, a, cfg, coef, False)
+        gp = master[s].double().cpu().numpy()
+        for name, got, ref in (("dp", gp - p0, rp - p0), ("m", m[s].double().cpu().numpy(), rm),
+                               ("v", v[s].double().cpu().numpy(), rv)):
+            err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+            assert err < 1e-4, f"{name} at {s.start}: {err:.3e}"
+        got_w = _bf16_bits(wbf[s])
+        ref_w = _bf16_bits(torch.from_numpy(rw.astype(np.float32)).to(torch.bfloat16))
+        assert np.max(np.abs(got_w - ref_w)) <= 1, f"w at {s.start}"
+
+
+def test_full_layer_eight_slices_sampled_rows():
+    w = WORKLOADS[5]
+    sh = OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=w.tp)
+    h, f, T = w.hidden, w.ffn, w.tokens
+    print(f"full layer: {w.tp} slices, batch {w.batch} x seq {w.seq}, h {h}", flush=True)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5000 + 17)
+
+    def rnd(shape, std=0.02, mean=0.0):
+        t = torch.randn(shape, device=dev, generator=gen).mul_(std)
+        if mean:
+            t.add_(mean)
+        return t.to(torch.bfloat16)
+
+    full = {}
+    for k, s in OL.full_param_shapes(sh).items():
+        full[k] = rnd(s, 0.02, 1.0 if k in ("ln1_g", "ln2_g") else 0.0)
+    x = rnd((T, h), 1.0)
+
+    # slice the full parameters on the GPU (the slices are what each GPU of the
+    # sliced layer would hold)
+    wl, fl = sh.local_width, sh.local_ffn
+    pa, pm = [], []
+    for i in range(sh.tp):
+        cols = torch.from_numpy(OL.qkv_columns(sh, i)).to(dev)
+        pa.append({"ln_g": full["ln1_g"], "ln_b": full["ln1_b"],
+                   "w_in": full["w_qkv"].index_select(1, cols).contiguous(),
+                   "b_in": full["b_qkv"].index_select(0, cols).contiguous(),
+                   "w_out": full["w_o"][i * wl:(i + 1) * wl].contiguous()})
+        pm.append({"ln_g": full["ln2_g"], "ln_b": full["ln2_b"],
+                   "w_in": full["w_a"][:, i * fl:(i + 1) * fl].contiguous(),
+                   "b_in": full["b_a"][i * fl:(i + 1) * fl].contiguous(),
+                   "w_out": full["w_b"][i * fl:(i + 1) * fl].contiguous()})
+    descs = [tst.make_desc(w.batch, w.seq, h, w.heads, f, w.tp, i, tst.BF16, 1e-5) for i in range(sh.tp)]
+    sav_a = torch.empty(tst.saved_bytes(descs[0], tst.ATTN), dtype=torch.uint8, device=dev)
+    sav_m = torch.empty(tst.saved_bytes(descs[0], tst.MLP), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(tst.workspace_bytes(descs[0], tst.ATTN), tst.workspace_bytes(descs[0], tst.MLP)),
+                     dtype=torch.uint8, device=dev)
+    parts = [torch.empty((T, h), dtype=torch.bfloat16, device=dev) for _ in range(sh.tp)]
+    x1 = torch.empty((T, h), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(x1)
+    for i in range(sh.tp):
+        tst.layer_fwd(descs[i], tst.ATTN, pa[i], x, parts[i], sav_a, ws)
+    tst.reduce_partials(parts, x1, residual=x, bias=full["b_o"])
+    for i in range(sh.tp):
+        tst.layer_fwd(descs[i], tst.MLP, pm[i], x1, parts[i], sav_m, ws)
+    tst.reduce_partials(parts, out, residual=x1, bias=full["b_b"])
+    torch.cuda.synchronize()
+    del pa, pm, parts, sav_a, sav_m, ws
+
+    full_np = {k: v.float().cpu().numpy().astype(np.float64) for k, v in full.items()}
+    del full
+    x_np = x.float().cpu().numpy().astype(np.float64)
+    out_np = out.float().cpu().numpy().astype(np.float64)
+    rng = np.random.Generator(np.random.PCG64(5005))
+    got, ref = [], []
+    for b in range(w.batch):
+        rows = sorted({0, w.seq - 1, *rng.integers(1, w.seq - 1, size=30).tolist()})
+        print(f"sequence {b}: {len(rows)} rows", flush=True)
+        ref.append(OL.layer_fwd_rows(sh, x_np[b * w.seq:(b + 1) * w.seq], full_np, rows))
+        got.append(out_np[[b * w.seq + r for r in rows]])
+    got, ref = np.concatenate(got), np.concatenate(ref)
+    err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    print(f"full layer sampled rows: rel_inf {err:.3e}", flush=True)
+    assert err < 2e-2

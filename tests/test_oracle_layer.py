@@ -96,6 +96,30 @@ def test_brute_force_forward(tp):
     assert rel(out, ref) < 1e-12
 
 
+def test_rows_forward_against_brute_force():
+    """The row-sampled unsliced forward equals the brute-force layer on those rows."""
+    sh = L.LayerShape(batch=2, seq=3, hidden=4, heads=2, ffn=6, tp=1)
+    p = make_full(sh, seed=1)
+    x = rng(2).standard_normal((sh.tokens, sh.hidden))
+    ref = brute_layer(sh, x, p)
+    for b, rows in ((0, [2]), (1, [0, 2]), (1, [1])):
+        got = L.layer_fwd_rows(sh, x[b * sh.seq:(b + 1) * sh.seq], p, rows)
+        assert rel(got, ref[[b * sh.seq + r for r in rows]]) < 1e-12
+
+
+@pytest.mark.parametrize("tp", [1, 8])
+def test_rows_forward_against_layer(tp):
+    """...and the (sliced) full oracle layer on sampled rows of every sequence."""
+    sh = L.LayerShape(batch=3, seq=16, hidden=64, heads=8, ffn=128, tp=tp)
+    p = make_full(sh, seed=11)
+    x = rng(12).standard_normal((sh.tokens, sh.hidden))
+    out, _ = L.layer_fwd(sh, x, p)
+    for b in range(sh.batch):
+        rows = sorted({0, sh.seq - 1, *rng(20 + b).integers(0, sh.seq, size=4).tolist()})
+        got = L.layer_fwd_rows(sh, x[b * sh.seq:(b + 1) * sh.seq], p, rows)
+        assert rel(got, out[[b * sh.seq + r for r in rows]]) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # slicing invariant (forward and backward)
 # --------------------------------------------------------------------------
