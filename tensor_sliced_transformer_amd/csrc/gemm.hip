@@ -814,6 +814,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
     for (int s = 0; s < 4; ++s) {
       if (s < 3) read_frags(st, s + 1, (s + 1) & 1);
       mfmas(s & 1);
+      // Schedule: one MFMA, then one LDS read of the next substep's fragments,
+      // and so on, so every read has the rest of the substep to land (left to
+      // itself the compiler issues the reads late and waits on them at once).
+      constexpr int NR = (A_KC ? FM : 2 * FM) + (B_KC ? FN : 2 * FN);  // read instructions
+      constexpr int NM = FM * FN;
+      if (s < 3) {
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, NR / NM > 0 ? NR / NM : 1, 0);  // DS read
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // tile kt+1 has landed (this wave's part)
     __syncthreads();
