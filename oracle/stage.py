@@ -1,0 +1,94 @@
+"""Float64 oracle of one pipeline stage: chained layers, micro-batch gradient
+accumulation and one Adam step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+GPU library.
+
+From the pages: the 105 layers of MT-NLG 530B are divided over a 35-way
+pipeline with 8-way tensor slicing inside each node (jiqizhixin MT-NLG
+article, paragraph on the 3D-parallel system), so one GPU holds three
+consecutive layer slices; the batch is processed as micro-batches whose
+gradients are accumulated before the optimizer step (Elamur summary page, Key
+points).
+
+Readings:
+
+* A stage applies its layers in order; its backward runs them in reverse,
+  each layer receiving the gradient of its output from the layer after it.
+* Each micro-batch is independent: its forward and backward see the same
+  parameters, and the step's accumulated gradient is the sum of the
+  micro-batch gradients (the gradient of the sum of their losses).
+* The stage's loss stand-in is L = sum_k <Y_k, G_k> with G_k the given
+  gradient of micro-batch k's output (what the next stage would send).
+* One slice (t = 1) is the whole layer, so the stage oracle works on full
+  parameters; the optimizer step is the one in ``oracle.adam`` over all of
+  the stage's parameters as one share.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import adam as OA
+from . import layer as OL
+
+# Order of a layer's tensors in a flat parameter vector: attention half, then
+# MLP half, each (LayerNorm gain, LayerNorm bias, first linear weight and
+# bias, second linear weight, its bias added after the slice sum).
+FLAT_ORDER = (("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o"),
+              ("ln2_g", "ln2_b", "w_a", "b_a", "w_b", "b_b"))
+
+
+def stage_fwd(sh: OL.LayerShape, layers: list, x: np.ndarray):
+    """Output of the chained layers for input x, and the per-layer states."""
+    states = []
+    h = x
+    for full in layers:
+        h, st = OL.layer_fwd(sh, h, full)
+        states.append(st)
+    return h, states
+
+
+def stage_bwd(sh: OL.LayerShape, layers: list, states: list, g: np.ndarray):
+    """Gradient of L = <Y, g> w.r.t. the stage input and every layer's parameters."""
+    grads = [None] * len(layers)
+    for i in reversed(range(len(layers))):
+        g, grads[i] = OL.layer_bwd(sh, g, layers[i], states[i])
+    return g, grads
+
+
+def stage_loss(sh: OL.LayerShape, layers: list, xs, gs) -> float:
+    """L = sum over micro-batches k of <Y_k, G_k>."""
+    return float(sum((stage_fwd(sh, layers, x)[0] * g).sum() for x, g in zip(xs, gs)))
+
+
+def flatten(layer_dicts: list) -> np.ndarray:
+    """Concatenate per-layer tensors (parameters or gradients) in FLAT_ORDER."""
+    parts = []
+    for d in layer_dicts:
+        for half in FLAT_ORDER:
+            for k in half:
+                parts.append(np.asarray(d[k], dtype=np.float64).reshape(-1))
+    return np.concatenate(parts)
+
+
+def stage_micro_batches(sh: OL.LayerShape, layers: list, xs, gs):
+    """Forward and backward of every micro-batch. Returns (ys, dxs, per-micro-batch
+    flat gradients)."""
+    ys, dxs, flats = [], [], []
+    for x, g in zip(xs, gs):
+        y, states = stage_fwd(sh, layers, x)
+        dx, grads = stage_bwd(sh, layers, states, g)
+        ys.append(y)
+        dxs.append(dx)
+        flats.append(flatten(grads))
+    return ys, dxs, flats
+
+
+def stage_step(sh: OL.LayerShape, layers: list, xs, gs, master, m, v, cfg: OA.AdamConfig):
+    """The whole stage step: micro-batches, accumulation of their gradients, Adam.
+
+    Returns (ys, dxs, acc, (master, m, v, w, stats)).
+    """
+    ys, dxs, flats = stage_micro_batches(sh, layers, xs, gs)
+    acc = OA.accumulate(flats)
+    return ys, dxs, acc, OA.adam_step(master, m, v, acc, cfg)
