@@ -10,14 +10,19 @@ algorithmic FLOP count of the step (GEMMs plus causal attention, 2 per
 multiply-add, 7.795e12) divided by the step time.
 
 Also measured in the same run:
+  * the same step with activation recompute (each half's backward re-runs its
+    forward from the half's input);
   * the optimizer over one GPU's share of the 530B model (1,887,436,800
     parameters): fp32 accumulation of 4 bf16 micro-batch gradients, then the
     fused unscale + global-norm clip + Adam step, as HBM GB/s;
+  * one pipeline stage (3 chained layer slices, 4 micro-batches, gradient
+    accumulation with the norm folded into the last pass, Adam), with and
+    without activation recompute, as TFLOP/s of the model FLOPs;
   * each GEMM launch of the step alone (HIP events on the stream it runs on)
     for the roofline of the GEMM kernel;
   * the float64 CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam] [--no-recompute] [--no-stage]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -44,6 +49,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-adam", action="store_true")
     ap.add_argument("--adam-reps", type=int, default=5)
+    ap.add_argument("--no-recompute", action="store_true")
+    ap.add_argument("--no-stage", action="store_true")
+    ap.add_argument("--stage-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -139,6 +147,44 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"fwd+bwd step {ms:.3f} ms = {tflops:.1f} TFLOP/s")
 
+    # ---- the same step with the backward recomputing each half's forward from
+    # its input (only the layer inputs are kept between forward and backward) ----
+    rc = None
+    if not args.no_recompute:
+        ws_rc = torch.empty(max(tst.recompute_workspace_bytes(desc, tst.ATTN),
+                                tst.recompute_workspace_bytes(desc, tst.MLP)), dtype=torch.uint8, device=dev)
+
+        def step_rc():
+            tst.layer_fwd(desc, tst.ATTN, pa_call, x, part, sav_a, ws)
+            tst.reduce_partials([part], x1, residual=x, bias=pa["b_out"])
+            tst.layer_fwd(desc, tst.MLP, pm_call, x1, part, sav_m, ws)
+            tst.reduce_partials([part], out, residual=x1, bias=pm["b_out"])
+            tst.layer_bwd_recompute(desc, tst.MLP, pm_call, x1, g, dxp, gm, ws_rc)
+            tst.reduce_partials([dxp], g1, residual=g)
+            tst.layer_bwd_recompute(desc, tst.ATTN, pa_call, x, g1, dxp, ga, ws_rc)
+            tst.reduce_partials([dxp], dx, residual=g1)
+
+        for _ in range(args.warmup):
+            step_rc()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            step_rc()
+        end.record()
+        torch.cuda.synchronize()
+        ms_rc = start.elapsed_time(end) / args.steps
+        # executed work: the step plus a second forward without the two output GEMMs
+        hw_flops = flops + flops / 3.0 - 2.0 * T * h * (wl + fl)
+        rc = {"ms_per_step": round(ms_rc, 4),
+              "model_tflops": round(flops / (ms_rc * 1e-3) / 1e12, 2),
+              "executed_tflops": round(hw_flops / (ms_rc * 1e-3) / 1e12, 2),
+              "executed_flop_per_step": hw_flops,
+              "note": "model_tflops counts the step's 3x-forward FLOPs; executed_tflops adds "
+                      "the recomputed forward (output GEMMs skipped)"}
+        log(f"recompute step {ms_rc:.3f} ms = {rc['model_tflops']} model / {rc['executed_tflops']} "
+            f"executed TFLOP/s")
+        del ws_rc
+
     # ---- each GEMM launch of the step alone (same shapes and operand layouts) ----
     gemm_rows = gemm_breakdown(torch, tst, dev, T, h, wl, fl)
     g_fl = sum(r["flop"] for r in gemm_rows)
@@ -172,11 +218,17 @@ def main():
                      "launches": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                                   for r in gemm_rows]},
     }
+    if rc is not None:
+        result["recompute"] = rc
     del pa, pm, ga, gm, sav_a, sav_m, ws
     torch.cuda.empty_cache()
 
     if not args.no_adam:
         result["adam"] = adam_bench(torch, tst, dev, args.adam_reps)
+
+    if not args.no_stage:
+        result["stage"] = stage_bench(torch, tst, dev, args.stage_steps, 1, flops, False)
+        result["stage_recompute"] = stage_bench(torch, tst, dev, args.stage_steps, 1, flops, True)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pa_np, pm_np, x_np, g_np)
@@ -278,6 +330,39 @@ def adam_bench(torch, tst, dev, reps):
     t_acc /= reps
     t_step /= reps
     st = stats.cpu().tolist()
+
+    # the norm folded into the last accumulation, then the update alone
+    def accumulate_norm():
+        for k, gk in enumerate(grads):
+            if k + 1 < len(grads):
+                tst.grad_accumulate(gk, acc, overwrite=(k == 0))
+            else:
+                tst.grad_accumulate_norm(gk, acc, k == 0, cfg.inv_loss_scale, ws)
+
+    def opt_update():
+        tst.adam_update(cfg, master, m, v, acc, wbf, stats, ws)
+
+    accumulate_norm()
+    opt_update()
+    torch.cuda.synchronize()
+    f_acc = f_upd = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        accumulate_norm()
+        ev[1].record()
+        opt_update()
+        ev[2].record()
+        torch.cuda.synchronize()
+        f_acc += ev[0].elapsed_time(ev[1])
+        f_upd += ev[1].elapsed_time(ev[2])
+    f_acc /= reps
+    f_upd /= reps
+    fused = {"accumulate_with_norm_ms": round(f_acc, 3), "update_ms": round(f_upd, 3),
+             "update_GBps": round(30.0 * n / (f_upd * 1e-3) / 1e9, 1),
+             "total_ms": round(f_acc + f_upd, 3), "unfused_total_ms": round(t_acc + t_step, 3),
+             "bytes_per_param": 66, "unfused_bytes_per_param": 70}
+    log(f"norm folded into the last accumulation: {f_acc:.2f} + update {f_upd:.2f} ms "
+        f"(unfused {t_acc:.2f} + {t_step:.2f} ms)")
     acc_gbs = 36.0 * n / (t_acc * 1e-3) / 1e9
     step_gbs = 34.0 * n / (t_step * 1e-3) / 1e9
     log(f"accumulate x4 {t_acc:.2f} ms = {acc_gbs:.0f} GB/s; step {t_step:.2f} ms = {step_gbs:.0f} GB/s; "
@@ -287,8 +372,61 @@ def adam_bench(torch, tst, dev, reps):
            "step_hbm_frac": round(step_gbs / PEAK_HBM_GBS, 4), "step_bytes_per_param": 34,
            "accumulate_ms": round(t_acc, 3), "accumulate_GBps": round(acc_gbs, 1),
            "accumulate_hbm_frac": round(acc_gbs / PEAK_HBM_GBS, 4), "accumulate_bytes_per_param": 36,
-           "grad_norm": st[0], "clip_coef": st[1], "found_inf": st[2]}
+           "grad_norm": st[0], "clip_coef": st[1], "found_inf": st[2], "fused_norm": fused}
     del master, m, v, grads, acc, wbf, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def stage_bench(torch, tst, dev, steps, warmup, layer_flops, recompute):
+    """One pipeline stage on one GPU: 3 chained 1/8 layer slices, 4 micro-batches of
+    2048 tokens, gradient accumulation with the norm folded in, then Adam."""
+    from synth.inputs import WORKLOADS
+    w = WORKLOADS[7]
+    L, MB = w.extra["layers"], w.extra["micro_batches"]
+    ld = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, 0, tst.BF16, 1e-5)
+    sd = tst.make_stage_desc(ld, L, MB, recompute)
+    n = tst.stage_param_count(sd)
+    offs = tst.stage_param_offsets(sd)
+    log(f"stage: {L} layers x {MB} micro-batches, {n} parameters, recompute {recompute}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7000)
+    master = torch.randn(n, device=dev, generator=gen).mul_(0.02)
+    for lay in offs:
+        for half in lay:
+            master[half["ln_g"]:half["ln_g"] + w.hidden].add_(1.0)
+    m = torch.randn(n, device=dev, generator=gen).mul_(1e-3)
+    v = torch.randn(n, device=dev, generator=gen).mul_(1e-3).square_()
+    wt = master.to(torch.bfloat16)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    x = torch.randn((MB, w.tokens, w.hidden), device=dev, generator=gen).to(torch.bfloat16)
+    dy = torch.randn((MB, w.tokens, w.hidden), device=dev, generator=gen).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    stats = torch.zeros(3, dtype=torch.float32, device=dev)
+    ws = torch.empty(tst.stage_workspace_bytes(sd), dtype=torch.uint8, device=dev)
+    cfg = tst.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 100)
+    for _ in range(warmup):
+        tst.stage_step(sd, cfg, wt, master, m, v, grad, acc, x, dy, y, dx, stats, ws)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        tst.stage_step(sd, cfg, wt, master, m, v, grad, acc, x, dy, y, dx, stats, ws)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = L * MB * layer_flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    st = stats.cpu().tolist()
+    log(f"stage step {ms:.2f} ms = {tflops:.1f} TFLOP/s (model FLOPs), stats {st}")
+    out = {"layers": L, "micro_batches": MB, "tokens_per_micro_batch": w.tokens, "n_params": n,
+           "recompute": bool(recompute), "steps": steps, "ms_per_step": round(ms, 3), "tflops": round(tflops, 2),
+           "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flop_per_step": flops,
+           "workspace_bytes": tst.stage_workspace_bytes(sd), "grad_norm": st[0], "clip_coef": st[1],
+           "found_inf": st[2]}
+    del master, m, v, wt, grad, acc, x, dy, y, dx, ws
     torch.cuda.empty_cache()
     return out
 

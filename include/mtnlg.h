@@ -149,6 +149,25 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
                     const void* x, const void* saved, const void* dy, void* dx_partial,
                     const mtnlg_half_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
+/* Backward of one half with activation recomputation: the caller keeps only
+ * the half's input x (no `saved` buffer between forward and backward). The
+ * call first recomputes, into its workspace, everything mtnlg_layer_fwd saves
+ * (LayerNorm, the QKV or MLP-up product and, for ATTN, the attention output
+ * and lse; the row-sliced output product is not needed and is skipped), then
+ * runs exactly the mtnlg_layer_bwd of that half. All kernels are
+ * deterministic, so dx_partial and the grads are bit-identical to those of
+ * mtnlg_layer_fwd + mtnlg_layer_bwd on the same inputs. This trades one more
+ * forward for the activation memory that the MT-NLG paper summary (Key
+ * points) budgets per micro-batch.
+ * ws: at least mtnlg_recompute_workspace_bytes(desc, half) bytes, owned by
+ * the caller; its first part holds the recomputed saved tensors, the rest is
+ * the backward's scratch. Argument meaning, layouts, overwrite semantics and
+ * errors are those of mtnlg_layer_bwd (MTNLG_ERR_WORKSPACE if ws is too small). */
+size_t mtnlg_recompute_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half);
+int mtnlg_layer_bwd_recompute(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params,
+                              const void* x, const void* dy, void* dx_partial, const mtnlg_half_grads* grads,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* out = residual + bias + sum_{j<n} partials[j], summed in fp32 and rounded
  * once (the g all-reduce, or f's backward, done locally on one device).
  *   partials   HOST array of n DEVICE pointers, each [rows, cols] dtype; 1 <= n <= 16
@@ -159,6 +178,38 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
 int mtnlg_reduce_partials(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials,
                           int32_t n, const void* residual, const void* bias, void* out,
                           void* stream);
+
+/* Dropout at the end of a half (STRONGHOLD slides, slide 8: the row-sliced
+ * linear's output goes through dropout, Z = Dropout(Y B), i.e. after operator
+ * g has summed the slices; the attention half is treated the same way). The
+ * keep mask is drawn from Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) so that the
+ * backward regenerates it instead of storing it: element e of the row-major
+ * [rows, cols] tensor takes 16 bits of the generator's block at counter
+ * (e / 16, 0, 0, 0) under key (seed, site) -- bits 16 * (e % 4) of word
+ * (e % 16) / 4 -- and is kept when those bits, as an integer, are
+ * >= thr = nearbyint((double)p * 65536) (ties to even); kept values are
+ * scaled by 65536 / (65536 - thr). `site` distinguishes the dropout sites of
+ * one step (layer, half, micro-batch). 0 <= p < 1 (p = 0 keeps everything);
+ * otherwise MTNLG_ERR_ARG. */
+typedef struct {
+  uint64_t seed, site;
+  float p;
+} mtnlg_dropout;
+
+/* out = residual + keep * scale * (sum_{j<n} partials[j] + bias): the partial
+ * sum of mtnlg_reduce_partials with dropout applied to the half's output
+ * before the residual. Arguments, layouts and errors as mtnlg_reduce_partials. */
+int mtnlg_reduce_partials_dropout(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials,
+                                  int32_t n, const void* residual, const void* bias,
+                                  const mtnlg_dropout* dropout, void* out, void* stream);
+
+/* The backward of that dropout: dz = keep * scale * dy with the same mask
+ * (same rows, cols and dropout struct). dz is the dy the half's backward
+ * (mtnlg_layer_bwd) takes; the residual path keeps dy itself.
+ *   dy, dz [rows, cols] dtype, must not alias. cols a positive multiple of 8. */
+int mtnlg_dropout_bwd(int64_t rows, int64_t cols, int32_t dtype, const void* dy,
+                      const mtnlg_dropout* dropout, void* dz, void* stream);
 
 /* Gradient accumulation over micro-batches (Elamur summary, Key points):
  * acc[i] = (overwrite ? 0 : acc[i]) + grad[i] for i < n, in fp32.
@@ -193,6 +244,89 @@ size_t mtnlg_adam_workspace_bytes(int64_t n);
 int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v,
                     const float* grad, void* w_bf16, float* stats, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* The optimizer's norm pass folded into the last micro-batch's accumulation
+ * (Elamur summary, Key points: micro-batch gradient accumulation; the norm and
+ * clip are this library's reading): one pass does
+ *   acc[i] = (overwrite ? 0 : acc[i]) + grad[i]   (as mtnlg_grad_accumulate)
+ * and leaves in ws, per workgroup, the fp64 sum of (acc[i]*inv_loss_scale)^2
+ * and a non-finite flag. mtnlg_adam_update then takes the step without
+ * reading acc a second time for the norm (4 bytes per parameter less).
+ *   grad [n] dtype, acc [n] f32 (may be NULL only when n == 0);
+ *   ws >= mtnlg_adam_workspace_bytes(n), device memory the caller owns; its
+ *   contents are consumed by the next mtnlg_adam_update on the same stream.
+ * n >= 0 (n == 0 writes an empty norm). Errors as mtnlg_grad_accumulate,
+ * plus MTNLG_ERR_WORKSPACE and MTNLG_ERR_ARG for a non-finite inv_loss_scale. */
+int mtnlg_grad_accumulate_norm(int64_t n, int32_t dtype, const void* grad, float* acc,
+                               int32_t overwrite, float inv_loss_scale, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* mtnlg_adam_step without its own norm pass: the norm, clip coefficient and
+ * found_inf come from the partials that mtnlg_grad_accumulate_norm left in
+ * ws. Same arguments, semantics and errors as mtnlg_adam_step, with three
+ * conditions the caller keeps: grad is that call's acc, n is that call's n,
+ * and cfg->inv_loss_scale equals that call's inv_loss_scale (the update
+ * scales by it; the norm was formed with it). ws is only read. */
+int mtnlg_adam_update(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v,
+                      const float* grad, void* w_bf16, float* stats, const void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ---- One pipeline stage on one GPU ----
+ *
+ * A stage is `layers` consecutive decoder layers, each held as the same slice
+ * (desc.layer.tp_rank of desc.layer.tp_size) -- in MT-NLG 530B, 105 layers in
+ * 35 pipeline stages of 3 (jiqizhixin MT-NLG article, system paragraph) --
+ * trained on `micro_batches` micro-batches whose gradients are accumulated
+ * before one optimizer step (Elamur summary, Key points). On one GPU the
+ * all-reduces that join the slices (operators f and g) are the identity:
+ * each layer's partial is summed alone, with its residual and output bias,
+ * by mtnlg_reduce_partials; on a real tensor-sliced run this is where the
+ * all-reduce would be. Only BF16 layers (mixed precision) are supported. */
+typedef struct {
+  mtnlg_layer_desc layer;  /* shape and slice of every layer; batch sequences per micro-batch */
+  int32_t layers;          /* >= 1 */
+  int32_t micro_batches;   /* >= 1 */
+  int32_t recompute;       /* 0: keep each layer's saved tensors from forward to backward;
+                              1: keep only each half's input and recompute in the backward */
+} mtnlg_stage_desc;
+
+/* The stage's parameters live in ONE flat element array (the bf16 weights,
+ * the bf16 gradients and the fp32 master, m, v and accumulator all share this
+ * layout), layer after layer, each layer as ATTN then MLP, each half as
+ *   ln_g [h] | ln_b [h] | w_in [h, win] | b_in [win] | w_out [win, h] | b_out [h]
+ * with win = 3 * local heads * head_dim (ATTN) or ffn / tp_size (MLP), shapes
+ * and meaning as in mtnlg_half_params / mtnlg_half_grads (b_out is b_o or
+ * b_B). Every tensor starts on a multiple of 8 elements.
+ * mtnlg_stage_param_count: total elements, or -1 if the descriptor is invalid.
+ * mtnlg_stage_param_offsets: writes layers*2*6 element offsets (HOST array
+ * `off`, order layer, half, tensor as listed); MTNLG_ERR_* if invalid. */
+int64_t mtnlg_stage_param_count(const mtnlg_stage_desc* desc);
+int mtnlg_stage_param_offsets(const mtnlg_stage_desc* desc, int64_t* off);
+
+/* Scratch bytes of mtnlg_stage_step; 0 if the descriptor is invalid. */
+size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
+
+/* One training step of the stage: for each micro-batch k in order, the
+ * forward through every layer, then the backward in reverse order; then the
+ * flat gradient is accumulated into acc (overwritten by k = 0, added for
+ * k > 0; the last accumulation carries the norm pass, see
+ * mtnlg_grad_accumulate_norm); then mtnlg_adam_update with cfg.
+ *   w       [n] bf16 flat weights; read by every layer and rewritten by the
+ *           step as bf16(master)
+ *   master, m, v  [n] f32 optimizer state (updated in place)
+ *   grad    [n] bf16 scratch: one micro-batch's gradient
+ *   acc     [n] f32: the accumulated gradient (left holding it)
+ *   x       [micro_batches, T, h] bf16: stage input (T = batch * seq)
+ *   dy      [micro_batches, T, h] bf16: gradient of the stage output
+ *   y       [micro_batches, T, h] bf16: stage output, written
+ *   dx      [micro_batches, T, h] bf16: gradient of the stage input, written
+ *   stats   DEVICE f32[3]: {norm, coef, found_inf} of the step
+ *   ws      >= mtnlg_stage_workspace_bytes(desc)
+ * n = mtnlg_stage_param_count(desc). All arguments are validated before
+ * anything is enqueued; errors as the calls it makes. */
+int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, void* w, float* master,
+                     float* m, float* v, void* grad, float* acc, const void* x, const void* dy, void* y,
+                     void* dx, float* stats, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Component entry points (the kernels the layer calls, one at a time) ---- */
 

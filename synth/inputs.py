@@ -110,6 +110,11 @@ WORKLOADS = {
                 extra={"n": 1_887_436_800, "micro_batches": 4, "step": 100}),
     5: Workload(5, "mtnlg-full-layer-8-slices-b4-bf16", batch=4, seq=2048, hidden=20480,
                 heads=128, ffn=81920, tp=8, slices=tuple(range(8)), dtype="bf16"),
+    # a pipeline stage of chained layers with micro-batch accumulation
+    6: Workload(6, "stage-3-layers-tiny-bf16", batch=2, seq=128, hidden=256, heads=4, ffn=1024,
+                tp=1, slices=(0,), dtype="bf16", extra={"layers": 3, "micro_batches": 2, "step": 5}),
+    7: Workload(7, "mtnlg-stage-3-layers-shard-bf16", batch=1, seq=2048, hidden=20480, heads=128,
+                ffn=81920, tp=8, slices=(0,), dtype="bf16", extra={"layers": 3, "micro_batches": 4, "step": 100}),
 }
 
 
@@ -129,13 +134,14 @@ def _finish(x: np.ndarray, dtype: str) -> np.ndarray:
     return round_f32_to_bf16(x) if dtype == "bf16" else x
 
 
-def make_half_params(w: Workload, half: str, slice_index: int) -> dict:
-    """float32 arrays (bf16-exact when dtype is bf16) for one slice of one half.
+def make_half_params(w: Workload, half: str, slice_index: int, layer: int = 0) -> dict:
+    """float32 arrays (bf16-exact when dtype is bf16) for one slice of one half
+    of layer `layer` (layers of a stage get their own seeds).
 
     LayerNorm parameters and the row-sliced output bias are replicated across
     slices, so their seeds do not depend on the slice index.
     """
-    base = 1000 * w.index + (0 if half == "attn" else 100)
+    base = 1000 * w.index + 200 * layer + (0 if half == "attn" else 100)
     shapes = half_param_shapes(w, half)
     out = {}
     out["ln_g"] = _finish(randn(base + 1, shapes["ln_g"], 0.02, 1.0), w.dtype)

@@ -13,11 +13,14 @@ from __future__ import annotations
 
 import ctypes
 from . import _lib
-from ._lib import ATTN, MLP, BF16, F32, AdamCfg, HalfGrads, HalfParams, LayerDesc, MtnlgError, check, load
+from ._lib import ATTN, MLP, BF16, F32, AdamCfg, HalfGrads, HalfParams, LayerDesc, MtnlgError, StageDesc, check, load
 
 __all__ = ["ATTN", "MLP", "BF16", "F32", "LayerDesc", "AdamCfg", "MtnlgError", "load", "make_desc",
            "saved_bytes", "workspace_bytes", "layer_fwd", "layer_bwd", "reduce_partials",
-           "grad_accumulate", "adam_workspace_bytes", "adam_step", "gemm", "gemm_workspace_bytes", "layernorm_fwd",
+           "grad_accumulate", "adam_workspace_bytes", "adam_step", "grad_accumulate_norm", "adam_update",
+           "reduce_partials_dropout", "dropout_bwd",
+           "recompute_workspace_bytes", "layer_bwd_recompute", "StageDesc", "make_stage_desc",
+           "stage_param_count", "stage_param_offsets", "stage_workspace_bytes", "stage_step", "gemm", "gemm_workspace_bytes", "layernorm_fwd",
            "layernorm_bwd_workspace_bytes", "layernorm_bwd", "attention_fwd",
            "attention_bwd_workspace_bytes", "attention_bwd", "torch_dtype"]
 
@@ -94,6 +97,21 @@ def layer_bwd(desc, half, params: dict, x, saved, dy, dx_partial, grads: dict, w
                                  _stream(stream)), "mtnlg_layer_bwd")
 
 
+def recompute_workspace_bytes(desc: LayerDesc, half: int) -> int:
+    return int(load().mtnlg_recompute_workspace_bytes(ctypes.byref(desc), half))
+
+
+def layer_bwd_recompute(desc, half, params: dict, x, dy, dx_partial, grads: dict, ws, stream=None) -> None:
+    """One slice's half backward that first recomputes its saved activations from x
+    (mtnlg_layer_bwd_recompute); ws of recompute_workspace_bytes(desc, half) bytes."""
+    p = _params(params)
+    g = _grads(grads)
+    check(load().mtnlg_layer_bwd_recompute(ctypes.byref(desc), half, ctypes.byref(p), _ptr(x), _ptr(dy),
+                                           _ptr(dx_partial), ctypes.byref(g), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream(stream)),
+          "mtnlg_layer_bwd_recompute")
+
+
 def reduce_partials(partials, out, residual=None, bias=None, stream=None) -> None:
     """out = residual + bias + sum(partials) (mtnlg_reduce_partials)."""
     rows, cols = out.shape
@@ -102,6 +120,27 @@ def reduce_partials(partials, out, residual=None, bias=None, stream=None) -> Non
         _ptr(p)
     check(load().mtnlg_reduce_partials(rows, cols, _code(out), arr, len(partials), _ptr(residual), _ptr(bias),
                                        _ptr(out), _stream(stream)), "mtnlg_reduce_partials")
+
+
+def reduce_partials_dropout(partials, out, p: float, seed: int, site: int, residual=None, bias=None,
+                            stream=None) -> None:
+    """out = residual + keep * scale * (sum(partials) + bias) (mtnlg_reduce_partials_dropout)."""
+    rows, cols = out.shape
+    arr = (ctypes.c_void_p * len(partials))(*[t.data_ptr() for t in partials])
+    for t in partials:
+        _ptr(t)
+    d = _lib.Dropout(seed, site, p)
+    check(load().mtnlg_reduce_partials_dropout(rows, cols, _code(out), arr, len(partials), _ptr(residual),
+                                               _ptr(bias), ctypes.byref(d), _ptr(out), _stream(stream)),
+          "mtnlg_reduce_partials_dropout")
+
+
+def dropout_bwd(dy, dz, p: float, seed: int, site: int, stream=None) -> None:
+    """dz = keep * scale * dy with the mask of the same (p, seed, site) (mtnlg_dropout_bwd)."""
+    rows, cols = dy.shape
+    d = _lib.Dropout(seed, site, p)
+    check(load().mtnlg_dropout_bwd(rows, cols, _code(dy), _ptr(dy), ctypes.byref(d), _ptr(dz), _stream(stream)),
+          "mtnlg_dropout_bwd")
 
 
 def grad_accumulate(grad, acc, overwrite: bool, stream=None) -> None:
@@ -117,6 +156,55 @@ def adam_step(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None) 
     check(load().mtnlg_adam_step(ctypes.byref(cfg), master.numel(), _ptr(master), _ptr(m), _ptr(v), _ptr(grad),
                                  _ptr(w_bf16), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "mtnlg_adam_step")
+
+
+def grad_accumulate_norm(grad, acc, overwrite: bool, inv_loss_scale: float, ws, stream=None) -> None:
+    """acc (+)= grad and, in the same pass, the norm partials of acc * inv_loss_scale
+    left in ws for adam_update (mtnlg_grad_accumulate_norm)."""
+    check(load().mtnlg_grad_accumulate_norm(acc.numel(), _code(grad), _ptr(grad), _ptr(acc), int(overwrite),
+                                            float(inv_loss_scale), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)), "mtnlg_grad_accumulate_norm")
+
+
+def adam_update(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None) -> None:
+    """The Adam step on the norm partials grad_accumulate_norm left in ws (mtnlg_adam_update)."""
+    check(load().mtnlg_adam_update(ctypes.byref(cfg), master.numel(), _ptr(master), _ptr(m), _ptr(v), _ptr(grad),
+                                   _ptr(w_bf16), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "mtnlg_adam_update")
+
+
+STAGE_TENSORS = ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out")
+
+
+def make_stage_desc(layer: LayerDesc, layers: int, micro_batches: int, recompute: bool = False) -> StageDesc:
+    return StageDesc(layer, layers, micro_batches, int(recompute))
+
+
+def stage_param_count(sd: StageDesc) -> int:
+    n = int(load().mtnlg_stage_param_count(ctypes.byref(sd)))
+    if n < 0:
+        raise MtnlgError("invalid stage descriptor")
+    return n
+
+
+def stage_param_offsets(sd: StageDesc) -> list:
+    """[layer][half] -> {tensor name: element offset} in the flat parameter array."""
+    off = (ctypes.c_int64 * (sd.layers * 2 * 6))()
+    check(load().mtnlg_stage_param_offsets(ctypes.byref(sd), off), "mtnlg_stage_param_offsets")
+    return [[{k: int(off[(l * 2 + h) * 6 + i]) for i, k in enumerate(STAGE_TENSORS)} for h in range(2)]
+            for l in range(sd.layers)]
+
+
+def stage_workspace_bytes(sd: StageDesc) -> int:
+    return int(load().mtnlg_stage_workspace_bytes(ctypes.byref(sd)))
+
+
+def stage_step(sd: StageDesc, cfg: AdamCfg, w, master, m, v, grad, acc, x, dy, y, dx, stats, ws,
+               stream=None) -> None:
+    """One training step of a pipeline stage (mtnlg_stage_step)."""
+    check(load().mtnlg_stage_step(ctypes.byref(sd), ctypes.byref(cfg), _ptr(w), _ptr(master), _ptr(m), _ptr(v),
+                                  _ptr(grad), _ptr(acc), _ptr(x), _ptr(dy), _ptr(y), _ptr(dx), _ptr(stats),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "mtnlg_stage_step")
 
 
 def gemm_workspace_bytes(dtype: int, M: int, N: int, K: int) -> int:

@@ -26,6 +26,14 @@ class LayerDesc(ctypes.Structure):
                 ("ln_eps", c_float)]
 
 
+class StageDesc(ctypes.Structure):
+    _fields_ = [("layer", LayerDesc), ("layers", c_int32), ("micro_batches", c_int32), ("recompute", c_int32)]
+
+
+class Dropout(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("site", ctypes.c_uint64), ("p", c_float)]
+
+
 class HalfParams(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("ln_g", "ln_b", "w_in", "b_in", "w_out")]
 
@@ -48,12 +56,28 @@ SIGNATURES = {
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
     "mtnlg_layer_bwd": (c_int32, [POINTER(LayerDesc), c_int32, POINTER(HalfParams), c_void_p, c_void_p,
                                   c_void_p, c_void_p, POINTER(HalfGrads), c_void_p, c_size_t, c_void_p]),
+    "mtnlg_recompute_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32]),
+    "mtnlg_layer_bwd_recompute": (c_int32, [POINTER(LayerDesc), c_int32, POINTER(HalfParams), c_void_p, c_void_p,
+                                            c_void_p, POINTER(HalfGrads), c_void_p, c_size_t, c_void_p]),
     "mtnlg_reduce_partials": (c_int32, [c_int64, c_int64, c_int32, POINTER(c_void_p), c_int32, c_void_p,
                                         c_void_p, c_void_p, c_void_p]),
+    "mtnlg_reduce_partials_dropout": (c_int32, [c_int64, c_int64, c_int32, POINTER(c_void_p), c_int32, c_void_p,
+                                                c_void_p, POINTER(Dropout), c_void_p, c_void_p]),
+    "mtnlg_dropout_bwd": (c_int32, [c_int64, c_int64, c_int32, c_void_p, POINTER(Dropout), c_void_p, c_void_p]),
     "mtnlg_grad_accumulate": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
     "mtnlg_adam_workspace_bytes": (c_size_t, [c_int64]),
     "mtnlg_adam_step": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mtnlg_grad_accumulate_norm": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_int32, c_float, c_void_p,
+                                             c_size_t, c_void_p]),
+    "mtnlg_adam_update": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mtnlg_stage_param_count": (c_int64, [POINTER(StageDesc)]),
+    "mtnlg_stage_param_offsets": (c_int32, [POINTER(StageDesc), POINTER(c_int64)]),
+    "mtnlg_stage_workspace_bytes": (c_size_t, [POINTER(StageDesc)]),
+    "mtnlg_stage_step": (c_int32, [POINTER(StageDesc), POINTER(AdamCfg), c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]),
     "mtnlg_gemm_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, c_int64]),
     "mtnlg_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

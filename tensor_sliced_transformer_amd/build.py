@@ -22,7 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmtnlg.so")
 
-SOURCES = ["api.cpp", "gemm.hip", "layernorm.hip", "attention.hip", "attention_bf16.hip",
+SOURCES = ["api.cpp", "stage.cpp", "gemm.hip", "layernorm.hip", "attention.hip", "attention_bf16.hip",
            "attention_bf16_dkdv.hip", "stream.hip"]
 # Per-source extra flags. The forward and dQ attention kernels keep their MFMA
 # accumulators in VGPRs, so that the softmax arithmetic on them needs no copies

@@ -16,48 +16,14 @@
 #include <algorithm>
 
 #include "../../include/mtnlg.h"
+#include "abi_common.hpp"
 #include "kernels.hpp"
 
 using namespace mtnlg;
+using namespace mtnlg::abi;
 
 namespace {
 
-thread_local char g_last_error[512] = "";
-
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-int fail(int status, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-  va_end(ap);
-  return status;
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return fail(MTNLG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
-
-#define MTNLG_HIP(call, what)                 \
-  do {                                         \
-    hipError_t e_ = (call);                    \
-    if (e_ != hipSuccess) return hip_fail(e_, what); \
-  } while (0)
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-int check_ptr(const void* p, const char* name) {
-  if (!p) return fail(MTNLG_ERR_ARG, "%s is NULL", name);
-  if (!aligned16(p)) return fail(MTNLG_ERR_ALIGN, "%s is not 16-byte aligned", name);
-  return MTNLG_OK;
-}
-
-#define CHECK_PTR(p)                               \
-  do {                                             \
-    int s_ = check_ptr((p), #p);                   \
-    if (s_ != MTNLG_OK) return s_;                 \
-  } while (0)
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Dims {
   int64_t T;      // tokens = batch*seq
@@ -180,61 +146,10 @@ WsLayout ws_layout(const Dims& d, int half) {
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
 
-}  // namespace
-
-extern "C" {
-
-const char* mtnlg_status_str(int32_t status) {
-  switch (status) {
-    case MTNLG_OK: return "ok";
-    case MTNLG_ERR_ARG: return "invalid argument";
-    case MTNLG_ERR_SHAPE: return "unsupported or inconsistent shape";
-    case MTNLG_ERR_DTYPE: return "unsupported dtype";
-    case MTNLG_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case MTNLG_ERR_WORKSPACE: return "workspace too small";
-    case MTNLG_ERR_HIP: return "HIP error";
-    case MTNLG_ERR_UNIMPLEMENTED: return "unimplemented";
-    default: return "unknown status";
-  }
-}
-
-const char* mtnlg_last_error(void) { return g_last_error; }
-
-size_t mtnlg_saved_bytes(const mtnlg_layer_desc* desc, int32_t half) {
-  Dims d;
-  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
-  return saved_layout(d, half).total;
-}
-
-size_t mtnlg_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half) {
-  Dims d;
-  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
-  return ws_layout(d, half).total;
-}
-
-int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
-                    void* y_partial, void* saved, void* ws, size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
-  Dims d;
-  int s = validate_desc(desc, half, &d);
-  if (s != MTNLG_OK) return s;
-  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
-  CHECK_PTR(params->ln_g);
-  CHECK_PTR(params->ln_b);
-  CHECK_PTR(params->w_in);
-  CHECK_PTR(params->b_in);
-  CHECK_PTR(params->w_out);
-  CHECK_PTR(x);
-  CHECK_PTR(y_partial);
-  CHECK_PTR(saved);
-  const WsLayout W = ws_layout(d, half);
-  const size_t need = W.t1;  // the forward uses only the GEMM partial region, which comes first
-  if (need > 0) {
-    CHECK_PTR(ws);
-    if (ws_bytes < need) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
-  }
-  void* gws = need > 0 ? at(ws, W.gemm) : nullptr;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// The forward of one half into `saved`; the row-sliced output GEMM is
+// skipped when y_partial is NULL (a recompute needs only what is saved).
+int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mtnlg_half_params* params,
+                 const void* x, void* y_partial, void* saved, void* gws, hipStream_t st) {
   const SavedLayout L = saved_layout(d, half);
   void* ln_out = at(saved, L.ln_out);
   float* mean = reinterpret_cast<float*>(at(saved, L.mean));
@@ -251,51 +166,30 @@ int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
               "qkv gemm");
     MTNLG_HIP(attention_fwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, st),
               "attention_fwd");
-    MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.w, o, d.w, params->w_out, d.h, y_partial, d.h, EPI_STORE,
-                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.w, true), gws, st),
-              "out-proj gemm");
+    if (y_partial)
+      MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.w, o, d.w, params->w_out, d.h, y_partial, d.h, EPI_STORE,
+                     nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.w, true), gws, st),
+                "out-proj gemm");
   } else {
     void* u = at(saved, L.a);
     void* y = at(saved, L.b);
     MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.fl, d.h, ln_out, d.h, params->w_in, d.fl, u, d.fl, EPI_BIAS_GELU,
                    params->b_in, y, nullptr, plan_gemm(d.dtype, d.T, d.fl, d.h, true), gws, st),
               "mlp-up gemm");
-    MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.fl, y, d.fl, params->w_out, d.h, y_partial, d.h, EPI_STORE,
-                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, true), gws, st),
-              "mlp-down gemm");
+    if (y_partial)
+      MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.fl, y, d.fl, params->w_out, d.h, y_partial, d.h, EPI_STORE,
+                     nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, true), gws, st),
+                "mlp-down gemm");
   }
   return MTNLG_OK;
 }
 
-int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
-                    const void* saved, const void* dy, void* dx_partial, const mtnlg_half_grads* grads, void* ws,
-                    size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
-  Dims d;
-  int s = validate_desc(desc, half, &d);
-  if (s != MTNLG_OK) return s;
-  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
-  if (!grads) return fail(MTNLG_ERR_ARG, "grads is NULL");
-  CHECK_PTR(params->ln_g);
-  CHECK_PTR(params->ln_b);
-  CHECK_PTR(params->w_in);
-  CHECK_PTR(params->b_in);
-  CHECK_PTR(params->w_out);
-  CHECK_PTR(grads->ln_g);
-  CHECK_PTR(grads->ln_b);
-  CHECK_PTR(grads->w_in);
-  CHECK_PTR(grads->b_in);
-  CHECK_PTR(grads->w_out);
-  CHECK_PTR(grads->b_out);
-  CHECK_PTR(x);
-  CHECK_PTR(saved);
-  CHECK_PTR(dy);
-  CHECK_PTR(dx_partial);
-  CHECK_PTR(ws);
+
+// The backward of one half from `saved` (workspace laid out by ws_layout).
+int backward_from(const mtnlg_layer_desc* desc, const Dims& d, int half, const mtnlg_half_params* params,
+                  const void* x, const void* saved, const void* dy, void* dx_partial, const mtnlg_half_grads* grads,
+                  void* ws, hipStream_t st) {
   const WsLayout W = ws_layout(d, half);
-  if (ws_bytes < W.total)
-    return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, W.total);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const SavedLayout L = saved_layout(d, half);
   const void* ln_out = at(saved, L.ln_out);
   const float* mean = reinterpret_cast<const float*>(at(saved, L.mean));
@@ -360,6 +254,138 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
   return MTNLG_OK;
 }
 
+
+}  // namespace
+
+extern "C" {
+
+const char* mtnlg_status_str(int32_t status) {
+  switch (status) {
+    case MTNLG_OK: return "ok";
+    case MTNLG_ERR_ARG: return "invalid argument";
+    case MTNLG_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case MTNLG_ERR_DTYPE: return "unsupported dtype";
+    case MTNLG_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MTNLG_ERR_WORKSPACE: return "workspace too small";
+    case MTNLG_ERR_HIP: return "HIP error";
+    case MTNLG_ERR_UNIMPLEMENTED: return "unimplemented";
+    default: return "unknown status";
+  }
+}
+
+const char* mtnlg_last_error(void) { return g_last_error; }
+
+size_t mtnlg_saved_bytes(const mtnlg_layer_desc* desc, int32_t half) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return saved_layout(d, half).total;
+}
+
+size_t mtnlg_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return ws_layout(d, half).total;
+}
+
+int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
+                    void* y_partial, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  Dims d;
+  int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
+  CHECK_PTR(params->ln_g);
+  CHECK_PTR(params->ln_b);
+  CHECK_PTR(params->w_in);
+  CHECK_PTR(params->b_in);
+  CHECK_PTR(params->w_out);
+  CHECK_PTR(x);
+  CHECK_PTR(y_partial);
+  CHECK_PTR(saved);
+  const WsLayout W = ws_layout(d, half);
+  const size_t need = W.t1;  // the forward uses only the GEMM partial region, which comes first
+  if (need > 0) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  }
+  void* gws = need > 0 ? at(ws, W.gemm) : nullptr;
+  return forward_into(desc, d, half, params, x, y_partial, saved, gws, static_cast<hipStream_t>(stream));
+}
+
+int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
+                    const void* saved, const void* dy, void* dx_partial, const mtnlg_half_grads* grads, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  Dims d;
+  int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
+  if (!grads) return fail(MTNLG_ERR_ARG, "grads is NULL");
+  CHECK_PTR(params->ln_g);
+  CHECK_PTR(params->ln_b);
+  CHECK_PTR(params->w_in);
+  CHECK_PTR(params->b_in);
+  CHECK_PTR(params->w_out);
+  CHECK_PTR(grads->ln_g);
+  CHECK_PTR(grads->ln_b);
+  CHECK_PTR(grads->w_in);
+  CHECK_PTR(grads->b_in);
+  CHECK_PTR(grads->w_out);
+  CHECK_PTR(grads->b_out);
+  CHECK_PTR(x);
+  CHECK_PTR(saved);
+  CHECK_PTR(dy);
+  CHECK_PTR(dx_partial);
+  CHECK_PTR(ws);
+  const WsLayout W = ws_layout(d, half);
+  if (ws_bytes < W.total)
+    return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, W.total);
+  return backward_from(desc, d, half, params, x, saved, dy, dx_partial, grads, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+size_t mtnlg_recompute_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return align256(saved_layout(d, half).total) + ws_layout(d, half).total;
+}
+
+int mtnlg_layer_bwd_recompute(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params,
+                              const void* x, const void* dy, void* dx_partial, const mtnlg_half_grads* grads,
+                              void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  Dims d;
+  int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  if (!params) return fail(MTNLG_ERR_ARG, "params is NULL");
+  if (!grads) return fail(MTNLG_ERR_ARG, "grads is NULL");
+  CHECK_PTR(params->ln_g);
+  CHECK_PTR(params->ln_b);
+  CHECK_PTR(params->w_in);
+  CHECK_PTR(params->b_in);
+  CHECK_PTR(params->w_out);
+  CHECK_PTR(grads->ln_g);
+  CHECK_PTR(grads->ln_b);
+  CHECK_PTR(grads->w_in);
+  CHECK_PTR(grads->b_in);
+  CHECK_PTR(grads->w_out);
+  CHECK_PTR(grads->b_out);
+  CHECK_PTR(x);
+  CHECK_PTR(dy);
+  CHECK_PTR(dx_partial);
+  CHECK_PTR(ws);
+  const size_t sv = align256(saved_layout(d, half).total);
+  const WsLayout W = ws_layout(d, half);
+  if (ws_bytes < sv + W.total)
+    return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, sv + W.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* saved = ws;
+  void* rest = at(ws, sv);
+  s = forward_into(desc, d, half, params, x, nullptr, saved, at(rest, W.gemm), st);
+  if (s != MTNLG_OK) return s;
+  return backward_from(desc, d, half, params, x, saved, dy, dx_partial, grads, rest, st);
+}
+
 int mtnlg_reduce_partials(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials, int32_t n,
                           const void* residual, const void* bias, void* out, void* stream) {
   g_last_error[0] = 0;
@@ -379,6 +405,53 @@ int mtnlg_reduce_partials(int64_t rows, int64_t cols, int32_t dtype, const void*
   return MTNLG_OK;
 }
 
+static int dropout_thr(const mtnlg_dropout* dr, uint32_t* thr) {
+  if (!dr) return fail(MTNLG_ERR_ARG, "dropout is NULL");
+  if (!(dr->p >= 0.0f && dr->p < 1.0f)) return fail(MTNLG_ERR_ARG, "dropout rate must be in [0, 1)");
+  *thr = (uint32_t)nearbyint((double)dr->p * 65536.0);
+  if (*thr >= 65536u) return fail(MTNLG_ERR_ARG, "dropout rate rounds to 1");
+  return MTNLG_OK;
+}
+
+int mtnlg_reduce_partials_dropout(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials, int32_t n,
+                                  const void* residual, const void* bias, const mtnlg_dropout* dropout, void* out,
+                                  void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return fail(MTNLG_ERR_SHAPE, "rows >= 0, cols > 0 and cols %% 8 == 0");
+  if (!partials || n < 1 || n > kMaxPartials) return fail(MTNLG_ERR_ARG, "1 <= n <= %d partials", kMaxPartials);
+  uint32_t thr;
+  int s = dropout_thr(dropout, &thr);
+  if (s != MTNLG_OK) return s;
+  for (int j = 0; j < n; ++j) {
+    s = check_ptr(partials[j], "partials[j]");
+    if (s != MTNLG_OK) return s;
+  }
+  if (residual) CHECK_PTR(residual);
+  if (bias) CHECK_PTR(bias);
+  CHECK_PTR(out);
+  MTNLG_HIP(reduce_partials_dropout(dtype, rows, cols, partials, n, residual, bias, out, dropout->seed,
+                                    dropout->site, thr, static_cast<hipStream_t>(stream)),
+            "reduce_partials_dropout");
+  return MTNLG_OK;
+}
+
+int mtnlg_dropout_bwd(int64_t rows, int64_t cols, int32_t dtype, const void* dy, const mtnlg_dropout* dropout,
+                      void* dz, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return fail(MTNLG_ERR_SHAPE, "rows >= 0, cols > 0 and cols %% 8 == 0");
+  uint32_t thr;
+  int s = dropout_thr(dropout, &thr);
+  if (s != MTNLG_OK) return s;
+  CHECK_PTR(dy);
+  CHECK_PTR(dz);
+  MTNLG_HIP(dropout_bwd(dtype, rows * cols, dy, dz, dropout->seed, dropout->site, thr,
+                        static_cast<hipStream_t>(stream)),
+            "dropout_bwd");
+  return MTNLG_OK;
+}
+
 int mtnlg_grad_accumulate(int64_t n, int32_t dtype, const void* grad, float* acc, int32_t overwrite, void* stream) {
   g_last_error[0] = 0;
   if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
@@ -393,9 +466,12 @@ int mtnlg_grad_accumulate(int64_t n, int32_t dtype, const void* grad, float* acc
 
 size_t mtnlg_adam_workspace_bytes(int64_t n) { return n < 0 ? 0 : adam_ws(n); }
 
-int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
-                    void* w_bf16, float* stats, void* ws, size_t ws_bytes, void* stream) {
-  g_last_error[0] = 0;
+}  // extern "C"
+
+namespace mtnlg {
+namespace abi {
+int adam_args(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
+              void* w_bf16, float* stats, const void* ws, size_t ws_bytes, AdamScalars* c) {
   if (!cfg) return fail(MTNLG_ERR_ARG, "cfg is NULL");
   if (n < 0) return fail(MTNLG_ERR_SHAPE, "n < 0");
   if (cfg->step < 1) return fail(MTNLG_ERR_ARG, "step must be >= 1");
@@ -411,17 +487,58 @@ int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* 
   CHECK_PTR(ws);
   if (w_bf16) CHECK_PTR(w_bf16);
   if (ws_bytes < adam_ws(n)) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, adam_ws(n));
+  c->lr = cfg->lr;
+  c->beta1 = cfg->beta1;
+  c->beta2 = cfg->beta2;
+  c->eps = cfg->eps;
+  c->weight_decay = cfg->weight_decay;
+  c->max_grad_norm = cfg->max_grad_norm;
+  c->inv_loss_scale = cfg->inv_loss_scale;
+  c->inv_bc1 = (float)(1.0 / (1.0 - pow((double)cfg->beta1, (double)cfg->step)));
+  c->inv_bc2 = (float)(1.0 / (1.0 - pow((double)cfg->beta2, (double)cfg->step)));
+  return MTNLG_OK;
+}
+}  // namespace abi
+}  // namespace mtnlg
+
+extern "C" {
+
+int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
+                    void* w_bf16, float* stats, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
   AdamScalars c{};
-  c.lr = cfg->lr;
-  c.beta1 = cfg->beta1;
-  c.beta2 = cfg->beta2;
-  c.eps = cfg->eps;
-  c.weight_decay = cfg->weight_decay;
-  c.max_grad_norm = cfg->max_grad_norm;
-  c.inv_loss_scale = cfg->inv_loss_scale;
-  c.inv_bc1 = (float)(1.0 / (1.0 - pow((double)cfg->beta1, (double)cfg->step)));
-  c.inv_bc2 = (float)(1.0 / (1.0 - pow((double)cfg->beta2, (double)cfg->step)));
+  const int s = adam_args(cfg, n, master, m, v, grad, w_bf16, stats, ws, ws_bytes, &c);
+  if (s != MTNLG_OK) return s;
   MTNLG_HIP(adam_step(c, n, master, m, v, grad, w_bf16, stats, ws, static_cast<hipStream_t>(stream)), "adam_step");
+  return MTNLG_OK;
+}
+
+int mtnlg_grad_accumulate_norm(int64_t n, int32_t dtype, const void* grad, float* acc, int32_t overwrite,
+                               float inv_loss_scale, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
+  if (n < 0) return fail(MTNLG_ERR_SHAPE, "n < 0");
+  if (!isfinite(inv_loss_scale)) return fail(MTNLG_ERR_ARG, "inv_loss_scale must be finite");
+  if (n > 0) {
+    CHECK_PTR(grad);
+    CHECK_PTR(acc);
+  }
+  CHECK_PTR(ws);
+  if (ws_bytes < adam_ws(n)) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, adam_ws(n));
+  MTNLG_HIP(grad_accumulate_norm(n, dtype, grad, acc, overwrite != 0, inv_loss_scale, ws,
+                                 static_cast<hipStream_t>(stream)),
+            "grad_accumulate_norm");
+  return MTNLG_OK;
+}
+
+int mtnlg_adam_update(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
+                      void* w_bf16, float* stats, const void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  AdamScalars c{};
+  const int s = adam_args(cfg, n, master, m, v, grad, w_bf16, stats, ws, ws_bytes, &c);
+  if (s != MTNLG_OK) return s;
+  MTNLG_HIP(adam_update(c, n, master, m, v, grad, w_bf16, stats, ws, static_cast<hipStream_t>(stream)),
+            "adam_update");
   return MTNLG_OK;
 }
 

@@ -80,6 +80,14 @@ hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim,
 constexpr int kMaxPartials = 16;
 hipError_t reduce_partials(int dtype, int64_t rows, int64_t cols, const void* const* parts, int n,
                            const void* residual, const void* bias, void* out, hipStream_t st);
+// reduce_partials with dropout on (sum + bias) before the residual is added,
+// and the matching backward dz = keep * scale * dy. The keep mask comes from
+// Philox4x64-10 keyed by (seed, site); thr = drop threshold on 16-bit draws.
+hipError_t reduce_partials_dropout(int dtype, int64_t rows, int64_t cols, const void* const* parts, int n,
+                                   const void* residual, const void* bias, void* out, uint64_t seed,
+                                   uint64_t site, uint32_t thr, hipStream_t st);
+hipError_t dropout_bwd(int dtype, int64_t total, const void* dy, void* dz, uint64_t seed, uint64_t site,
+                       uint32_t thr, hipStream_t st);
 size_t colsum_ws(int64_t rows, int64_t cols);
 // out[c] = sum_r x[r, c] (x dtype, out dtype), two-stage deterministic.
 hipError_t colsum(int dtype, int64_t rows, int64_t cols, const void* x, void* out, void* ws,
@@ -93,5 +101,11 @@ struct AdamScalars {
 };
 hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v,
                      const float* grad, void* w_bf16, float* stats, void* ws, hipStream_t st);
+// The accumulation that also leaves the norm partials in ws (adam_ws bytes),
+// and the Adam step that takes them from there instead of its own norm pass.
+hipError_t grad_accumulate_norm(int64_t n, int dtype, const void* grad, float* acc, bool overwrite,
+                                float inv_loss_scale, void* ws, hipStream_t st);
+hipError_t adam_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v,
+                       const float* grad, void* w_bf16, float* stats, const void* ws, hipStream_t st);
 
 }  // namespace mtnlg

@@ -1,0 +1,223 @@
+// One pipeline stage of chained layer slices on one GPU (include/mtnlg.h,
+// "One pipeline stage on one GPU"): the host-side schedule that runs the
+// micro-batches through the layer-half entry points, accumulates the flat
+// gradient, and takes the Adam step on the norm folded into the last
+// accumulation.
+//
+// In MT-NLG 530B the 105 layers are split over 35 pipeline stages with 8-way
+// tensor slicing inside each (jiqizhixin MT-NLG article, system paragraph), so
+// one GPU holds 3 layer slices, and gradients of several micro-batches are
+// accumulated before each step (Elamur summary, Key points). Each micro-batch
+// runs forward then backward before the next starts: with no neighbouring
+// stage this is the order a one-forward-one-backward schedule gives, and it
+// keeps the saved activations of a single micro-batch alive at a time.
+#include <string.h>
+
+#include <algorithm>
+
+#include "abi_common.hpp"
+
+using namespace mtnlg;
+using namespace mtnlg::abi;
+
+namespace {
+
+constexpr int kTensors = 6;  // ln_g, ln_b, w_in, b_in, w_out, b_out
+
+struct StageDims {
+  int64_t T, h, act;          // rows, hidden, elements of one [T, h] activation
+  int64_t win[2], wout[2];    // columns of w_in and rows of w_out per half
+  int64_t per_layer;          // parameter elements of one layer
+};
+
+int stage_dims(const mtnlg_stage_desc* sd, StageDims* o) {
+  if (!sd) return fail(MTNLG_ERR_ARG, "stage desc is NULL");
+  if (sd->layers < 1 || sd->micro_batches < 1) return fail(MTNLG_ERR_SHAPE, "layers and micro_batches must be >= 1");
+  if (sd->recompute != 0 && sd->recompute != 1) return fail(MTNLG_ERR_ARG, "recompute must be 0 or 1");
+  const mtnlg_layer_desc& L = sd->layer;
+  if (L.dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "a stage runs bf16 layers (mixed precision)");
+  if (mtnlg_saved_bytes(&L, MTNLG_ATTN) == 0 || mtnlg_saved_bytes(&L, MTNLG_MLP) == 0)
+    return fail(MTNLG_ERR_SHAPE, "invalid layer descriptor");
+  o->T = (int64_t)L.batch * L.seq;
+  o->h = L.hidden;
+  o->wout[MTNLG_ATTN] = (int64_t)(L.heads / L.tp_size) * (L.hidden / L.heads);  // local heads * head_dim
+  o->win[MTNLG_ATTN] = 3 * o->wout[MTNLG_ATTN];                                   // q, k and v
+  o->win[MTNLG_MLP] = o->wout[MTNLG_MLP] = (int64_t)L.ffn / L.tp_size;
+  o->act = o->T * o->h;
+  o->per_layer = 0;
+  for (int half = 0; half < 2; ++half)
+    o->per_layer += 2 * o->h + o->h * o->win[half] + o->win[half] + o->wout[half] * o->h + o->h;
+  return MTNLG_OK;
+}
+
+void layer_offsets(const StageDims& d, int layer, int64_t off[2][kTensors]) {
+  int64_t p = (int64_t)layer * d.per_layer;
+  for (int half = 0; half < 2; ++half) {
+    const int64_t sizes[kTensors] = {d.h, d.h, d.h * d.win[half], d.win[half], d.wout[half] * d.h, d.h};
+    for (int t = 0; t < kTensors; ++t) {
+      off[half][t] = p;
+      p += sizes[t];
+    }
+  }
+}
+
+// Workspace regions, each on a 256-byte boundary.
+struct StageWs {
+  size_t adam, xin, mid, part, g1, g2, saved, layer, total;
+  size_t saved_a, saved_m;  // bytes of one layer's saved tensors per half
+};
+
+StageWs stage_ws(const mtnlg_stage_desc* sd, const StageDims& d, int64_t n) {
+  const mtnlg_layer_desc* L = &sd->layer;
+  const size_t act = align256((size_t)d.act * 2);
+  StageWs w{};
+  w.saved_a = align256(mtnlg_saved_bytes(L, MTNLG_ATTN));
+  w.saved_m = align256(mtnlg_saved_bytes(L, MTNLG_MLP));
+  size_t p = 0;
+  w.adam = p;
+  p += align256(mtnlg_adam_workspace_bytes(n));
+  w.xin = p;  // inputs of layers 1 .. layers-1 (layer 0 reads the caller's x)
+  p += act * (size_t)(sd->layers - 1);
+  w.mid = p;  // each layer's MLP-half input X1
+  p += act * (size_t)sd->layers;
+  w.part = p;  // one slice partial (forward) or input-gradient partial (backward)
+  p += act;
+  w.g1 = p;
+  p += act;
+  w.g2 = p;
+  p += act;
+  w.saved = p;  // every layer's saved tensors, or one scratch set when recomputing
+  p += sd->recompute ? std::max(w.saved_a, w.saved_m) : (w.saved_a + w.saved_m) * (size_t)sd->layers;
+  w.layer = p;
+  const size_t lw = sd->recompute
+                        ? std::max(mtnlg_recompute_workspace_bytes(L, MTNLG_ATTN),
+                                   mtnlg_recompute_workspace_bytes(L, MTNLG_MLP))
+                        : std::max(mtnlg_workspace_bytes(L, MTNLG_ATTN), mtnlg_workspace_bytes(L, MTNLG_MLP));
+  p += align256(lw);
+  w.total = p;
+  return w;
+}
+
+#define STAGE_CALL(call)          \
+  do {                            \
+    const int s_ = (call);        \
+    if (s_ != MTNLG_OK) return s_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int64_t mtnlg_stage_param_count(const mtnlg_stage_desc* desc) {
+  StageDims d;
+  if (stage_dims(desc, &d) != MTNLG_OK) return -1;
+  return d.per_layer * desc->layers;
+}
+
+int mtnlg_stage_param_offsets(const mtnlg_stage_desc* desc, int64_t* off) {
+  g_last_error[0] = 0;
+  StageDims d;
+  STAGE_CALL(stage_dims(desc, &d));
+  if (!off) return fail(MTNLG_ERR_ARG, "off is NULL");
+  for (int l = 0; l < desc->layers; ++l) {
+    int64_t o[2][kTensors];
+    layer_offsets(d, l, o);
+    memcpy(off + (size_t)l * 2 * kTensors, o, sizeof(o));
+  }
+  return MTNLG_OK;
+}
+
+size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc) {
+  StageDims d;
+  if (stage_dims(desc, &d) != MTNLG_OK) return 0;
+  return stage_ws(desc, d, d.per_layer * desc->layers).total;
+}
+
+int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, void* w, float* master, float* m,
+                     float* v, void* grad, float* acc, const void* x, const void* dy, void* y, void* dx,
+                     float* stats, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  StageDims d;
+  STAGE_CALL(stage_dims(desc, &d));
+  const int64_t n = d.per_layer * desc->layers;
+  // everything is checked before the first launch
+  AdamScalars unused;
+  STAGE_CALL(adam_args(cfg, n, master, m, v, acc, w, stats, ws, ws_bytes, &unused));
+  CHECK_PTR(grad);
+  CHECK_PTR(x);
+  CHECK_PTR(dy);
+  CHECK_PTR(y);
+  CHECK_PTR(dx);
+  const StageWs W = stage_ws(desc, d, n);
+  if (ws_bytes < W.total) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, W.total);
+
+  const mtnlg_layer_desc* L = &desc->layer;
+  const size_t act = (size_t)d.act * 2;
+  const size_t act_al = align256(act);
+  char* base = static_cast<char*>(ws);
+  char* part = base + W.part;
+  char* g1 = base + W.g1;
+  char* g2 = base + W.g2;
+  char* lws = base + W.layer;
+  const size_t lws_bytes = ws_bytes - W.layer;
+  char* wb = static_cast<char*>(w);
+  char* gb = static_cast<char*>(grad);
+  auto xin = [&](int l, int k) -> const void* {
+    return l == 0 ? static_cast<const char*>(x) + (size_t)k * act : base + W.xin + (size_t)(l - 1) * act_al;
+  };
+  auto xout = [&](int l, int k) -> void* {
+    return l == desc->layers - 1 ? static_cast<char*>(y) + (size_t)k * act : base + W.xin + (size_t)l * act_al;
+  };
+  auto mid = [&](int l) -> void* { return base + W.mid + (size_t)l * act_al; };
+  auto saved = [&](int l, int half) -> void* {
+    if (desc->recompute) return base + W.saved;
+    return base + W.saved + (size_t)l * (W.saved_a + W.saved_m) + (half == MTNLG_MLP ? W.saved_a : 0);
+  };
+
+  for (int k = 0; k < desc->micro_batches; ++k) {
+    for (int l = 0; l < desc->layers; ++l) {
+      int64_t o[2][kTensors];
+      layer_offsets(d, l, o);
+      const void* in[2] = {xin(l, k), mid(l)};
+      void* out[2] = {mid(l), xout(l, k)};
+      for (int half = 0; half < 2; ++half) {
+        const int64_t* t = o[half];
+        const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
+        STAGE_CALL(mtnlg_layer_fwd(L, half, &p, in[half], part, saved(l, half), lws, lws_bytes, stream));
+        const void* parts[1] = {part};
+        STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, in[half], wb + 2 * t[5], out[half], stream));
+      }
+    }
+    const void* gcur = static_cast<const char*>(dy) + (size_t)k * act;
+    for (int l = desc->layers - 1; l >= 0; --l) {
+      int64_t o[2][kTensors];
+      layer_offsets(d, l, o);
+      const void* in[2] = {xin(l, k), mid(l)};
+      for (int half = 1; half >= 0; --half) {
+        const int64_t* t = o[half];
+        const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
+        const mtnlg_half_grads g = {gb + 2 * t[0], gb + 2 * t[1], gb + 2 * t[2],
+                                    gb + 2 * t[3], gb + 2 * t[4], gb + 2 * t[5]};
+        if (desc->recompute)
+          STAGE_CALL(mtnlg_layer_bwd_recompute(L, half, &p, in[half], gcur, part, &g, lws, lws_bytes, stream));
+        else
+          STAGE_CALL(mtnlg_layer_bwd(L, half, &p, in[half], saved(l, half), gcur, part, &g, lws, lws_bytes,
+                                     stream));
+        // dx of the half = dy (residual path) + the slice's partial
+        void* dst = half == MTNLG_MLP ? g1 : (l == 0 ? static_cast<char*>(dx) + (size_t)k * act : g2);
+        const void* parts[1] = {part};
+        STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, gcur, nullptr, dst, stream));
+        gcur = dst;
+      }
+    }
+    const bool first = k == 0;
+    if (k + 1 < desc->micro_batches)
+      STAGE_CALL(mtnlg_grad_accumulate(n, MTNLG_BF16, grad, acc, first, stream));
+    else
+      STAGE_CALL(mtnlg_grad_accumulate_norm(n, MTNLG_BF16, grad, acc, first, cfg->inv_loss_scale, base + W.adam,
+                                            W.xin - W.adam, stream));
+  }
+  return mtnlg_adam_update(cfg, n, master, m, v, acc, w, stats, base + W.adam, W.xin - W.adam, stream);
+}
+
+}  // extern "C"

@@ -1,5 +1,6 @@
-// HBM-streaming kernels (gfx950): the local sum of slice partials, fp32
-// gradient accumulation, and the fused mixed-precision Adam step.
+// HBM-streaming kernels (gfx950): the local sum of slice partials (with an
+// optional dropout), fp32 gradient accumulation, and the fused mixed-precision
+// Adam step.
 //
 // * Partial sum (operator g's forward / f's backward of the tensor-slicing
 //   example in the STRONGHOLD slides, done on one device):
@@ -11,7 +12,9 @@
 //   gradient in fp64 plus a non-finite flag, (2) a one-workgroup finish in
 //   fixed order that writes {norm, clip coef, found_inf} to device memory,
 //   (3) the update, which reads those scalars itself and leaves every buffer
-//   untouched when found_inf is set -- the host never waits.
+//   untouched when found_inf is set -- the host never waits. Step (1) can
+//   instead ride along the last micro-batch's accumulation (grad_accumulate_norm,
+//   then adam_update runs (2) and (3)).
 // Grid-stride loops over 16-byte vectors; all pointers are 16-byte aligned
 // (checked on the host) and the ragged tail is done per element.
 #include "common.hpp"
@@ -78,12 +81,126 @@ __global__ __launch_bounds__(kStreamThreads) void reduce_partials_kernel(Partial
   }
 }
 
+// ---- dropout on the sum of the partials (counter-based mask) ----
+//
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC 2011): ten rounds, each multiplying two of the four
+// 64-bit words by a round constant into 128-bit products and mixing the
+// halves with the other words and the key; the key advances by two Weyl
+// increments between rounds. One call yields 256 bits, sixteen 16-bit draws:
+// element e of a row-major tensor uses block e / 16 (counter (e/16, 0, 0, 0),
+// key (seed, site)) and the draw at bits 16 * (e % 4) of word (e % 16) / 4.
+// It is kept when draw >= thr; kept values are multiplied by scale.
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64(uint64_t c0, uint64_t k0, uint64_t k1, uint64_t w[4]) {
+  uint64_t x0 = c0, x1 = 0, x2 = 0, x3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, x0), lo0 = kPhiloxM0 * x0;
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, x2), lo1 = kPhiloxM1 * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  w[0] = x0;
+  w[1] = x1;
+  w[2] = x2;
+  w[3] = x3;
+}
+
+struct DropoutArgs {
+  uint64_t seed, site;
+  uint32_t thr;  // drop when the 16-bit draw is below thr
+  float scale;   // 65536 / (65536 - thr)
+};
+
+// keep bit j (0..15) of a 16-element group as a 16-bit mask
+__device__ __forceinline__ uint32_t keep_bits(uint64_t group, const DropoutArgs& d) {
+  uint64_t w[4];
+  philox4x64(group, d.seed, d.site, w);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) bits |= (uint32_t)(((w[j >> 2] >> (16 * (j & 3))) & 0xFFFFu) >= d.thr) << j;
+  return bits;
+}
+
+// out = residual + keep * scale * (sum of partials + bias), 16 elements (one
+// generator block) per thread and iteration; total is a multiple of 8.
 template <typename T>
+__global__ __launch_bounds__(kStreamThreads) void reduce_dropout_kernel(PartialPtrs parts, int n, int64_t total,
+                                                                        int64_t cols, const T* __restrict__ residual,
+                                                                        const T* __restrict__ bias,
+                                                                        T* __restrict__ out, DropoutArgs d) {
+  const int64_t groups = (total + 15) / 16;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t keep = keep_bits((uint64_t)g, d);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int64_t i = g * 16 + hf * 8;
+      if (i >= total) break;
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int j = 0; j < n; ++j) {
+        float v[8];
+        load8(static_cast<const T*>(parts.p[j]) + i, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] += v[e];
+      }
+      if (bias) {
+        float b[8];
+        load8(bias + (i % cols), b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] += b[e];
+      }
+      float r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (residual) load8(residual + i, r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] += ((keep >> (hf * 8 + e)) & 1u) ? z[e] * d.scale : 0.0f;
+      store8(out + i, r);
+    }
+  }
+}
+
+// dz = keep * scale * dy (the same mask, regenerated)
+template <typename T>
+__global__ __launch_bounds__(kStreamThreads) void dropout_bwd_kernel(int64_t total, const T* __restrict__ dy,
+                                                                     T* __restrict__ dz, DropoutArgs d) {
+  const int64_t groups = (total + 15) / 16;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t keep = keep_bits((uint64_t)g, d);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int64_t i = g * 16 + hf * 8;
+      if (i >= total) break;
+      float v[8];
+      load8(dy + i, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = ((keep >> (hf * 8 + e)) & 1u) ? v[e] * d.scale : 0.0f;
+      store8(dz + i, v);
+    }
+  }
+}
+
+// acc = (overwrite ? 0 : acc) + grad. With NORM the same pass also leaves, per
+// workgroup, the fp64 sum of (acc * s)^2 over the elements it wrote and a
+// non-finite flag: the norm pass of the optimizer folded into the last
+// micro-batch's accumulation, one fewer read of the accumulator.
+template <typename T, bool NORM>
 __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, const T* __restrict__ g,
-                                                                  float* __restrict__ acc, int overwrite) {
+                                                                  float* __restrict__ acc, int overwrite, float s,
+                                                                  double* __restrict__ part,
+                                                                  int* __restrict__ flag) {
   const int64_t units = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 2;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x;
+  double sq = 0.0;
+  int bad = 0;
   for (int64_t u0 = t0; u0 < units; u0 += stride) {
     float v[2][8], a[2][8];
 #pragma unroll
@@ -103,13 +220,36 @@ __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, con
           for (int e = 0; e < 8; ++e) v[k][e] += a[k][e];
         }
         store8(acc + u * 8, v[k]);
+        if (NORM) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float t = v[k][e] * s;
+            bad |= !isfinite(t);
+            sq += (double)t * t;
+          }
+        }
       }
     }
   }
   const int64_t s1 = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = units * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += s1) {
     const float v = Elem<T>::to_f(g[i]);
-    acc[i] = overwrite ? v : acc[i] + v;
+    const float r = overwrite ? v : acc[i] + v;
+    acc[i] = r;
+    if (NORM) {
+      const float t = r * s;
+      bad |= !isfinite(t);
+      sq += (double)t * t;
+    }
+  }
+  if (NORM) {
+    __shared__ double red[kStreamThreads / kWave];
+    const double tot = block_sum<kStreamThreads>(sq, red);
+    const double nbad = block_sum<kStreamThreads>((double)bad, red);
+    if (threadIdx.x == 0) {
+      part[blockIdx.x] = tot;
+      flag[blockIdx.x] = nbad > 0.0;
+    }
   }
 }
 
@@ -265,37 +405,116 @@ hipError_t reduce_partials(int dtype, int64_t rows, int64_t cols, const void* co
   return hipGetLastError();
 }
 
-hipError_t grad_accumulate(int64_t n, int dtype, const void* grad, float* acc, bool overwrite, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  const int grid = stream_grid(n / 16 + 1, kOptBlocks);
+namespace {
+DropoutArgs dropout_args(uint64_t seed, uint64_t site, uint32_t thr) {
+  DropoutArgs d;
+  d.seed = seed;
+  d.site = site;
+  d.thr = thr;
+  d.scale = (float)(65536.0 / (65536.0 - (double)thr));
+  return d;
+}
+}  // namespace
+
+hipError_t reduce_partials_dropout(int dtype, int64_t rows, int64_t cols, const void* const* parts, int n,
+                                   const void* residual, const void* bias, void* out, uint64_t seed,
+                                   uint64_t site, uint32_t thr, hipStream_t st) {
+  const int64_t total = rows * cols;
+  if (total == 0) return hipSuccess;
+  PartialPtrs pp{};
+  for (int j = 0; j < n; ++j) pp.p[j] = parts[j];
+  const DropoutArgs d = dropout_args(seed, site, thr);
+  const int grid = stream_grid((total + 15) / 16);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(grad_acc_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, n,
-                       static_cast<const bf16_t*>(grad), acc, (int)overwrite);
+    hipLaunchKernelGGL(reduce_dropout_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, pp, n, total, cols,
+                       static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(bias),
+                       static_cast<bf16_t*>(out), d);
   else
-    hipLaunchKernelGGL(grad_acc_kernel<float>, dim3(grid), dim3(kStreamThreads), 0, st, n,
-                       static_cast<const float*>(grad), acc, (int)overwrite);
+    hipLaunchKernelGGL(reduce_dropout_kernel<float>, dim3(grid), dim3(kStreamThreads), 0, st, pp, n, total, cols,
+                       static_cast<const float*>(residual), static_cast<const float*>(bias),
+                       static_cast<float*>(out), d);
   return hipGetLastError();
 }
 
-size_t adam_ws(int64_t) { return (size_t)kNormBlocks * (sizeof(double) + sizeof(int)); }
+hipError_t dropout_bwd(int dtype, int64_t total, const void* dy, void* dz, uint64_t seed, uint64_t site,
+                       uint32_t thr, hipStream_t st) {
+  if (total == 0) return hipSuccess;
+  const DropoutArgs d = dropout_args(seed, site, thr);
+  const int grid = stream_grid((total + 15) / 16);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(dropout_bwd_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, total,
+                       static_cast<const bf16_t*>(dy), static_cast<bf16_t*>(dz), d);
+  else
+    hipLaunchKernelGGL(dropout_bwd_kernel<float>, dim3(grid), dim3(kStreamThreads), 0, st, total,
+                       static_cast<const float*>(dy), static_cast<float*>(dz), d);
+  return hipGetLastError();
+}
 
-hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
-                     void* w_bf16, float* stats, void* ws, hipStream_t st) {
+int acc_grid(int64_t n) { return stream_grid(n / 16 + 1, kOptBlocks); }
+
+hipError_t grad_accumulate(int64_t n, int dtype, const void* grad, float* acc, bool overwrite, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int grid = acc_grid(n);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((grad_acc_kernel<bf16_t, false>), dim3(grid), dim3(kStreamThreads), 0, st, n,
+                       static_cast<const bf16_t*>(grad), acc, (int)overwrite, 1.0f, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((grad_acc_kernel<float, false>), dim3(grid), dim3(kStreamThreads), 0, st, n,
+                       static_cast<const float*>(grad), acc, (int)overwrite, 1.0f, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// Workspace: per-workgroup fp64 partial sums and int flags, sized for the
+// larger of the two grids that fill it (the norm pass, the accumulation).
+size_t adam_ws(int64_t) { return (size_t)kOptBlocks * (sizeof(double) + sizeof(int)); }
+
+hipError_t grad_accumulate_norm(int64_t n, int dtype, const void* grad, float* acc, bool overwrite,
+                                float inv_loss_scale, void* ws, hipStream_t st) {
   double* part = static_cast<double*>(ws);
-  int* flag = reinterpret_cast<int*>(part + kNormBlocks);
-  const int nb = n == 0 ? 1 : std::min<int>(kNormBlocks, stream_grid(n / 8 + 1, kNormBlocks));
-  hipLaunchKernelGGL(adam_norm_kernel, dim3(nb), dim3(kStreamThreads), 0, st, n, grad, c.inv_loss_scale, part,
-                     flag);
+  int* flag = reinterpret_cast<int*>(part + kOptBlocks);
+  const int grid = acc_grid(n);  // n == 0 still writes the one (zero) partial
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((grad_acc_kernel<bf16_t, true>), dim3(grid), dim3(kStreamThreads), 0, st, n,
+                       static_cast<const bf16_t*>(grad), acc, (int)overwrite, inv_loss_scale, part, flag);
+  else
+    hipLaunchKernelGGL((grad_acc_kernel<float, true>), dim3(grid), dim3(kStreamThreads), 0, st, n,
+                       static_cast<const float*>(grad), acc, (int)overwrite, inv_loss_scale, part, flag);
+  return hipGetLastError();
+}
+
+namespace {
+// (2) + (3): the finish over nparts partials, then the update
+hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                             void* w_bf16, float* stats, const double* part, const int* flag, int nparts,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(adam_finish_kernel, dim3(1), dim3(kStreamThreads), 0, st, part, flag, nparts,
+                     c.max_grad_norm, stats);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(adam_finish_kernel, dim3(1), dim3(kStreamThreads), 0, st, part, flag, nb, c.max_grad_norm,
-                     stats);
-  e = hipGetLastError();
   if (e != hipSuccess || n == 0) return e;
   const int grid = stream_grid(n / 8 + 1, kOptBlocks);
   hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
                      static_cast<bf16_t*>(w_bf16), stats);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                     void* w_bf16, float* stats, void* ws, hipStream_t st) {
+  double* part = static_cast<double*>(ws);
+  int* flag = reinterpret_cast<int*>(part + kOptBlocks);
+  const int nb = n == 0 ? 1 : std::min<int>(kNormBlocks, stream_grid(n / 8 + 1, kNormBlocks));
+  hipLaunchKernelGGL(adam_norm_kernel, dim3(nb), dim3(kStreamThreads), 0, st, n, grad, c.inv_loss_scale, part,
+                     flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return finish_and_update(c, n, master, m, v, grad, w_bf16, stats, part, flag, nb, st);
+}
+
+hipError_t adam_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                       void* w_bf16, float* stats, const void* ws, hipStream_t st) {
+  const double* part = static_cast<const double*>(ws);
+  const int* flag = reinterpret_cast<const int*>(part + kOptBlocks);
+  return finish_and_update(c, n, master, m, v, grad, w_bf16, stats, part, flag, acc_grid(n), st);
 }
 
 }  // namespace mtnlg

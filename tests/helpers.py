@@ -48,3 +48,17 @@ def empty(shape, dtype: str):
 def empty_bytes(n):
     import torch
     return torch.empty(max(int(n), 16), dtype=torch.uint8, device="cuda")
+
+
+def assert_bf16_copy(w_gpu, master_gpu, rw, rp):
+    """The bf16 weight copy is the GPU's fp32 master rounded to nearest even, bit
+    for bit; against the oracle's copy rw (of its fp64 master rp) it may differ by
+    one bf16 ulp plus the GPU master's own deviation, which dominates where an
+    update nearly cancels a weight (fp32 keeps the absolute error of the old
+    value, far above the new value's bf16 ulp)."""
+    from synth.inputs import round_f32_to_bf16
+    w_gpu = np.asarray(w_gpu, dtype=np.float64)
+    master_gpu = np.asarray(master_gpu, dtype=np.float64)
+    assert np.array_equal(w_gpu, round_f32_to_bf16(master_gpu.astype(np.float32)).astype(np.float64))
+    allow = np.abs(rw) * 2.0 ** -7 + 2.0 * np.abs(master_gpu - rp) + 1e-38
+    assert np.all(np.abs(w_gpu - rw) <= allow)

@@ -124,6 +124,26 @@ def test_small_workspace_rejected():
     assert st == -1
 
 
+def test_recompute_workspace_and_validation():
+    """The recompute backward's workspace is the saved tensors (256-aligned) plus the
+    ordinary backward workspace; it validates like mtnlg_layer_bwd."""
+    L = lib()
+    d = desc()
+    p = _lib.HalfParams(A, A, A, A, A)
+    g = _lib.HalfGrads(A, A, A, A, A, A)
+    for half in (_lib.ATTN, _lib.MLP):
+        need = L.mtnlg_recompute_workspace_bytes(ctypes.byref(d), half)
+        assert need == align256(L.mtnlg_saved_bytes(ctypes.byref(d), half)) + \
+            L.mtnlg_workspace_bytes(ctypes.byref(d), half)
+        st = L.mtnlg_layer_bwd_recompute(ctypes.byref(d), half, ctypes.byref(p), A, A, A, ctypes.byref(g), A,
+                                         need - 1, None)
+        assert st == -5
+        st = L.mtnlg_layer_bwd_recompute(ctypes.byref(d), half, ctypes.byref(p), None, A, A, ctypes.byref(g), A,
+                                         need, None)
+        assert st == -1
+    assert L.mtnlg_recompute_workspace_bytes(ctypes.byref(desc(seq=100)), _lib.ATTN) == 0
+
+
 def test_other_entry_points_validate():
     L = lib()
     arr = (ctypes.c_void_p * 2)(A, A)
@@ -140,6 +160,11 @@ def test_other_entry_points_validate():
     assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 1 << 20, None) == -1   # beta1
     cfg = _lib.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 1)
     assert L.mtnlg_adam_step(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 8, None) == -5
+    assert L.mtnlg_adam_update(ctypes.byref(cfg), 16, A, A, A, A, None, A, A, 8, None) == -5
+    assert L.mtnlg_grad_accumulate_norm(16, _lib.BF16, A, A, 1, 1.0, A, 8, None) == -5
+    assert L.mtnlg_grad_accumulate_norm(16, _lib.BF16, A, A, 1, float("inf"), A, 1 << 20, None) == -1
+    assert L.mtnlg_grad_accumulate_norm(16, _lib.BF16, None, A, 1, 1.0, A, 1 << 20, None) == -1
+    assert L.mtnlg_grad_accumulate_norm(16, 7, A, A, 1, 1.0, A, 1 << 20, None) == -3
     assert L.mtnlg_gemm(_lib.BF16, 0, 0, 12, 16, 16, A, A, A, None, None, 0, None) == -2
     assert L.mtnlg_gemm(_lib.BF16, 0, 0, 16, 16, 16, None, A, A, None, None, 0, None) == -1
     # 2048 x 10240 tiles: the leftover round is split along K, so a workspace is required
@@ -151,3 +176,60 @@ def test_other_entry_points_validate():
     assert L.mtnlg_attention_fwd(_lib.F32, 1, 128, 2, 160, A, A, A, None) == -2               # f32 hd 160
     assert L.mtnlg_attention_fwd(_lib.BF16, 1, 96, 2, 128, A, A, A, None) == -2
     assert L.mtnlg_attention_bwd(_lib.BF16, 1, 128, 2, 128, A, A, A, A, A, A, 0, None) == -5
+
+
+def _stage(layers=3, mb=4, recompute=0, **kw):
+    return _lib.StageDesc(desc(**kw), layers, mb, recompute)
+
+
+def test_stage_layout_follows_header():
+    """Flat layout: per layer ATTN then MLP, each ln_g | ln_b | w_in | b_in | w_out | b_out."""
+    L = lib()
+    sd = _stage()
+    h, wl, fl = 20480, 16 * 160, 10240
+    sizes = {0: [h, h, h * 3 * wl, 3 * wl, wl * h, h], 1: [h, h, h * fl, fl, fl * h, h]}
+    per_layer = sum(sizes[0]) + sum(sizes[1])
+    assert L.mtnlg_stage_param_count(ctypes.byref(sd)) == 3 * per_layer
+    assert 3 * (20480 * 7680 + 2560 * 20480 + 2 * 20480 * 10240) == 1_887_436_800   # GEMM weights alone
+    off = (ctypes.c_int64 * 36)()
+    assert L.mtnlg_stage_param_offsets(ctypes.byref(sd), off) == 0
+    pos = 0
+    for l in range(3):
+        for half in (0, 1):
+            for t in range(6):
+                assert off[(l * 2 + half) * 6 + t] == pos
+                assert pos % 8 == 0
+                pos += sizes[half][t]
+
+
+def test_stage_workspace_and_validation():
+    L = lib()
+    sd = _stage()
+    n = L.mtnlg_stage_param_count(ctypes.byref(sd))
+    act = align256(2048 * 20480 * 2)
+    sa = align256(L.mtnlg_saved_bytes(ctypes.byref(sd.layer), _lib.ATTN))
+    sm = align256(L.mtnlg_saved_bytes(ctypes.byref(sd.layer), _lib.MLP))
+    lw = max(L.mtnlg_workspace_bytes(ctypes.byref(sd.layer), h) for h in (0, 1))
+    want = align256(L.mtnlg_adam_workspace_bytes(n)) + act * (2 + 3 + 3) + 3 * (sa + sm) + align256(lw)
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(sd)) == want
+    rc = _stage(recompute=1)
+    lw = max(L.mtnlg_recompute_workspace_bytes(ctypes.byref(rc.layer), h) for h in (0, 1))
+    want_rc = align256(L.mtnlg_adam_workspace_bytes(n)) + act * 8 + max(sa, sm) + align256(lw)
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(rc)) == want_rc
+    # invalid descriptors
+    assert L.mtnlg_stage_param_count(ctypes.byref(_stage(dtype=_lib.F32))) == -1
+    assert L.mtnlg_stage_param_count(ctypes.byref(_stage(layers=0))) == -1
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(_stage(recompute=2))) == 0
+    off = (ctypes.c_int64 * 36)()
+    assert L.mtnlg_stage_param_offsets(ctypes.byref(_stage(dtype=_lib.F32)), off) == -3
+    assert L.mtnlg_stage_param_offsets(ctypes.byref(sd), None) == -1
+    cfg = _lib.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 1)
+    big = 1 << 40
+
+    def step(c=cfg, ws_bytes=big, grad=A):
+        return L.mtnlg_stage_step(ctypes.byref(sd), ctypes.byref(c), A, A, A, A, grad, A, A, A, A, A, A, A,
+                                  ws_bytes, None)
+    assert step(ws_bytes=want - 1) == -5
+    assert step(grad=None) == -1
+    assert step(grad=ODD) == -4
+    assert step(c=_lib.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 0)) == -1

@@ -7,8 +7,9 @@ element with the oracle (float64) on the same bf16-exact or fp32 values.
 import numpy as np
 import pytest
 
-from helpers import TOL, assert_close, empty, empty_bytes, rel_inf, to_gpu, to_np
+from helpers import TOL, assert_bf16_copy, assert_close, empty, empty_bytes, rel_inf, to_gpu, to_np
 from oracle import adam as OA
+from oracle import dropout as OD
 from oracle import layer as OL
 from synth.inputs import randn, round_f32_to_bf16
 
@@ -143,6 +144,52 @@ def test_reduce_partials(dtype, n):
     assert_close("out_nores", to_np(out2), ref2, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,p", [(3, 24, 0.1), (67, 264, 0.3), (33, 20480, 0.1), (16, 64, 0.0)])
+def test_reduce_partials_dropout(dtype, rows, cols, p):
+    """Dropout after the partial sum: the mask (Philox4x64-10 on the GPU,
+    independently in the oracle) must match element for element -- dropped
+    elements are exactly the residual -- and the kept values to the dtype's
+    tolerance. 3 x 24 ends in half a generator block."""
+    p = float(np.float32(p))           # the rate as the library receives it
+    seed, site = 0x5EED0000DEADBEEF, 7
+    parts = [inputs(140 + j, (rows, cols), dtype) for j in range(2)]
+    res = inputs(150, (rows, cols), dtype)
+    bias = inputs(151, (cols,), dtype)
+    out = empty((rows, cols), dtype)
+    tst.reduce_partials_dropout([to_gpu(q, dtype) for q in parts], out, p, seed, site, to_gpu(res, dtype),
+                                to_gpu(bias, dtype))
+    torch.cuda.synchronize()
+    got = to_np(out)
+    keep = OD.mask((rows, cols), p, seed, site)
+    ref = OD.dropout_sum_fwd([q.astype(np.float64) for q in parts], res.astype(np.float64), bias.astype(np.float64),
+                             p, seed, site)
+    assert np.array_equal(got[~keep], res.astype(np.float64)[~keep])
+    assert_close("out", got, ref, dtype)
+    if p == 0.0:
+        assert keep.all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols,p", [(3, 24, 0.5), (129, 2056, 0.1)])
+def test_dropout_bwd(dtype, rows, cols, p):
+    p = float(np.float32(p))
+    seed, site = 12345, 3
+    g = inputs(160, (rows, cols), dtype)
+    dz = empty((rows, cols), dtype)
+    tst.dropout_bwd(to_gpu(g, dtype), dz, p, seed, site)
+    torch.cuda.synchronize()
+    got = to_np(dz)
+    keep = OD.mask((rows, cols), p, seed, site)
+    assert np.all(got[~keep] == 0.0)
+    assert_close("dz", got, OD.dropout_bwd(g.astype(np.float64), p, seed, site), dtype)
+    # a different site gives a different mask
+    dz2 = empty((rows, cols), dtype)
+    tst.dropout_bwd(to_gpu(g, dtype), dz2, p, seed, site + 1)
+    torch.cuda.synchronize()
+    assert not np.array_equal(to_np(dz2) == 0.0, got == 0.0)
+
+
 @pytest.mark.parametrize("n", [8, 1000003])
 def test_grad_accumulate(n):
     gs = [round_f32_to_bf16(randn(60 + k, (n,), 1e-3)) for k in range(4)]
@@ -185,9 +232,65 @@ def test_adam_step(n, max_norm):
     assert rel_inf(gp - master, rp - master) < 1e-4
     assert rel_inf(gm, rm) < 1e-5
     assert rel_inf(gv, rv) < 1e-5
-    # bf16 weight copy: within one bf16 ulp of the oracle's rounding
-    ulp = np.abs(rw) * 2.0 ** -7 + 1e-38
-    assert np.all(np.abs(gw - rw) <= ulp)
+    assert_bf16_copy(gw, gp, rw, rp)
+
+
+@pytest.mark.parametrize("n,mb", [(5, 1), (4096, 3), (1000003, 4)])
+def test_accumulate_norm_then_update(n, mb):
+    """The norm folded into the last micro-batch's accumulation, then the update
+    on it: the same accumulator and step as accumulate + adam_step, checked
+    against the oracle like test_adam_step."""
+    master = randn(90, (n,), 0.02)
+    m = randn(91, (n,), 1e-3)
+    v = randn(92, (n,), 1e-3) ** 2
+    gs = [round_f32_to_bf16(randn(93 + k, (n,), 1e-3)) for k in range(mb)]
+    cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, max_grad_norm=2e-4 * np.sqrt(n),
+                        inv_loss_scale=2.0 ** -2, step=7)
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = empty_bytes(tst.adam_workspace_bytes(n))
+    for k, g in enumerate(gs):
+        if k < mb - 1:
+            tst.grad_accumulate(to_gpu(g, "bf16"), acc, overwrite=(k == 0))
+        else:
+            tst.grad_accumulate_norm(to_gpu(g, "bf16"), acc, k == 0, cfg.inv_loss_scale, ws)
+    mg, mm, vv = (torch.from_numpy(a.astype(np.float32)).cuda() for a in (master, m, v))
+    w = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    stats = torch.zeros(3, dtype=torch.float32, device="cuda")
+    c = tst.AdamCfg(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.max_grad_norm,
+                    cfg.inv_loss_scale, cfg.step)
+    tst.adam_update(c, mg, mm, vv, acc, w, stats, ws)
+    torch.cuda.synchronize()
+    a = to_np(acc)
+    assert rel_inf(a, OA.accumulate([g.astype(np.float64) for g in gs])) < 1e-6
+    rp, rm, rv, rw, (norm, coef, inf) = OA.adam_step(master.astype(np.float64), m.astype(np.float64),
+                                                    v.astype(np.float64), a, cfg)
+    st = to_np(stats)
+    assert not inf and st[2] == 0.0
+    assert abs(st[0] - norm) <= 1e-6 * norm
+    assert abs(st[1] - coef) <= 1e-6
+    assert rel_inf(to_np(mg) - master, rp - master) < 1e-4
+    assert rel_inf(to_np(mm), rm) < 1e-5
+    assert rel_inf(to_np(vv), rv) < 1e-5
+    assert_bf16_copy(to_np(w), to_np(mg), rw, rp)
+
+
+def test_accumulate_norm_nonfinite_skips():
+    n = 4099
+    master = randn(95, (n,), 0.02)
+    g = round_f32_to_bf16(randn(96, (n,), 1e-3))
+    g[17] = np.inf
+    acc = torch.zeros(n, dtype=torch.float32, device="cuda")
+    ws = empty_bytes(tst.adam_workspace_bytes(n))
+    tst.grad_accumulate_norm(to_gpu(g, "bf16"), acc, False, 1.0, ws)
+    mg = torch.from_numpy(master).cuda()
+    mm = torch.zeros(n, device="cuda")
+    vv = torch.zeros(n, device="cuda")
+    stats = torch.zeros(3, device="cuda")
+    tst.adam_update(tst.AdamCfg(1e-3, 0.9, 0.95, 1e-8, 1.0, 1.0, 1.0, 1), mg, mm, vv, acc, None, stats, ws)
+    torch.cuda.synchronize()
+    assert to_np(stats)[2] == 1.0
+    assert np.array_equal(to_np(mg), master.astype(np.float64))
+    assert not to_np(mm).any() and not to_np(vv).any()
 
 
 @pytest.mark.parametrize("bad", [float("nan"), float("inf")])

@@ -6,7 +6,9 @@
 * GPT-style layer h 4096, t = 1, bf16: each half forward + backward in full;
 * MT-NLG 1/8 shard h 20480, 16 heads x 160, bf16: each half forward + backward
   in full (the oracle runs the same slice in float64);
-* run-to-run determinism of a backward.
+* run-to-run determinism of a backward;
+* the backward that recomputes the forward is bit-identical to the stored one;
+* the tiny layer with dropout on both halves (Philox masks) against the oracle.
 Tolerance: ||gpu - oracle||_inf / ||oracle||_inf per tensor (1e-4 fp32, 2e-2 bf16).
 """
 import numpy as np
@@ -14,6 +16,7 @@ import pytest
 
 from helpers import TOL, assert_close, empty, empty_bytes, rel_inf, rel_l2, to_gpu, to_np
 from oracle import adam as OA
+from oracle import dropout as OD
 from oracle import layer as OL
 from synth.inputs import WORKLOADS, make_activation, make_half_params
 
@@ -198,3 +201,86 @@ def test_backward_is_deterministic():
     assert torch.equal(dx1, dx2)
     for k in g1:
         assert torch.equal(g1[k], gh.g[k]), k
+
+
+@pytest.mark.parametrize("wi,half", [(1, "attn"), (1, "mlp"), (3, "attn"), (3, "mlp")])
+def test_recompute_backward_matches_stored(wi, half):
+    """The backward that re-runs the forward from the layer input alone gives
+    bit-identical input and parameter gradients to forward + backward with the
+    stored activations (the same kernels run on the same values)."""
+    w = WORKLOADS[wi]
+    print(f"recompute {w.name} {half}", flush=True)
+    pn = make_half_params(w, half, 0)
+    x = to_gpu(make_activation(w, 1), w.dtype)
+    g = to_gpu(make_activation(w, 2), w.dtype)
+    gh = GpuHalf(w, half, pn)
+    gh.fwd(x)
+    dx_ref = gh.bwd(x, g).clone()
+    g_ref = {k: v.clone() for k, v in gh.g.items()}
+    ws = empty_bytes(tst.recompute_workspace_bytes(gh.desc, HALF[half]))
+    dx = empty((w.tokens, w.hidden), w.dtype)
+    for k in gh.g:
+        gh.g[k].fill_(float("nan"))
+    tst.layer_bwd_recompute(gh.desc, HALF[half], gh.p, x, g, dx, gh.g, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_ref)
+    for k in g_ref:
+        assert torch.equal(gh.g[k], g_ref[k]), k
+
+
+def test_tiny_layer_two_slices_with_dropout():
+    """The t = 2 fp32 layer with dropout (p = 0.2) on both halves' outputs:
+    forward through mtnlg_reduce_partials_dropout, backward through
+    mtnlg_dropout_bwd into each half's backward, against the oracle with the
+    same Philox masks (1e-4)."""
+    w = WORKLOADS[1]
+    sh = shape_of(w)
+    p = float(np.float32(0.2))
+    seed, sites = 2024, (10, 11)
+    ap = [make_half_params(w, "attn", i) for i in range(w.tp)]
+    mp = [make_half_params(w, "mlp", i) for i in range(w.tp)]
+    x = make_activation(w, 1)
+    gout = make_activation(w, 2)
+    full = {k: np.zeros(s) for k, s in OL.full_param_shapes(sh).items()}
+    full["ln1_g"], full["ln1_b"], full["b_o"] = ap[0]["ln_g"], ap[0]["ln_b"], ap[0]["b_out"]
+    full["ln2_g"], full["ln2_b"], full["b_b"] = mp[0]["ln_g"], mp[0]["ln_b"], mp[0]["b_out"]
+    wl, fl = sh.local_width, sh.local_ffn
+    for i in range(w.tp):
+        cols = OL.qkv_columns(sh, i)
+        full["w_qkv"][:, cols] = ap[i]["w_in"]
+        full["b_qkv"][cols] = ap[i]["b_in"]
+        full["w_o"][i * wl:(i + 1) * wl] = ap[i]["w_out"]
+        full["w_a"][:, i * fl:(i + 1) * fl] = mp[i]["w_in"]
+        full["b_a"][i * fl:(i + 1) * fl] = mp[i]["b_in"]
+        full["w_b"][i * fl:(i + 1) * fl] = mp[i]["w_out"]
+    full = {k: np.asarray(v, dtype=np.float64) for k, v in full.items()}
+
+    dt = w.dtype
+    A = [GpuHalf(w, "attn", ap[i], i) for i in range(w.tp)]
+    M = [GpuHalf(w, "mlp", mp[i], i) for i in range(w.tp)]
+    xg = to_gpu(x, dt)
+    bo, bb = to_gpu(ap[0]["b_out"], dt), to_gpu(mp[0]["b_out"], dt)
+    x1 = empty(x.shape, dt)
+    tst.reduce_partials_dropout([a.fwd(xg) for a in A], x1, p, seed, sites[0], residual=xg, bias=bo)
+    out = empty(x.shape, dt)
+    tst.reduce_partials_dropout([m.fwd(x1) for m in M], out, p, seed, sites[1], residual=x1, bias=bb)
+    gg = to_gpu(gout, dt)
+    dz = empty(x.shape, dt)
+    tst.dropout_bwd(gg, dz, p, seed, sites[1])
+    g1 = empty(x.shape, dt)
+    tst.reduce_partials([m.bwd(x1, dz) for m in M], g1, residual=gg)
+    dz1 = empty(x.shape, dt)
+    tst.dropout_bwd(g1, dz1, p, seed, sites[0])
+    dx = empty(x.shape, dt)
+    tst.reduce_partials([a.bwd(xg, dz1) for a in A], dx, residual=g1)
+    torch.cuda.synchronize()
+
+    rout, st = OD.layer_fwd(sh, x.astype(np.float64), full, p, seed, sites)
+    rdx, ga, gm = OD.layer_bwd(sh, gout.astype(np.float64), st, p, seed, sites)
+    assert_close("x1", to_np(x1), st["x1"], dt)
+    assert_close("out", to_np(out), rout, dt)
+    assert_close("dx", to_np(dx), rdx, dt)
+    for i in range(w.tp):
+        for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out"):
+            assert_close(f"attn{i}.{k}", to_np(A[i].g[k]), ga[i][k], dt)
+            assert_close(f"mlp{i}.{k}", to_np(M[i].g[k]), gm[i][k], dt)
