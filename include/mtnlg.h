@@ -288,6 +288,10 @@ typedef struct {
   int32_t micro_batches;   /* >= 1 */
   int32_t recompute;       /* 0: keep each layer's saved tensors from forward to backward;
                               1: keep only each half's input and recompute in the backward */
+  float dropout_p;         /* dropout on each half's output, 0 <= p < 1 (0: none), as
+                              mtnlg_reduce_partials_dropout */
+  uint64_t dropout_seed;   /* the generator key's first word; the site of micro-batch k,
+                              layer l, half h is (k * layers + l) * 2 + h */
 } mtnlg_stage_desc;
 
 /* The stage's parameters live in ONE flat element array (the bf16 weights,
@@ -307,7 +311,9 @@ int mtnlg_stage_param_offsets(const mtnlg_stage_desc* desc, int64_t* off);
 size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
 
 /* One training step of the stage: for each micro-batch k in order, the
- * forward through every layer, then the backward in reverse order; then the
+ * forward through every layer, then the backward in reverse order (with
+ * dropout_p > 0 each half's output goes through mtnlg_reduce_partials_dropout
+ * and its backward starts from mtnlg_dropout_bwd of the same site); then the
  * flat gradient is accumulated into acc (overwritten by k = 0, added for
  * k > 0; the last accumulation carries the norm pass, see
  * mtnlg_grad_accumulate_norm); then mtnlg_adam_update with cfg.

@@ -23,6 +23,9 @@ Readings:
 * One slice (t = 1) is the whole layer, so the stage oracle works on full
   parameters; the optimizer step is the one in ``oracle.adam`` over all of
   the stage's parameters as one share.
+* With dropout (``oracle.dropout``), each half's output of micro-batch k and
+  layer l uses its own site, (k * layers + l) * 2 + half, so that no two
+  dropout masks of a step coincide.
 """
 from __future__ import annotations
 
@@ -71,13 +74,41 @@ def flatten(layer_dicts: list) -> np.ndarray:
     return np.concatenate(parts)
 
 
-def stage_micro_batches(sh: OL.LayerShape, layers: list, xs, gs):
+def _stage_dropout(sh: OL.LayerShape, layers: list, x, g, k: int, p: float, seed: int):
+    """One micro-batch through the stage with dropout on every half's output
+    (``oracle.dropout``): the site of micro-batch k, layer l, half h is
+    (k * layers + l) * 2 + h. One slice (t = 1), so a slice's gradients are
+    the layer's."""
+    from . import dropout as OD
+    assert sh.tp == 1
+    nl = len(layers)
+    sites = [((k * nl + l) * 2, (k * nl + l) * 2 + 1) for l in range(nl)]
+    states, h = [], x
+    for l, full in enumerate(layers):
+        h, st = OD.layer_fwd(sh, h, full, p, seed, sites[l])
+        states.append(st)
+    y = h
+    grads = [None] * nl
+    names = {0: dict(zip(("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out"), FLAT_ORDER[0])),
+             1: dict(zip(("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out"), FLAT_ORDER[1]))}
+    for l in reversed(range(nl)):
+        g, ga, gm = OD.layer_bwd(sh, g, states[l], p, seed, sites[l])
+        d = {names[0][key]: v for key, v in ga[0].items()}
+        d.update({names[1][key]: v for key, v in gm[0].items()})
+        grads[l] = d
+    return y, g, grads
+
+
+def stage_micro_batches(sh: OL.LayerShape, layers: list, xs, gs, dropout=None):
     """Forward and backward of every micro-batch. Returns (ys, dxs, per-micro-batch
-    flat gradients)."""
+    flat gradients). dropout = (p, seed) puts dropout on every half's output."""
     ys, dxs, flats = [], [], []
-    for x, g in zip(xs, gs):
-        y, states = stage_fwd(sh, layers, x)
-        dx, grads = stage_bwd(sh, layers, states, g)
+    for k, (x, g) in enumerate(zip(xs, gs)):
+        if dropout is not None and dropout[0] > 0.0:
+            y, dx, grads = _stage_dropout(sh, layers, x, g, k, dropout[0], dropout[1])
+        else:
+            y, states = stage_fwd(sh, layers, x)
+            dx, grads = stage_bwd(sh, layers, states, g)
         ys.append(y)
         dxs.append(dx)
         flats.append(flatten(grads))

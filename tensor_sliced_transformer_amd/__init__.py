@@ -176,8 +176,9 @@ def adam_update(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None
 STAGE_TENSORS = ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out")
 
 
-def make_stage_desc(layer: LayerDesc, layers: int, micro_batches: int, recompute: bool = False) -> StageDesc:
-    return StageDesc(layer, layers, micro_batches, int(recompute))
+def make_stage_desc(layer: LayerDesc, layers: int, micro_batches: int, recompute: bool = False,
+                    dropout_p: float = 0.0, dropout_seed: int = 0) -> StageDesc:
+    return StageDesc(layer, layers, micro_batches, int(recompute), dropout_p, dropout_seed)
 
 
 def stage_param_count(sd: StageDesc) -> int:

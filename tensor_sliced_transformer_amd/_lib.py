@@ -27,7 +27,8 @@ class LayerDesc(ctypes.Structure):
 
 
 class StageDesc(ctypes.Structure):
-    _fields_ = [("layer", LayerDesc), ("layers", c_int32), ("micro_batches", c_int32), ("recompute", c_int32)]
+    _fields_ = [("layer", LayerDesc), ("layers", c_int32), ("micro_batches", c_int32), ("recompute", c_int32),
+                ("dropout_p", c_float), ("dropout_seed", ctypes.c_uint64)]
 
 
 class Dropout(ctypes.Structure):

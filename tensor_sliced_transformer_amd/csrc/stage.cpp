@@ -11,6 +11,7 @@
 // runs forward then backward before the next starts: with no neighbouring
 // stage this is the order a one-forward-one-backward schedule gives, and it
 // keeps the saved activations of a single micro-batch alive at a time.
+#include <math.h>
 #include <string.h>
 
 #include <algorithm>
@@ -34,6 +35,8 @@ int stage_dims(const mtnlg_stage_desc* sd, StageDims* o) {
   if (!sd) return fail(MTNLG_ERR_ARG, "stage desc is NULL");
   if (sd->layers < 1 || sd->micro_batches < 1) return fail(MTNLG_ERR_SHAPE, "layers and micro_batches must be >= 1");
   if (sd->recompute != 0 && sd->recompute != 1) return fail(MTNLG_ERR_ARG, "recompute must be 0 or 1");
+  if (!(sd->dropout_p >= 0.0f && sd->dropout_p < 1.0f) || nearbyint((double)sd->dropout_p * 65536.0) >= 65536.0)
+    return fail(MTNLG_ERR_ARG, "dropout_p must be in [0, 1)");
   const mtnlg_layer_desc& L = sd->layer;
   if (L.dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "a stage runs bf16 layers (mixed precision)");
   if (mtnlg_saved_bytes(&L, MTNLG_ATTN) == 0 || mtnlg_saved_bytes(&L, MTNLG_MLP) == 0)
@@ -63,7 +66,7 @@ void layer_offsets(const StageDims& d, int layer, int64_t off[2][kTensors]) {
 
 // Workspace regions, each on a 256-byte boundary.
 struct StageWs {
-  size_t adam, xin, mid, part, g1, g2, saved, layer, total;
+  size_t adam, xin, mid, part, g1, g2, dz, saved, layer, total;
   size_t saved_a, saved_m;  // bytes of one layer's saved tensors per half
 };
 
@@ -86,6 +89,8 @@ StageWs stage_ws(const mtnlg_stage_desc* sd, const StageDims& d, int64_t n) {
   p += act;
   w.g2 = p;
   p += act;
+  w.dz = p;  // the masked gradient a half's backward starts from (dropout only)
+  p += sd->dropout_p > 0.0f ? act : 0;
   w.saved = p;  // every layer's saved tensors, or one scratch set when recomputing
   p += sd->recompute ? std::max(w.saved_a, w.saved_m) : (w.saved_a + w.saved_m) * (size_t)sd->layers;
   w.layer = p;
@@ -169,6 +174,10 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
     return l == desc->layers - 1 ? static_cast<char*>(y) + (size_t)k * act : base + W.xin + (size_t)l * act_al;
   };
   auto mid = [&](int l) -> void* { return base + W.mid + (size_t)l * act_al; };
+  const bool drop = desc->dropout_p > 0.0f;
+  auto site = [&](int k, int l, int half) -> uint64_t {
+    return ((uint64_t)k * (uint64_t)desc->layers + (uint64_t)l) * 2u + (uint64_t)half;
+  };
   auto saved = [&](int l, int half) -> void* {
     if (desc->recompute) return base + W.saved;
     return base + W.saved + (size_t)l * (W.saved_a + W.saved_m) + (half == MTNLG_MLP ? W.saved_a : 0);
@@ -185,7 +194,14 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
         const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
         STAGE_CALL(mtnlg_layer_fwd(L, half, &p, in[half], part, saved(l, half), lws, lws_bytes, stream));
         const void* parts[1] = {part};
-        STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, in[half], wb + 2 * t[5], out[half], stream));
+        if (drop) {
+          const mtnlg_dropout dr = {desc->dropout_seed, site(k, l, half), desc->dropout_p};
+          STAGE_CALL(mtnlg_reduce_partials_dropout(d.T, d.h, MTNLG_BF16, parts, 1, in[half], wb + 2 * t[5], &dr,
+                                                   out[half], stream));
+        } else {
+          STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, in[half], wb + 2 * t[5], out[half],
+                                           stream));
+        }
       }
     }
     const void* gcur = static_cast<const char*>(dy) + (size_t)k * act;
@@ -198,10 +214,17 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
         const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
         const mtnlg_half_grads g = {gb + 2 * t[0], gb + 2 * t[1], gb + 2 * t[2],
                                     gb + 2 * t[3], gb + 2 * t[4], gb + 2 * t[5]};
+        // the half's output gradient: gcur, or its dropout-masked copy
+        const void* dyh = gcur;
+        if (drop) {
+          const mtnlg_dropout dr = {desc->dropout_seed, site(k, l, half), desc->dropout_p};
+          STAGE_CALL(mtnlg_dropout_bwd(d.T, d.h, MTNLG_BF16, gcur, &dr, base + W.dz, stream));
+          dyh = base + W.dz;
+        }
         if (desc->recompute)
-          STAGE_CALL(mtnlg_layer_bwd_recompute(L, half, &p, in[half], gcur, part, &g, lws, lws_bytes, stream));
+          STAGE_CALL(mtnlg_layer_bwd_recompute(L, half, &p, in[half], dyh, part, &g, lws, lws_bytes, stream));
         else
-          STAGE_CALL(mtnlg_layer_bwd(L, half, &p, in[half], saved(l, half), gcur, part, &g, lws, lws_bytes,
+          STAGE_CALL(mtnlg_layer_bwd(L, half, &p, in[half], saved(l, half), dyh, part, &g, lws, lws_bytes,
                                      stream));
         // dx of the half = dy (residual path) + the slice's partial
         void* dst = half == MTNLG_MLP ? g1 : (l == 0 ? static_cast<char*>(dx) + (size_t)k * act : g2);

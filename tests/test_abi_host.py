@@ -144,6 +144,21 @@ def test_recompute_workspace_and_validation():
     assert L.mtnlg_recompute_workspace_bytes(ctypes.byref(desc(seq=100)), _lib.ATTN) == 0
 
 
+def test_dropout_entry_points_validate():
+    L = lib()
+    arr = (ctypes.c_void_p * 1)(A)
+    for p in (-0.1, 1.0, float("nan"), 0.99999999):
+        d = _lib.Dropout(1, 2, p)
+        assert L.mtnlg_reduce_partials_dropout(4, 16, _lib.BF16, arr, 1, None, None, ctypes.byref(d), A, None) == -1
+        assert L.mtnlg_dropout_bwd(4, 16, _lib.BF16, A, ctypes.byref(d), A, None) == -1
+    d = _lib.Dropout(1, 2, 0.5)
+    assert L.mtnlg_reduce_partials_dropout(4, 12, _lib.BF16, arr, 1, None, None, ctypes.byref(d), A, None) == -2
+    assert L.mtnlg_reduce_partials_dropout(4, 16, 9, arr, 1, None, None, ctypes.byref(d), A, None) == -3
+    assert L.mtnlg_reduce_partials_dropout(4, 16, _lib.BF16, arr, 1, None, None, None, A, None) == -1
+    assert L.mtnlg_dropout_bwd(4, 16, _lib.BF16, ODD, ctypes.byref(d), A, None) == -4
+    assert L.mtnlg_dropout_bwd(4, 16, _lib.BF16, A, ctypes.byref(d), None, None) == -1
+
+
 def test_other_entry_points_validate():
     L = lib()
     arr = (ctypes.c_void_p * 2)(A, A)
@@ -216,7 +231,15 @@ def test_stage_workspace_and_validation():
     lw = max(L.mtnlg_recompute_workspace_bytes(ctypes.byref(rc.layer), h) for h in (0, 1))
     want_rc = align256(L.mtnlg_adam_workspace_bytes(n)) + act * 8 + max(sa, sm) + align256(lw)
     assert L.mtnlg_stage_workspace_bytes(ctypes.byref(rc)) == want_rc
+    dr = _stage()
+    dr.dropout_p = 0.1
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(dr)) == want + act        # the masked-gradient buffer
     # invalid descriptors
+    bad = _stage()
+    bad.dropout_p = 1.0
+    assert L.mtnlg_stage_param_count(ctypes.byref(bad)) == -1
+    bad.dropout_p = 0.9999999                     # rounds to a threshold of 65536
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(bad)) == 0
     assert L.mtnlg_stage_param_count(ctypes.byref(_stage(dtype=_lib.F32))) == -1
     assert L.mtnlg_stage_param_count(ctypes.byref(_stage(layers=0))) == -1
     assert L.mtnlg_stage_workspace_bytes(ctypes.byref(_stage(recompute=2))) == 0

@@ -9,7 +9,9 @@ Checked:
 * the Adam step against the oracle applied to the GPU's own accumulator
   (delta p 1e-4, m and v 1e-5, norm 1e-6); the bf16 weights are the GPU
   master rounded to nearest even, bit for bit;
-* the recompute schedule gives bit-identical results to the stored one.
+* the recompute schedule gives bit-identical results to the stored one;
+* all of it without dropout and with dropout (p = 0.15) on every half's
+  output, the masks drawn by the GPU and, independently, by the oracle.
 Tolerance metric: ||gpu - oracle||_inf / ||oracle||_inf per tensor.
 """
 import numpy as np
@@ -48,8 +50,8 @@ def _setup():
     return w, L, MB, ld, halves, full, xs, gs
 
 
-def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg):
-    sd = tst.make_stage_desc(ld, L, MB, recompute)
+def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0):
+    sd = tst.make_stage_desc(ld, L, MB, recompute, p, seed)
     n = tst.stage_param_count(sd)
     offs = tst.stage_param_offsets(sd)
     flat = np.zeros(n, dtype=np.float32)
@@ -82,19 +84,23 @@ def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg):
     return out, flat, m0, v0, offs
 
 
-def test_stage_step_against_oracle_and_recompute():
+@pytest.mark.parametrize("p", [0.0, 0.15])
+def test_stage_step_against_oracle_and_recompute(p):
     w, L, MB, ld, halves, full, xs, gs = _setup()
-    print(f"stage {w.name}: {L} layers, {MB} micro-batches", flush=True)
+    p = float(np.float32(p))           # the rate as the library receives it
+    seed = 0xC0FFEE
+    print(f"stage {w.name}: {L} layers, {MB} micro-batches, dropout {p}", flush=True)
     cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, max_grad_norm=0.5, inv_loss_scale=1.0,
                         step=w.extra["step"])
-    got, flat, m0, v0, offs = _run(w, L, MB, ld, halves, xs, gs, False, cfg)
-    again, *_ = _run(w, L, MB, ld, halves, xs, gs, True, cfg)
+    got, flat, m0, v0, offs = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed)
+    again, *_ = _run(w, L, MB, ld, halves, xs, gs, True, cfg, p, seed)
     for k in got:
         assert np.array_equal(got[k], again[k]), f"recompute differs in {k}"
 
     sh = OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=1)
-    ys, dxs, flats = OS.stage_micro_batches(sh, [{k: v.astype(np.float64) for k, v in p.items()} for p in full],
-                                            [x.astype(np.float64) for x in xs], [g.astype(np.float64) for g in gs])
+    ys, dxs, flats = OS.stage_micro_batches(sh, [{k: v.astype(np.float64) for k, v in q.items()} for q in full],
+                                            [x.astype(np.float64) for x in xs], [g.astype(np.float64) for g in gs],
+                                            dropout=(p, seed))
     errs = {}
     for k in range(MB):
         errs[f"y{k}"] = rel_inf(got["y"][k], ys[k])

@@ -99,3 +99,40 @@ def test_flat_layout_follows_documented_order():
         for key, n in zip([k for half in OS.FLAT_ORDER for k in half], sizes):
             assert np.array_equal(flat[pos:pos + n], p[key].reshape(-1)), key
             pos += n
+
+
+def test_stage_with_dropout_finite_differences():
+    """With dropout on every half (masks fixed by seed and site), the summed
+    loss's gradient over 2 layers x 2 micro-batches matches central
+    differences; at p = 0 the dropout path equals the plain one."""
+    from oracle import dropout as OD
+    layers = make_layers(2, 140)
+    xs = [rng(150 + k).standard_normal((SH.tokens, SH.hidden)) for k in range(2)]
+    gs = [rng(160 + k).standard_normal((SH.tokens, SH.hidden)) for k in range(2)]
+    p, seed = 0.3, 77
+    _, dxs, flats = OS.stage_micro_batches(SH, layers, xs, gs, dropout=(p, seed))
+    acc = OA.accumulate(flats)
+    r = rng(170)
+    up = [{k: r.standard_normal(v.shape) for k, v in q.items()} for q in layers]
+    ux = [r.standard_normal(x.shape) for x in xs]
+    delta = 1e-5
+
+    def loss_at(s):
+        tot = 0.0
+        for k, (x, g) in enumerate(zip(xs, gs)):
+            lay = [{key: q[key] + s * u[key] for key in q} for q, u in zip(layers, up)]
+            h = x + s * ux[k]
+            for l, full in enumerate(lay):
+                h, _ = OD.layer_fwd(SH, h, full, p, seed, ((k * 2 + l) * 2, (k * 2 + l) * 2 + 1))
+            tot += float((h * g).sum())
+        return tot
+
+    fd = (loss_at(delta) - loss_at(-delta)) / (2 * delta)
+    an = float(acc @ OS.flatten(up)) + sum(float((dx * u).sum()) for dx, u in zip(dxs, ux))
+    assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0), (fd, an)
+    # p = 0: the dropout path reduces to the plain stage
+    ys0, dxs0, fl0 = OS.stage_micro_batches(SH, layers, xs[:1], gs[:1])
+    y1, dx1, g1 = OS._stage_dropout(SH, layers, xs[0], gs[0], 0, 0.0, seed)
+    np.testing.assert_allclose(y1, ys0[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dx1, dxs0[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(OS.flatten(g1), fl0[0], rtol=0, atol=1e-12)
