@@ -16,6 +16,11 @@
   of every sequence (always its first and last position) in float64.
   Tolerance 2e-2 (||gpu - oracle||_inf / ||oracle||_inf over the rows).
 
+* One pipeline-stage step at the slice shape (3 layers, 2 micro-batches,
+  1,887,859,200 flat parameters) against the same work done through the
+  layer-level entry points: bit-identical outputs, input gradients,
+  accumulator, master weights, bf16 weights and optimizer statistics.
+
 Inputs at these sizes are drawn with torch's seeded generator on the GPU
 (numpy would need minutes for 1.9e9 or 5e9 values), with the distributions of
 the other workloads: activations N(0,1), weights and biases N(0,0.02),
@@ -174,3 +179,107 @@ def test_full_layer_eight_slices_sampled_rows():
     err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
     print(f"full layer sampled rows: rel_inf {err:.3e}", flush=True)
     assert err < 2e-2
+
+
+def test_stage_full_shard_matches_layer_calls():
+    """One pipeline-stage step at the MT-NLG slice shape (3 layers, 2 micro-batches
+    of 2048 tokens, 1,887,859,200 flat parameters, 64-bit offsets) is bit-identical
+    to the same work done through the individual layer, partial-sum, accumulation
+    and optimizer entry points: checks the stage's flat layout, buffer chaining
+    and accumulation order at the real size (the layers themselves are checked
+    against the oracle in test_gpu_layer.py)."""
+    w = WORKLOADS[7]
+    L, MB = w.extra["layers"], 2
+    dev = torch.device("cuda:0")
+    ld = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, 0, tst.BF16, 1e-5)
+    sd = tst.make_stage_desc(ld, L, MB, False)
+    n = tst.stage_param_count(sd)
+    assert n == 1_887_859_200
+    offs = tst.stage_param_offsets(sd)
+    print(f"stage full shard: {L} layers x {MB} micro-batches, n={n}", flush=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7100)
+    master0 = torch.randn(n, device=dev, generator=gen).mul_(0.02)
+    for lay in offs:
+        for half in lay:
+            master0[half["ln_g"]:half["ln_g"] + w.hidden].add_(1.0)
+    x = torch.randn((MB, w.tokens, w.hidden), device=dev, generator=gen).to(torch.bfloat16)
+    dy = torch.randn((MB, w.tokens, w.hidden), device=dev, generator=gen).to(torch.bfloat16)
+    cfg = tst.AdamCfg(1e-4, 0.9, 0.95, 1e-8, 0.0, 1.0, 1.0, 3)
+
+    # (1) the stage entry point
+    master = master0.clone()
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    wt = master0.to(torch.bfloat16)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    stats = torch.zeros(3, dtype=torch.float32, device=dev)
+    ws = torch.empty(tst.stage_workspace_bytes(sd), dtype=torch.uint8, device=dev)
+    tst.stage_step(sd, cfg, wt, master, m, v, grad, acc, x, dy, y, dx, stats, ws)
+    torch.cuda.synchronize()
+    res = {"y": y.clone(), "dx": dx.clone(), "acc": acc.clone(), "master": master.clone(), "w": wt.clone(),
+           "stats": stats.clone()}
+    del ws, y, dx
+
+    # (2) the same work through the layer-level entry points
+    w2 = master0.to(torch.bfloat16)
+    g2 = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    keys = ("ln_g", "ln_b", "w_in", "b_in", "w_out")
+    win = {tst.ATTN: 3 * w.local_width, tst.MLP: w.local_ffn}
+    wout = {tst.ATTN: w.local_width, tst.MLP: w.local_ffn}
+
+    def views(buf, lay, half):
+        o = offs[lay][half]
+        h = w.hidden
+        shapes = {"ln_g": (h,), "ln_b": (h,), "w_in": (h, win[half]), "b_in": (win[half],),
+                  "w_out": (wout[half], h), "b_out": (h,)}
+        return {k: buf.narrow(0, o[k], int(np.prod(s))).view(s) for k, s in shapes.items()}
+
+    sav = {hf: torch.empty(tst.saved_bytes(ld, hf), dtype=torch.uint8, device=dev) for hf in (tst.ATTN, tst.MLP)}
+    saved = [[torch.empty_like(sav[hf]) for hf in (tst.ATTN, tst.MLP)] for _ in range(L)]
+    lws = torch.empty(max(tst.workspace_bytes(ld, tst.ATTN), tst.workspace_bytes(ld, tst.MLP)),
+                      dtype=torch.uint8, device=dev)
+    part = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=dev)
+    acc2 = torch.empty(n, dtype=torch.float32, device=dev)
+    aws = torch.empty(tst.adam_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    y2 = torch.empty_like(x)
+    dx2 = torch.empty_like(x)
+    for k in range(MB):
+        ins = []
+        cur = x[k]
+        for lay in range(L):
+            outs = []
+            for hf in (tst.ATTN, tst.MLP):
+                pv = views(w2, lay, hf)
+                tst.layer_fwd(ld, hf, {kk: pv[kk] for kk in keys}, cur, part, saved[lay][hf], lws)
+                nxt = y2[k] if (lay == L - 1 and hf == tst.MLP) else torch.empty_like(part)
+                tst.reduce_partials([part], nxt, residual=cur, bias=pv["b_out"])
+                outs.append(cur)
+                cur = nxt
+            ins.append(outs)
+        gcur = dy[k]
+        for lay in reversed(range(L)):
+            for hf in (tst.MLP, tst.ATTN):
+                pv = views(w2, lay, hf)
+                gv = views(g2, lay, hf)
+                tst.layer_bwd(ld, hf, {kk: pv[kk] for kk in keys}, ins[lay][hf], saved[lay][hf], gcur, part, gv, lws)
+                nxt = dx2[k] if (lay == 0 and hf == tst.ATTN) else torch.empty_like(part)
+                tst.reduce_partials([part], nxt, residual=gcur)
+                gcur = nxt
+        if k + 1 < MB:
+            tst.grad_accumulate(g2, acc2, overwrite=(k == 0))
+        else:
+            tst.grad_accumulate_norm(g2, acc2, k == 0, cfg.inv_loss_scale, aws)
+    m2 = torch.zeros(n, device=dev)
+    v2 = torch.zeros(n, device=dev)
+    master2 = master0.clone()
+    stats2 = torch.zeros(3, dtype=torch.float32, device=dev)
+    tst.adam_update(cfg, master2, m2, v2, acc2, w2, stats2, aws)
+    torch.cuda.synchronize()
+    for name, a, b in (("y", res["y"], y2), ("dx", res["dx"], dx2), ("acc", res["acc"], acc2),
+                       ("master", res["master"], master2), ("w", res["w"], w2), ("stats", res["stats"], stats2)):
+        assert torch.equal(a, b), name
+    print(f"stage full shard: bit-identical; norm {res['stats'][0].item():.6g}", flush=True)
