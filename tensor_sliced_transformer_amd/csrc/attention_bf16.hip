@@ -53,13 +53,19 @@ using namespace attn;
 // stay below 2^kSlack.
 constexpr float kSlack = 8.0f;
 
+// Two ring stages and at most 256 registers per lane, so that two workgroups
+// share a CU (two waves per SIMD): measured 8% faster than one workgroup with
+// a three-stage ring at head_dim 160.
+constexpr int kFwdRing = 2;
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ o,
-                                                            float* __restrict__ lse, int seq, int nh, int64_t tokens,
-                                                            int nbh, float scale_log2) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv,
+                                                               bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                               int seq, int nh, int64_t tokens, int nbh,
+                                                               float scale_log2) {
   using TL = Tile<D>;
   constexpr int EB = TL::EB, SUB = TL::SUB, STAGE = 2 * TL::BYTES;
-  __shared__ __align__(1024) char smem[kRing * STAGE];
+  __shared__ __align__(1024) char smem[kFwdRing * STAGE];
 
   const int nqb = seq / kRows;
   const int qb = nqb - 1 - (int)blockIdx.x / nbh;
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16_t* __rest
   for (int e = 0; e < EB; ++e) zero(oacc[e]);
   float m = -INFINITY, l = 0.0f;
 
-  ring_walk<2 * TL::IPW>(qb + 1, issue, [&](int it, int stage) {
+  ring_walk<2 * TL::IPW, kFwdRing>(qb + 1, issue, [&](int it, int stage) {
     const char* sk = smem + stage * STAGE;
     const char* sv = sk + TL::BYTES;
     const int kw0 = it * kRows + 32 * kh;
@@ -145,6 +151,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const bf16_t* __rest
   // merge the two key halves: (m, l, O) of wave kh=1 into wave kh=0
   l += __shfl_xor(l, 32, kWave);
   __syncthreads();  // every load has been waited for and every wave is done with the ring
+  static_assert(2 * (EB * 16 + 2) * 64 * 4 <= kFwdRing * STAGE, "merge staging exceeds the ring");
   float* xs = reinterpret_cast<float*>(smem) + qg * (EB * 16 + 2) * 64;
   if (kh == 1) {
 #pragma unroll

@@ -108,19 +108,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // starts the loads of tile t into a ring stage; body(it, stage) computes on
 // tile it. The loop is unrolled by the ring depth so that each stage index,
 // and with it every LDS address of the body, is a compile-time offset.
-template <int NLD, typename Issue, typename Body>
+// RING is the number of ring stages (kRing unless a kernel trades depth for a
+// second resident workgroup).
+template <int NLD, int RING = kRing, typename Issue, typename Body>
 __device__ __forceinline__ void ring_walk(int count, Issue&& issue, Body&& body) {
 #pragma unroll
-  for (int t = 0; t < kRing - 1; ++t)
+  for (int t = 0; t < RING - 1; ++t)
     if (t < count) issue(t, t);
-  for (int it0 = 0; it0 < count; it0 += kRing) {
+  for (int it0 = 0; it0 < count; it0 += RING) {
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) {
+    for (int j = 0; j < RING; ++j) {
       const int it = it0 + j;
       if (it < count) {
-        wait_tiles<NLD>(min(kRing - 2, count - 1 - it));
+        wait_tiles<NLD>(min(RING - 2, count - 1 - it));
         __syncthreads();
-        if (it + kRing - 1 < count) issue(it + kRing - 1, (j + kRing - 1) % kRing);
+        if (it + RING - 1 < count) issue(it + RING - 1, (j + RING - 1) % RING);
         body(it, j);
       }
     }

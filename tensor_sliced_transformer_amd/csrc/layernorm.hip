@@ -326,6 +326,15 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[u][e] = 0.0f;
   int64_t r = r0;
+  for (; r + 7 < r1; r += 8) {  // eight loads in flight per thread
+    float v[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8(x + (r + u) * cols + c8, v[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[u & 3][e] += v[u][e];
+  }
   for (; r + 3 < r1; r += 4) {
     float v[4][8];
 #pragma unroll
@@ -403,7 +412,9 @@ hipError_t col_reduce_launch(const float* part, int P, int nout, int cols, void*
   return hipGetLastError();
 }
 
-constexpr int kColsumRows = 64;
+// 32 rows per workgroup: at 2048 rows and 10240-20480 columns that is 320-640
+// workgroups, enough loads in flight to stream at close to the copy rate.
+constexpr int kColsumRows = 32;
 
 }  // namespace
 
