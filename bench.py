@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--adam-reps", type=int, default=5)
     ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--no-stage", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock and power sample")
     ap.add_argument("--stage-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (to scale HBM byte counters)")
@@ -136,16 +137,36 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event before every step (and one after the last): the mean over the
+    # K steps is `value`; the per-step median and minimum are reported beside it
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    start, end = evs[0], evs[-1]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        evs[i].record()
         step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    ms_min = per_step[0]
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"fwd+bwd step {ms:.3f} ms = {tflops:.1f} TFLOP/s")
+    log(f"fwd+bwd step {ms:.3f} ms = {tflops:.1f} TFLOP/s (median {ms_median:.3f}, min {ms_min:.3f} ms)")
+    # the same step under the other counting conventions: dense attention
+    # (every query against every key), and the 4x-forward count of a step that
+    # recomputes the forward (the convention of the throughput figures the
+    # MT-NLG news article quotes)
+    fwd_dense = shard_fwd_flops(T, h, w.local_heads, w.head_dim, fl, w.seq, w.batch, causal=False)
+
+    # ---- GPU clock and power while the step runs (not part of the timed region) ----
+    clocks = None if args.no_clock else clock_sample(torch, step, ms)
+    if clocks and clocks["gfx_clock_mhz"]:
+        peak_at_clock = PEAK_BF16_TFLOPS * clocks["gfx_clock_mhz"] / 2400.0
+        clocks["mfma_peak_frac_at_clock"] = round(tflops / peak_at_clock, 4)
+        log(f"under load: GPU clock {clocks['gfx_clock_mhz']:.0f} MHz, {clocks['socket_power_w']} W; "
+            f"{100 * tflops / peak_at_clock:.1f}% of the peak at that clock")
 
     # ---- the same step with the backward recomputing each half's forward from
     # its input (only the layer inputs are kept between forward and backward) ----
@@ -179,8 +200,11 @@ def main():
               "model_tflops": round(flops / (ms_rc * 1e-3) / 1e12, 2),
               "executed_tflops": round(hw_flops / (ms_rc * 1e-3) / 1e12, 2),
               "executed_flop_per_step": hw_flops,
+              "four_x_forward_tflops": round(4.0 * fwd_dense / (ms_rc * 1e-3) / 1e12, 2),
+              "four_x_forward_flop_per_step": 4.0 * fwd_dense,
               "note": "model_tflops counts the step's 3x-forward FLOPs; executed_tflops adds "
-                      "the recomputed forward (output GEMMs skipped)"}
+                      "the recomputed forward (output GEMMs skipped); four_x_forward_tflops uses the "
+                      "4x-forward, dense-attention count of the MT-NLG throughput figures"}
         log(f"recompute step {ms_rc:.3f} ms = {rc['model_tflops']} model / {rc['executed_tflops']} "
             f"executed TFLOP/s")
         del ws_rc
@@ -203,6 +227,13 @@ def main():
                    "local_heads": w.local_heads, "head_dim": w.head_dim, "local_ffn": fl, "causal": True,
                    "flop_per_step": flops},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "ms_per_step_min": round(ms_min, 4),
+        "clocks": clocks,
+        "dense_attention_convention": {
+            "tflops": round(3.0 * fwd_dense / (ms * 1e-3) / 1e12, 2), "flop_per_step": 3.0 * fwd_dense,
+            "note": "the same step time over the FLOP count with attention counted dense (every query "
+                    "against every key); value counts only the causal half"},
     }
     if rc is not None:
         result["recompute"] = rc
@@ -254,10 +285,65 @@ def gemm_traffic_bytes():
     return rec["avg_bytes_per_launch"]
 
 
-def shard_fwd_flops(tokens, hidden, heads_local, head_dim, ffn_local, seq, batch):
+def smi_sample():
+    """(mean GPU core clock over the XCDs in MHz, memory clock in MHz, socket power in W)
+    from amd-smi, or None where it is not available."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
+                             text=True, timeout=10)
+        d = json.loads(out.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = g["clock"]
+
+        def vals(prefix):
+            return [v["clk"]["value"] for k, v in clk.items()
+                    if k.startswith(prefix) and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        gfx, mem = vals("gfx_"), vals("mem_")
+        pw = g["power"]["socket_power"]
+        return (sum(gfx) / len(gfx) if gfx else None, sum(mem) / len(mem) if mem else None,
+                pw["value"] if isinstance(pw, dict) else None)
+    except Exception:
+        return None
+
+
+def clock_sample(torch, step, ms_step, seconds=1.5):
+    """Runs the step back to back for about `seconds` while amd-smi is polled from a
+    second thread; the medians of the samples taken while the GPU is busy."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            s = smi_sample()
+            if s is None:
+                return
+            samples.append(s)
+
+    n = max(1, int(seconds * 1e3 / ms_step))
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    for _ in range(n):
+        step()
+    th.start()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+
+    def med(i):
+        v = sorted(s[i] for s in samples if s[i] is not None)
+        return v[len(v) // 2] if v else None
+    return {"gfx_clock_mhz": med(0), "mem_clock_mhz": med(1), "socket_power_w": med(2), "samples": len(samples),
+            "steps": n}
+
+
+def shard_fwd_flops(tokens, hidden, heads_local, head_dim, ffn_local, seq, batch, causal=True):
     wl = heads_local * head_dim
     gemm = 2.0 * tokens * (hidden * 3 * wl + wl * hidden + hidden * ffn_local + ffn_local * hidden)
-    attn = 4.0 * batch * heads_local * head_dim * seq * (seq + 1) / 2.0
+    pairs = seq * (seq + 1) / 2.0 if causal else float(seq) * seq
+    attn = 4.0 * batch * heads_local * head_dim * pairs
     return gemm + attn
 
 
