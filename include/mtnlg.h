@@ -328,11 +328,20 @@ size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
  *   dx      [micro_batches, T, h] bf16: gradient of the stage input, written
  *   stats   DEVICE f32[3]: {norm, coef, found_inf} of the step
  *   ws      >= mtnlg_stage_workspace_bytes(desc)
+ *   aux_stream  nullable second hipStream_t. When given (and different from
+ *           stream), the gradient of each layer of every micro-batch but the
+ *           last is accumulated on it as soon as that layer's backward is
+ *           done, overlapping the accumulation with the rest of the work;
+ *           ordering between the two streams uses events the call creates and
+ *           releases itself. Results are identical with and without it. All
+ *           of the step's work is complete once `stream` has passed it.
  * n = mtnlg_stage_param_count(desc). All arguments are validated before
- * anything is enqueued; errors as the calls it makes. */
+ * anything is enqueued; errors as the calls it makes (MTNLG_ERR_HIP also
+ * when an event cannot be created). */
 int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, void* w, float* master,
                      float* m, float* v, void* grad, float* acc, const void* x, const void* dy, void* y,
-                     void* dx, float* stats, void* ws, size_t ws_bytes, void* stream);
+                     void* dx, float* stats, void* ws, size_t ws_bytes, void* stream,
+                     void* aux_stream);
 
 /* ---- Component entry points (the kernels the layer calls, one at a time) ---- */
 

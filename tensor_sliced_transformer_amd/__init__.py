@@ -201,11 +201,14 @@ def stage_workspace_bytes(sd: StageDesc) -> int:
 
 
 def stage_step(sd: StageDesc, cfg: AdamCfg, w, master, m, v, grad, acc, x, dy, y, dx, stats, ws,
-               stream=None) -> None:
-    """One training step of a pipeline stage (mtnlg_stage_step)."""
+               stream=None, aux_stream=None) -> None:
+    """One training step of a pipeline stage (mtnlg_stage_step); aux_stream, a second
+    torch stream, lets the gradient accumulation overlap the compute."""
+    aux = ctypes.c_void_p(aux_stream.cuda_stream) if aux_stream is not None else None
     check(load().mtnlg_stage_step(ctypes.byref(sd), ctypes.byref(cfg), _ptr(w), _ptr(master), _ptr(m), _ptr(v),
                                   _ptr(grad), _ptr(acc), _ptr(x), _ptr(dy), _ptr(y), _ptr(dx), _ptr(stats),
-                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "mtnlg_stage_step")
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream), aux),
+          "mtnlg_stage_step")
 
 
 def gemm_workspace_bytes(dtype: int, M: int, N: int, K: int) -> int:

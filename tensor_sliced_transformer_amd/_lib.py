@@ -78,7 +78,7 @@ SIGNATURES = {
     "mtnlg_stage_workspace_bytes": (c_size_t, [POINTER(StageDesc)]),
     "mtnlg_stage_step": (c_int32, [POINTER(StageDesc), POINTER(AdamCfg), c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                   c_size_t, c_void_p]),
+                                   c_size_t, c_void_p, c_void_p]),
     "mtnlg_gemm_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64, c_int64]),
     "mtnlg_gemm": (c_int32, [c_int32, c_int32, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

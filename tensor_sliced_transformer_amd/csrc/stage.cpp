@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "abi_common.hpp"
 
@@ -103,6 +104,24 @@ StageWs stage_ws(const mtnlg_stage_desc* sd, const StageDims& d, int64_t n) {
   return w;
 }
 
+// Events of one stage step, released when the step's work is enqueued (the
+// runtime frees an event whose last record is still pending once it completes).
+struct EventSet {
+  std::vector<hipEvent_t> e;
+  hipError_t create(int count) {
+    for (int i = 0; i < count; ++i) {
+      hipEvent_t ev;
+      const hipError_t r = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+      e.push_back(ev);
+    }
+    return hipSuccess;
+  }
+  ~EventSet() {
+    for (hipEvent_t ev : e) (void)hipEventDestroy(ev);
+  }
+};
+
 #define STAGE_CALL(call)          \
   do {                            \
     const int s_ = (call);        \
@@ -140,7 +159,7 @@ size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc) {
 
 int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, void* w, float* master, float* m,
                      float* v, void* grad, float* acc, const void* x, const void* dy, void* y, void* dx,
-                     float* stats, void* ws, size_t ws_bytes, void* stream) {
+                     float* stats, void* ws, size_t ws_bytes, void* stream, void* aux_stream) {
   g_last_error[0] = 0;
   StageDims d;
   STAGE_CALL(stage_dims(desc, &d));
@@ -155,6 +174,19 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
   CHECK_PTR(dx);
   const StageWs W = stage_ws(desc, d, n);
   if (ws_bytes < W.total) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, W.total);
+
+  // With a second stream, each layer's gradient of micro-batch k < last is
+  // accumulated on it as soon as that layer's backward is done, overlapping the
+  // HBM-bound accumulation with the MFMA-bound work of the following layers and
+  // micro-batches; the next micro-batch's backward of that layer waits for it.
+  const int nl = desc->layers, mb = desc->micro_batches;
+  hipStream_t S = static_cast<hipStream_t>(stream), A = static_cast<hipStream_t>(aux_stream);
+  const bool overlap = A != nullptr && A != S && mb > 1;
+  EventSet bwd_done, acc_done;
+  if (overlap) {
+    MTNLG_HIP(bwd_done.create(nl), "hipEventCreateWithFlags");
+    MTNLG_HIP(acc_done.create(nl), "hipEventCreateWithFlags");
+  }
 
   const mtnlg_layer_desc* L = &desc->layer;
   const size_t act = (size_t)d.act * 2;
@@ -208,6 +240,9 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
     for (int l = desc->layers - 1; l >= 0; --l) {
       int64_t o[2][kTensors];
       layer_offsets(d, l, o);
+      // layer l's gradient buffer is rewritten below: the previous micro-batch's
+      // accumulation of it must be done
+      if (overlap && k > 0) MTNLG_HIP(hipStreamWaitEvent(S, acc_done.e[l], 0), "hipStreamWaitEvent");
       const void* in[2] = {xin(l, k), mid(l)};
       for (int half = 1; half >= 0; --half) {
         const int64_t* t = o[half];
@@ -232,13 +267,23 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
         STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, gcur, nullptr, dst, stream));
         gcur = dst;
       }
+      if (overlap && k + 1 < mb) {
+        const int64_t lo = (int64_t)l * d.per_layer;
+        MTNLG_HIP(hipEventRecord(bwd_done.e[l], S), "hipEventRecord");
+        MTNLG_HIP(hipStreamWaitEvent(A, bwd_done.e[l], 0), "hipStreamWaitEvent");
+        STAGE_CALL(mtnlg_grad_accumulate(d.per_layer, MTNLG_BF16, gb + 2 * lo, acc + lo, k == 0, A));
+        MTNLG_HIP(hipEventRecord(acc_done.e[l], A), "hipEventRecord");
+      }
     }
     const bool first = k == 0;
-    if (k + 1 < desc->micro_batches)
-      STAGE_CALL(mtnlg_grad_accumulate(n, MTNLG_BF16, grad, acc, first, stream));
-    else
+    if (k + 1 < mb) {
+      if (!overlap) STAGE_CALL(mtnlg_grad_accumulate(n, MTNLG_BF16, grad, acc, first, stream));
+    } else {
+      // every earlier accumulation is ordered before this one: S waited for each
+      // layer's before rewriting that layer's gradient
       STAGE_CALL(mtnlg_grad_accumulate_norm(n, MTNLG_BF16, grad, acc, first, cfg->inv_loss_scale, base + W.adam,
                                             W.xin - W.adam, stream));
+    }
   }
   return mtnlg_adam_update(cfg, n, master, m, v, acc, w, stats, base + W.adam, W.xin - W.adam, stream);
 }

@@ -251,7 +251,7 @@ def test_stage_workspace_and_validation():
 
     def step(c=cfg, ws_bytes=big, grad=A):
         return L.mtnlg_stage_step(ctypes.byref(sd), ctypes.byref(c), A, A, A, A, grad, A, A, A, A, A, A, A,
-                                  ws_bytes, None)
+                                  ws_bytes, None, None)
     assert step(ws_bytes=want - 1) == -5
     assert step(grad=None) == -1
     assert step(grad=ODD) == -4

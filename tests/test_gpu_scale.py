@@ -17,7 +17,8 @@
   Tolerance 2e-2 (||gpu - oracle||_inf / ||oracle||_inf over the rows).
 
 * One pipeline-stage step at the slice shape (3 layers, 2 micro-batches,
-  1,887,859,200 flat parameters) against the same work done through the
+  1,887,859,200 flat parameters, the accumulation overlapped on a second
+  stream) against the same work done through the
   layer-level entry points: bit-identical outputs, input gradients,
   accumulator, master weights, bf16 weights and optimizer statistics.
 
@@ -218,7 +219,7 @@ def test_stage_full_shard_matches_layer_calls():
     dx = torch.empty_like(x)
     stats = torch.zeros(3, dtype=torch.float32, device=dev)
     ws = torch.empty(tst.stage_workspace_bytes(sd), dtype=torch.uint8, device=dev)
-    tst.stage_step(sd, cfg, wt, master, m, v, grad, acc, x, dy, y, dx, stats, ws)
+    tst.stage_step(sd, cfg, wt, master, m, v, grad, acc, x, dy, y, dx, stats, ws, aux_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     res = {"y": y.clone(), "dx": dx.clone(), "acc": acc.clone(), "master": master.clone(), "w": wt.clone(),
            "stats": stats.clone()}

@@ -9,7 +9,8 @@ Checked:
 * the Adam step against the oracle applied to the GPU's own accumulator
   (delta p 1e-4, m and v 1e-5, norm 1e-6); the bf16 weights are the GPU
   master rounded to nearest even, bit for bit;
-* the recompute schedule gives bit-identical results to the stored one;
+* the recompute schedule, and the accumulation overlapped on a second
+  stream, give bit-identical results to the plain schedule;
 * all of it without dropout and with dropout (p = 0.15) on every half's
   output, the masks drawn by the GPU and, independently, by the oracle.
 Tolerance metric: ||gpu - oracle||_inf / ||oracle||_inf per tensor.
@@ -50,7 +51,7 @@ def _setup():
     return w, L, MB, ld, halves, full, xs, gs
 
 
-def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0):
+def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0, aux=False):
     sd = tst.make_stage_desc(ld, L, MB, recompute, p, seed)
     n = tst.stage_param_count(sd)
     offs = tst.stage_param_offsets(sd)
@@ -76,7 +77,8 @@ def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0):
     ws = empty_bytes(tst.stage_workspace_bytes(sd))
     c = tst.AdamCfg(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.max_grad_norm,
                     cfg.inv_loss_scale, cfg.step)
-    tst.stage_step(sd, c, wt, master, mm, vv, grad, acc, x, dy, y, dx, stats, ws)
+    aux_stream = torch.cuda.Stream() if aux else None
+    tst.stage_step(sd, c, wt, master, mm, vv, grad, acc, x, dy, y, dx, stats, ws, aux_stream=aux_stream)
     torch.cuda.synchronize()
     out = {"y": y.float().cpu().numpy(), "dx": dx.float().cpu().numpy(), "acc": acc.cpu().numpy(),
            "master": master.cpu().numpy(), "m": mm.cpu().numpy(), "v": vv.cpu().numpy(),
@@ -96,6 +98,10 @@ def test_stage_step_against_oracle_and_recompute(p):
     again, *_ = _run(w, L, MB, ld, halves, xs, gs, True, cfg, p, seed)
     for k in got:
         assert np.array_equal(got[k], again[k]), f"recompute differs in {k}"
+    # the accumulation overlapped on a second stream gives the same bits
+    ovl, *_ = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed, aux=True)
+    for k in got:
+        assert np.array_equal(got[k], ovl[k]), f"second stream differs in {k}"
 
     sh = OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=1)
     ys, dxs, flats = OS.stage_micro_batches(sh, [{k: v.astype(np.float64) for k, v in q.items()} for q in full],
