@@ -66,8 +66,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's tensor slice on one GPU; runs on more than one GPU "
-              "are not supported by this build (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+        print("bench.py measures one GPU's tensor slice on one GPU; the library has no multi-GPU "
+              "path, so only --gpus 1 runs (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 
