@@ -543,12 +543,43 @@ def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=2048):
         OL.attn_half_bwd(sh, g1, pa, sa)
     dt = time.perf_counter() - t0
     fl = reps * 3.0 * shard_fwd_flops(sample_tokens, 20480, 16, 160, 10240, sample_tokens, 1)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
     log(f"cpu baseline {dt:.1f}s, {fl / dt / 1e12:.3f} TFLOP/s on {threads} threads")
+
+    # the oracle's optimizer step on a 2^22-element chunk of the same workload, as
+    # GB/s with the step's 34 bytes per parameter (accumulator, master, m, v read;
+    # master, m, v and the bf16 copy written; the norm pass)
+    from oracle import adam as OA
+    rng = np.random.Generator(np.random.PCG64(4040))
+    nc = 1 << 22
+    p0 = rng.standard_normal(nc) * 0.02
+    m0 = rng.standard_normal(nc) * 1e-3
+    v0 = (rng.standard_normal(nc) * 1e-3) ** 2
+    a0 = rng.standard_normal(nc) * 2e-3
+    t1 = time.perf_counter()
+    OA.adam_step(p0, m0, v0, a0, OA.AdamConfig(step=100))
+    dta = time.perf_counter() - t1
+    adam_gbs = 34.0 * nc / dta / 1e9
+    log(f"cpu baseline adam: {dta:.2f}s for 2^22 parameters = {adam_gbs:.2f} GB/s")
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 oracle fwd+bwd of the same 1/8 slice on the first {sample_tokens} tokens "
                       f"of the workload, {reps} passes ({fl / 1e12:.3f} TFLOP), {dt:.1f} s",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2),
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "blas": [{k: i.get(k) for k in ("internal_api", "version", "num_threads")} for i in info],
+            "adam": {"value": round(adam_gbs, 3), "unit": "GB/s", "sample": "float64 oracle Adam step over 2^22 "
+                     "parameters (34 B/param accounting)", "seconds": round(dta, 3)}}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
