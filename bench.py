@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--adam-reps", type=int, default=5)
     ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--no-stage", action="store_true")
-    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock and power sample")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amdsmi clock and power sample")
     ap.add_argument("--stage-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (to scale HBM byte counters)")
@@ -285,30 +285,54 @@ def gemm_traffic_bytes():
     return rec["avg_bytes_per_launch"]
 
 
+_SMI = []
+
+
+def _smi_handle():
+    """The amdsmi library and the handle of the GPU torch calls device 0 (queried
+    in-process: no external program is started from a process that uses the GPU)."""
+    if not _SMI:
+        import amdsmi
+        import torch
+        try:
+            h = torch.cuda._get_amdsmi_handler(0)
+        except Exception:
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+        _SMI.append((amdsmi, h))
+    return _SMI[0]
+
+
 def smi_sample():
     """(mean GPU core clock over the XCDs in MHz, memory clock in MHz, socket power in W)
-    from amd-smi, or None where it is not available."""
-    import subprocess
+    from the amdsmi library, or None where it is not available."""
+    def num(v):
+        return v if isinstance(v, (int, float)) and not isinstance(v, bool) and 0 < v < 65535 else None
     try:
-        out = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
-                             text=True, timeout=10)
-        d = json.loads(out.stdout)
-        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        clk = g["clock"]
-
-        def vals(prefix):
-            return [v["clk"]["value"] for k, v in clk.items()
-                    if k.startswith(prefix) and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
-        gfx, mem = vals("gfx_"), vals("mem_")
-        pw = g["power"]["socket_power"]
-        return (sum(gfx) / len(gfx) if gfx else None, sum(mem) / len(mem) if mem else None,
-                pw["value"] if isinstance(pw, dict) else None)
+        amdsmi, h = _smi_handle()
+        gfx = None
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            xcd = [c for c in (num(v) for v in m.get("current_gfxclks", []) or []) if c is not None]
+            gfx = sum(xcd) / len(xcd) if xcd else None
+        except Exception:
+            pass
+        if gfx is None:
+            ci = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            gfx = num(ci.get("clk", ci.get("cur_clk")))
+        mi = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+        mem = num(mi.get("clk", mi.get("cur_clk")))
+        pi = amdsmi.amdsmi_get_power_info(h)
+        pw = num(pi.get("current_socket_power"))
+        if pw is None:
+            pw = num(pi.get("average_socket_power"))
+        return (gfx, mem, pw) if gfx is not None else None
     except Exception:
         return None
 
 
 def clock_sample(torch, step, ms_step, seconds=1.5):
-    """Runs the step back to back for about `seconds` while amd-smi is polled from a
+    """Runs the step back to back for about `seconds` while amdsmi is polled from a
     second thread; the medians of the samples taken while the GPU is busy."""
     import threading
     samples, stop = [], threading.Event()
@@ -319,6 +343,7 @@ def clock_sample(torch, step, ms_step, seconds=1.5):
             if s is None:
                 return
             samples.append(s)
+            stop.wait(0.02)
 
     n = max(1, int(seconds * 1e3 / ms_step))
     torch.cuda.synchronize()

@@ -142,6 +142,16 @@ __device__ __forceinline__ void dtl16(i32x4_t rsrc, const void* lds_base, uint32
                : "memory", "m0");
 }
 
+// As dtl16, with the destination given as a 32-bit LDS byte address (no
+// generic-to-LDS pointer conversion on the issue path).
+__device__ __forceinline__ void dtl16_at(i32x4_t rsrc, uint32_t lds_addr, uint32_t off) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
 // As dtl16, with a wave-uniform byte offset `soff` added to every lane's `off`.
 __device__ __forceinline__ void dtl16_so(i32x4_t rsrc, const void* lds_base, uint32_t off, uint32_t soff) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MTNLG_LDS(lds_base));

@@ -664,9 +664,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl_kernel(GemmArgs p)
 //   read serves at a time land in 8 distinct bank groups, and each row of a
 //   tile is one whole 128-byte line in memory.
 // * M/N-contiguous operands: as in the 32-deep kernel, 64 rows of k.
-// * A 2-stage ring (2 x 64 KiB): right after the barrier that publishes tile
-//   t (and so frees the stage of tile t-1) the loads of tile t+1 are issued
-//   in one burst; they are waited for (vmcnt) just before the next barrier.
+// * A 2-stage ring (2 x 64 KiB) and one barrier per K tile, placed before
+//   the tile's last k-substep: by then every fragment of the tile is in
+//   registers, so the barrier both publishes tile t+1 and frees the stage of
+//   tile t. The last substep's MFMAs then cover the first fragment reads of
+//   tile t+1 and the loads of tile t+2 into the freed stage, which have a
+//   whole tile to land before the next barrier waits for them (vmcnt).
+// * Each substep issues all reads of the next substep's fragments right
+//   after its first MFMA, in the order the next substep consumes them, so
+//   they have the rest of the substep to arrive.
+// * The direct-to-LDS destination (m0) is computed as a 32-bit LDS address
+//   from the array base, not from a generic pointer.
 // ---------------------------------------------------------------------------
 constexpr int kBK64 = 64;
 
@@ -697,7 +705,7 @@ struct Dtl64 {
     }
   }
   __device__ __forceinline__ void load_one(int u, i32x4_t rs, int64_t ld, int r0, int rmax, int k0, int kend,
-                                           char* dst, int wave) const {
+                                           uint32_t dst, int wave) const {
     const int q = wave * PER_WAVE + u;
     uint32_t off;
     if (KC) {
@@ -707,7 +715,7 @@ struct Dtl64 {
       const int k = k0 + r_[u], m = r0 + c_[u];
       off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)k * ld + m) * 2) : kOob;
     }
-    dtl16(rs, dst + q * 1024, off);
+    dtl16_at(rs, dst + (uint32_t)q * 1024u, off);
   }
 };
 
@@ -733,8 +741,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
   const int nk = (kend - kbeg + kBK64 - 1) / kBK64;
   float* const pt = tw.split >= 0 ? p.part + ((int64_t)tw.split * p.tail_tiles + tw.tl) * BM * BN : nullptr;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)MTNLG_LDS(smem);
   const i32x4_t ra = rsrc_words(p.A, (uint32_t)((int64_t)p.M * p.K * 2));
   const i32x4_t rb = rsrc_words(p.B, (uint32_t)((int64_t)p.K * p.N * 2));
   OA oa;
@@ -762,30 +771,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   uint4 af[2][FM], bfr[2][FN];
-  auto read_frags = [&](const char* st, int s, int buf) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const char* q = st + aoff[s][i];
-      if (A_KC) {
-        af[buf][i] = *reinterpret_cast<const uint4*>(q);
-      } else {
-        const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OA::RB);
-        af[buf][i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const char* q = st + boff[s][j];
-      if (B_KC) {
-        bfr[buf][j] = *reinterpret_cast<const uint4*>(q);
-      } else {
-        const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OB::RB);
-        bfr[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
+  // fragments are read in the order the MFMAs consume them: a0, b0 .. b(FN-1), a1 .. a(FM-1)
+  auto read_a = [&](const char* st, int s, int buf, int i) {
+    const char* q = st + aoff[s][i];
+    if (A_KC) {
+      af[buf][i] = *reinterpret_cast<const uint4*>(q);
+    } else {
+      const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OA::RB);
+      af[buf][i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
   };
+  auto read_b = [&](const char* st, int s, int buf, int j) {
+    const char* q = st + boff[s][j];
+    if (B_KC) {
+      bfr[buf][j] = *reinterpret_cast<const uint4*>(q);
+    } else {
+      const uint2 lo = ds_read_tr(q), hi = ds_read_tr(q + 4 * OB::RB);
+      bfr[buf][j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+  auto read_frags = [&](const char* st, int s, int buf) {
+    read_a(st, s, buf, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) read_b(st, s, buf, j);
+#pragma unroll
+    for (int i = 1; i < FM; ++i) read_a(st, s, buf, i);
+  };
   auto issue = [&](int t) {
-    char* st = smem + (t & 1) * SS;
+    const uint32_t st = lds0 + (uint32_t)((t & 1) * SS);
 #pragma unroll
     for (int u = 0; u < OA::PER_WAVE; ++u) oa.load_one(u, ra, p.lda, m0, p.M, kbeg + t * kBK64, kend, st, wave);
 #pragma unroll
@@ -800,38 +813,70 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
       }
   };
 
+  // Schedule of one substep: its first MFMA, then every read of the next
+  // substep's fragments, then the remaining MFMAs, so the reads have almost
+  // the whole substep to arrive.
+  constexpr int NM = FM * FN;
+  constexpr int NR = (A_KC ? FM : 2 * FM) + (B_KC ? FN : 2 * FN);
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - 1, 0);
+  };
+
+  auto load_u = [&](int t, int u) {  // this wave's u-th load of tile t (A loads first, then B)
+    const uint32_t st = lds0 + (uint32_t)((t & 1) * SS);
+    if (u < OA::PER_WAVE) oa.load_one(u, ra, p.lda, m0, p.M, kbeg + t * kBK64, kend, st, wave);
+    else ob.load_one(u - OA::PER_WAVE, rb, p.ldb, n0, p.N, kbeg + t * kBK64, kend, st + SA, wave);
+  };
+  constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // loads per tile per wave
+
+  // prologue: tiles 0 and 1 in flight, wait for tile 0
   if (nk > 0) {
     issue(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (nk > 1) {
+      issue(1);
+      MTNLG_VMCNT(NL);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
     __syncthreads();
     read_frags(smem, 0, 0);
   }
   for (int kt = 0; kt < nk; ++kt) {
     const char* st = smem + (kt & 1) * SS;
-    // stage (kt+1)&1 held tile kt-1, which every wave finished before the barrier above
-    if (kt + 1 < nk) issue(kt + 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) read_frags(st, s + 1, (s + 1) & 1);
+    for (int s = 0; s < 3; ++s) {
+      read_frags(st, s + 1, (s + 1) & 1);
       mfmas(s & 1);
-      // Schedule: one MFMA, then one LDS read of the next substep's fragments,
-      // and so on, so every read has the rest of the substep to land (left to
-      // itself the compiler issues the reads late and waits on them at once).
-      constexpr int NR = (A_KC ? FM : 2 * FM) + (B_KC ? FN : 2 * FN);  // read instructions
-      constexpr int NM = FM * FN;
-      if (s < 3) {
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, NR / NM > 0 ? NR / NM : 1, 0);  // DS read
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
-      }
+      interleave();
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // tile kt+1 has landed (this wave's part)
+    // Substep 3: its fragments are in registers. Publish tile kt+1 (loaded
+    // since substep 3 of the previous tile) and free this stage; then the
+    // first reads of tile kt+1 and the loads of tile kt+2 into this stage are
+    // woven into the last MFMAs of tile kt.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    if (kt + 1 < nk) read_frags(smem + ((kt + 1) & 1) * SS, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    Mfma<bf16_t>::run(af[1][0], bfr[1][0], acc[0][0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // (after the last tile this reads a stale stage; the values are unused)
+    read_frags(smem + ((kt + 1) & 1) * SS, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = kt + 2 < nk;
+#pragma unroll
+    for (int idx = 1; idx < NM; ++idx) {
+      Mfma<bf16_t>::run(af[1][idx / FN], bfr[1][idx % FN], acc[idx / FN][idx % FN]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        // NL loads over MFMAs 1 .. NM-1
+        const int lo = (idx - 1) * NL / (NM - 1), hi = idx * NL / (NM - 1);
+#pragma unroll
+        for (int u = lo; u < hi; ++u) load_u(kt + 2, u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   __builtin_amdgcn_s_waitcnt(0x0F70);
