@@ -22,7 +22,7 @@ Also measured in the same run:
     for the roofline of the GEMM kernel;
   * the float64 CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam] [--no-recompute] [--no-stage]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam] [--no-recompute] [--no-stage] [--no-components]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--adam-reps", type=int, default=5)
     ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--no-stage", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the LayerNorm / partial-sum / attention kernels timed alone")
     ap.add_argument("--no-clock", action="store_true", help="skip the amdsmi clock and power sample")
     ap.add_argument("--stage-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -246,6 +248,9 @@ def main():
     if not args.no_stage:
         result["stage"] = stage_bench(torch, tst, dev, args.stage_steps, 1, flops, False)
         result["stage_recompute"] = stage_bench(torch, tst, dev, args.stage_steps, 1, flops, True)
+
+    if not args.no_components:
+        result["components"] = component_bench(torch, tst, dev, T, h, w.local_heads, w.head_dim)
 
     # ---- each GEMM launch of the step alone (same shapes and operand layouts),
     # last so that a kernel trace of this script ends with these launches ----
@@ -489,7 +494,94 @@ def adam_bench(torch, tst, dev, reps):
            "grad_norm": st[0], "clip_coef": st[1], "found_inf": st[2], "fused_norm": fused}
     del master, m, v, grads, acc, wbf, ws
     torch.cuda.empty_cache()
+    # what a plain device-to-device copy reaches on the same GPU in the same run
+    # (the practical streaming ceiling the optimizer kernels are compared with)
+    src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_copy = ev[0].elapsed_time(ev[1]) / reps
+    copy_gbs = 2.0 * src.numel() * 4 / (t_copy * 1e-3) / 1e9
+    out["device_copy"] = {"bytes_moved": 2 * src.numel() * 4, "ms": round(t_copy, 3), "GBps": round(copy_gbs, 1),
+                          "hbm_frac": round(copy_gbs / PEAK_HBM_GBS, 4),
+                          "step_vs_copy": round(step_gbs / copy_gbs, 4),
+                          "accumulate_vs_copy": round(acc_gbs / copy_gbs, 4),
+                          "note": "torch copy_ of 2 GiB fp32 (read + write counted)"}
+    log(f"plain device copy: {copy_gbs:.0f} GB/s; Adam step at {100 * step_gbs / copy_gbs:.0f}% of it, "
+        f"accumulation at {100 * acc_gbs / copy_gbs:.0f}%")
+    del src, dst
+    torch.cuda.empty_cache()
     return out
+
+
+def component_bench(torch, tst, dev, T, h, heads, head_dim, reps=20):
+    """The step's bandwidth-bound kernels and the attention kernels, each launched
+    alone at the slice's shapes and timed with HIP events on the stream they run
+    on: achieved GB/s against their algorithmic bytes (bf16 [T, h] tensors read or
+    written once, fp32 row statistics), attention in TFLOP/s (causal count)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7000)
+    bf = torch.bfloat16
+
+    def rn(*shape, scale=1.0):
+        return (torch.randn(*shape, device=dev, generator=gen) * scale).to(bf)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    x, gy, part = rn(T, h), rn(T, h), rn(T, h)
+    gamma, beta, bias = rn(h, scale=0.02), rn(h, scale=0.02), rn(h, scale=0.02)
+    y, dx, out = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    mean = torch.empty(T, dtype=torch.float32, device=dev)
+    rstd = torch.empty_like(mean)
+    dgamma, dbeta = torch.empty_like(gamma), torch.empty_like(beta)
+    lws = torch.empty(max(16, tst.layernorm_bwd_workspace_bytes(T, h)), dtype=torch.uint8, device=dev)
+    tb = T * h * 2
+    res = {}
+
+    def bw(name, ms, nbytes, what):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "bytes": nbytes, "GBps": round(gbs, 1),
+                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_counted": what}
+
+    bw("layernorm_fwd", timed(lambda: tst.layernorm_fwd(x, gamma, beta, 1e-5, y, mean, rstd)),
+       2 * tb + 8 * T, "x read, y written, mean/rstd written")
+    bw("layernorm_bwd", timed(lambda: tst.layernorm_bwd(gy, x, mean, rstd, gamma, dx, dgamma, dbeta, lws)),
+       3 * tb + 8 * T, "dy and x read, dx written (+ row stats; gamma/beta grads are h-sized)")
+    bw("reduce_partials", timed(lambda: tst.reduce_partials([part], out, residual=x, bias=bias)),
+       3 * tb, "one partial and the residual read, the sum written")
+    wl = heads * head_dim
+    qkv = rn(T, 3 * wl, scale=2.9)
+    o = torch.empty(T, wl, dtype=bf, device=dev)
+    lse = torch.empty(heads, T, dtype=torch.float32, device=dev)
+    do, dqkv = rn(T, wl), torch.empty_like(qkv)
+    aws = torch.empty(max(16, tst.attention_bwd_workspace_bytes(1, T, heads)), dtype=torch.uint8, device=dev)
+    causal = 4.0 * heads * head_dim * (T * (T + 1) / 2.0)
+    ms_f = timed(lambda: tst.attention_fwd(qkv, o, lse, 1, T, heads, head_dim))
+    ms_b = timed(lambda: tst.attention_bwd(qkv, o, lse, do, dqkv, aws, 1, T, heads, head_dim))
+    res["attention_fwd"] = {"us": round(ms_f * 1e3, 2), "flop": causal, "tflops": round(causal / (ms_f * 1e-3) / 1e12, 1)}
+    res["attention_bwd"] = {"us": round(ms_b * 1e3, 2), "flop": 2 * causal,
+                            "tflops": round(2 * causal / (ms_b * 1e-3) / 1e12, 1),
+                            "note": "algorithmic count (dV, dP, dQ, dK); the recomputed scores are not counted"}
+    log("components alone: " + ", ".join(
+        f"{k} {v['us']:.1f} us" + (f" {v['GBps']:.0f} GB/s" if "GBps" in v else f" {v['tflops']:.0f} TFLOP/s")
+        for k, v in res.items()))
+    del x, gy, part, y, dx, out, qkv, o, do, dqkv, lws, aws
+    torch.cuda.empty_cache()
+    return res
 
 
 def stage_bench(torch, tst, dev, steps, warmup, layer_flops, recompute):
