@@ -63,6 +63,25 @@ def test_gemm_large_tiles_bf16(M, N, K):
     assert_close("C", to_np(c), a.astype(np.float64) @ b.astype(np.float64) + bias[None, :], "bf16")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 64), (4096, 4096, 128), (4096, 4096, 200), (4000, 4104, 1032)])
+def test_gemm_large_tiles_layouts_short_and_ragged_k(ta, tb, M, N, K):
+    """The 256x256-tile kernel in every operand layout with one, two and a
+    ragged number of 64-deep K tiles (the loop's prologue, its last tile and
+    the loads it skips past the end of K), and ragged M and N (272 tiles)."""
+    print(f"gemm large ta={ta} tb={tb} {M}x{N}x{K}", flush=True)
+    a = inputs(17, (K, M) if ta else (M, K), "bf16")
+    b = inputs(18, (N, K) if tb else (K, N), "bf16")
+    bias = inputs(19, (N,), "bf16")
+    c = empty((M, N), "bf16")
+    ws = empty_bytes(tst.gemm_workspace_bytes(tst.BF16, M, N, K))
+    tst.gemm(to_gpu(a, "bf16"), to_gpu(b, "bf16"), c, bool(ta), bool(tb), bias=to_gpu(bias, "bf16"), ws=ws)
+    torch.cuda.synchronize()
+    A = a.astype(np.float64).T if ta else a.astype(np.float64)
+    B = b.astype(np.float64).T if tb else b.astype(np.float64)
+    assert_close("C", to_np(c), A @ B + bias.astype(np.float64)[None, :], "bf16")
+
+
 # ------------------------------------------------------------------ LayerNorm
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rows,cols", [(64, 256), (37, 4096), (9, 20480), (5, 264)])
