@@ -25,12 +25,16 @@
 //   * MFMA blocks are 32x32 (v_mfma_f32_32x32x16_bf16); fragments are
 //     double-buffered across 16-deep k-substeps. Out-of-range elements come
 //     from buffer loads past num_records (zeros), not from branches.
-//   * Workgroup ids are remapped so that each XCD (ids round-robin over 8
-//     XCDs) gets a contiguous range of tiles, walked in groups of 8 tile rows
-//     so that concurrently running tiles share operand panels in that XCD's L2.
+//   * Work ids are remapped so that each XCD (ids round-robin over 8 XCDs)
+//     gets a contiguous range of tiles, walked in groups of 8 tile rows so
+//     that concurrently running tiles share operand panels in that XCD's L2.
 //   * Wave quantisation: when the last round of tiles would leave at least
 //     half the CUs idle, only those leftover tiles are split along K into
-//     fp32 partials that a second kernel sums before the epilogue.
+//     fp32 partials that a second kernel sums before the epilogue; the pieces
+//     are ordered split-major before being handed out per XCD.
+//   * The 256x256 kernel is persistent (one workgroup per CU looping over work
+//     items): the first two K tiles of its next item are loaded while the
+//     current item's epilogue runs from a private 16-row LDS slab per wave.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +45,9 @@ namespace {
 constexpr int kCH = 8;        // 16-byte chunks per LDS row
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
+// Workgroups of the persistent 256x256 kernel: one per CU of MI355X (a
+// multiple of the 8 XCDs, so a workgroup's items all map to its own XCD).
+constexpr int kPersistentGrid = 256;
 
 __device__ __forceinline__ float gelu_f(float u) {
   return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
@@ -223,16 +230,56 @@ __device__ __forceinline__ void epilogue_slab(const GemmArgs& p, const float* st
   }
 }
 
-// Tile index L, K range and tail piece (split < 0: whole tile) of workgroup w.
+// Epilogue over one wave's private 16 x 64 fp32 slab (row r's column c stored
+// at c ^ (32 * ((r >> 2) & 1))) whose first element is tile-local (rl0, cl0).
+template <typename T, int WN, int BN>
+__device__ __forceinline__ void epilogue_slab16(const GemmArgs& p, const float* slab, int m0, int n0, int rl0,
+                                                int cl0, int lane, float* pt) {
+  static_assert(WN == 64, "slab swizzle assumes two 32-column halves");
+  constexpr int VPR = WN / 8;
+#pragma unroll 1
+  for (int u = lane; u < 16 * VPR; u += kWave) {
+    const int rr = u / VPR, cc = (u % VPR) * 8;
+    const float* q = slab + rr * WN + (cc ^ (32 * ((rr >> 2) & 1)));
+    float v[8];
+    const float4 a = *reinterpret_cast<const float4*>(q);
+    const float4 b = *reinterpret_cast<const float4*>(q + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    if (pt) {
+      store8(pt + (int64_t)(rl0 + rr) * BN + cl0 + cc, v);
+      continue;
+    }
+    const int row = m0 + rl0 + rr, col = n0 + cl0 + cc;
+    if (row >= p.M || col >= p.N) continue;
+    apply_epi_store<T>(p, row, col, v);
+  }
+}
+
+// Tile position of tile index L: groups of kGroupM tile rows, walked column by column.
+__device__ __forceinline__ void tile_pos(const GemmArgs& p, int L, int& tm, int& tn) {
+  const int group = kGroupM * p.tiles_n;
+  const int gq = L / group;
+  const int first_m = gq * kGroupM;
+  const int gm = min(p.tiles_m - first_m, kGroupM);
+  tm = first_m + (L % group) % gm;
+  tn = (L % group) / gm;
+}
+
+// Tile index L, K range and tail piece (split < 0: whole tile) of work item w.
+// Consecutive ids go round-robin over the 8 XCDs (XCD w & 7), so each XCD is
+// given a contiguous range of whole tiles, and of tail pieces ordered
+// split-major: the pieces sharing an XCD's L2 then cover one K range of
+// neighbouring tiles rather than every K range of one tile row.
 struct TileWork {
   int tm, tn, split, tl, kbeg, kend;
 };
 __device__ __forceinline__ TileWork tile_work(const GemmArgs& p, int w) {
   TileWork t;
   int L;
+  const int xcd = w & 7;
   if (w < p.nfull) {
-    // XCD-contiguous ranges: consecutive ids go round-robin over 8 XCDs
-    const int xcd = w & 7, idx = w >> 3;
+    const int idx = w >> 3;
     const int base = p.nfull >> 3, rem = p.nfull & 7;
     L = xcd * base + min(xcd, rem) + idx;
     t.split = -1;
@@ -240,20 +287,23 @@ __device__ __forceinline__ TileWork tile_work(const GemmArgs& p, int w) {
     t.kbeg = 0;
     t.kend = p.K;
   } else {
+    const int np = p.tail_tiles * p.tail_split;
     const int u = w - p.nfull;
-    t.tl = u % p.tail_tiles;
-    t.split = u / p.tail_tiles;
+    // pieces u on this XCD are u0, u0 + 8, ...; XCDs before it own the first pieces in split-major order
+    const int u0 = (xcd - p.nfull) & 7;
+    int first = 0;
+    for (int y = 0; y < xcd; ++y) {
+      const int uy = (y - p.nfull) & 7;
+      first += uy < np ? (np - uy + 7) >> 3 : 0;
+    }
+    const int v = first + ((u - u0) >> 3);
+    t.tl = v % p.tail_tiles;
+    t.split = v / p.tail_tiles;
     L = p.nfull + t.tl;
     t.kbeg = t.split * p.k_chunk;
     t.kend = min(p.K, t.kbeg + p.k_chunk);
   }
-  // groups of kGroupM tile rows, walked column by column
-  const int group = kGroupM * p.tiles_n;
-  const int gq = L / group;
-  const int first_m = gq * kGroupM;
-  const int gm = min(p.tiles_m - first_m, kGroupM);
-  t.tm = first_m + (L % group) % gm;
-  t.tn = (L % group) / gm;
+  tile_pos(p, L, t.tm, t.tn);
   return t;
 }
 
@@ -676,6 +726,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl_kernel(GemmArgs p)
 //   they have the rest of the substep to arrive.
 // * The direct-to-LDS destination (m0) is computed as a 32-bit LDS address
 //   from the array base, not from a generic pointer.
+// * Persistent: one workgroup per CU (the ring fills LDS anyway) takes work
+//   items b, b + 256, ... Once an item's last fragments are read, the first
+//   two K tiles of the next item are issued into the ring and the epilogue
+//   runs from a private 16 x 64 fp32 slab per wave (the 32 KiB left beside
+//   the ring, so no workgroup barrier), hiding the next item's load latency
+//   behind the epilogue (+1 to 2.5% on the K = 2048 weight-gradient shapes).
+// * Per-lane load and fragment offsets are affine in the load index and the
+//   k-substep, so only their bases are kept, and they are recomputed per work
+//   item so that they are not live across the epilogue (no VGPR spills at the
+//   256-register budget of two waves per SIMD).
 // ---------------------------------------------------------------------------
 constexpr int kBK64 = 64;
 
@@ -685,38 +745,41 @@ struct Dtl64 {
   static constexpr int INSTR = STAGE_BYTES / 1024;
   static constexpr int PER_WAVE = INSTR / NW;
   static constexpr int RB = R * 2;  // MN layout: bytes per k row
+  // rows (KC: of M/N, MN: of k) that one wave-wide KiB load covers
+  static constexpr int STEP = KC ? 8 : 1024 / RB;
   static_assert(PER_WAVE >= 1 && INSTR % NW == 0, "tile too small");
-  int r_[PER_WAVE], c_[PER_WAVE];
+  static_assert(PER_WAVE % 2 == 0 && (KC || RB == 512), "slot pattern assumes even loads per wave, 256-wide MN rows");
+  // Load q = wave * PER_WAVE + u covers row r0 + (q - wave * PER_WAVE) * STEP;
+  // its column within the row depends only on q's parity (cpar[q & 1]).
+  int r0, cpar[2];
   __device__ __forceinline__ void init(int wave, int lane) {
+    const int q = wave * PER_WAVE;  // even
+    if (KC) {
+      r0 = q * 8 + lane / 8;        // 8 rows of 128 B per KiB
+      const int slot = lane & 7;    // chunk slot ^ ((r >> 1) & 7), (r >> 1) & 7 = 4 (q & 1) + lane / 16
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u) {
-      const int q = wave * PER_WAVE + u;
-      if (KC) {
-        const int r = q * 8 + lane / 8;       // 8 rows of 128 B per KiB
-        const int slot = lane & 7;
-        r_[u] = r;
-        c_[u] = 8 * (slot ^ ((r >> 1) & 7));
-      } else {
-        const int rows_per = 1024 / RB;
-        const int k = q * rows_per + (16 * lane) / RB;
-        const int slot = ((16 * lane) % RB) / 16;
-        r_[u] = k;
-        c_[u] = 8 * (slot ^ (4 * (k & 3)));
-      }
+      for (int e = 0; e < 2; ++e) cpar[e] = 8 * (slot ^ (4 * e + lane / 16));
+    } else {
+      r0 = q * 2 + lane / 32;       // 2 k rows of 512 B per KiB
+      const int slot = lane & 31;   // chunk slot ^ 4 (k & 3), k & 3 = 2 (q & 1) + lane / 32
+#pragma unroll
+      for (int e = 0; e < 2; ++e) cpar[e] = 8 * (slot ^ (4 * (2 * e + lane / 32)));
     }
   }
-  __device__ __forceinline__ void load_one(int u, i32x4_t rs, int64_t ld, int r0, int rmax, int k0, int kend,
+  // issue load u (+ QOFF, an even count of loads of other waves) of the K-tile at k0 into the stage at dst
+  template <int QOFF = 0>
+  __device__ __forceinline__ void load_one(int u, i32x4_t rs, int64_t ld, int rb0, int rmax, int k0, int kend,
                                            uint32_t dst, int wave) const {
-    const int q = wave * PER_WAVE + u;
+    const int r = r0 + (u + QOFF) * STEP, c = cpar[u & 1];
     uint32_t off;
     if (KC) {
-      const int m = r0 + r_[u], k = k0 + c_[u];
+      const int m = rb0 + r, k = k0 + c;
       off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)m * ld + k) * 2) : kOob;
     } else {
-      const int k = k0 + r_[u], m = r0 + c_[u];
+      const int k = k0 + r, m = rb0 + c;
       off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)k * ld + m) * 2) : kOob;
     }
-    dtl16_at(rs, dst + (uint32_t)q * 1024u, off);
+    dtl16_at(rs, dst + (uint32_t)(wave * PER_WAVE + u + QOFF) * 1024u, off);
   }
 };
 
@@ -734,13 +797,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
   using OA = Dtl64<BM, A_KC, NW>;
   using OB = Dtl64<BN, B_KC, NW>;
   constexpr int SA = OA::STAGE_BYTES, SB = OB::STAGE_BYTES, SS = SA + SB;
-  __shared__ __align__(1024) char smem[2 * SS];
+  // the ring, then one private 16-row epilogue slab per wave
+  constexpr int ESLAB = 16 * TN;  // floats
+  __shared__ __align__(1024) char smem[2 * SS + NW * ESLAB * 4];
 
-  const TileWork tw = tile_work(p, blockIdx.x);
-  const int m0 = tw.tm * BM, n0 = tw.tn * BN;
-  const int kbeg = tw.kbeg, kend = tw.kend;
-  const int nk = (kend - kbeg + kBK64 - 1) / kBK64;
-  float* const pt = tw.split >= 0 ? p.part + ((int64_t)tw.split * p.tail_tiles + tw.tl) * BM * BN : nullptr;
+  // Persistent: workgroup b takes work items b, b + gridDim.x, ... (gridDim.x a
+  // multiple of 8, so every item of a workgroup maps to the XCD it runs on).
+  const int total = p.nfull + p.tail_tiles * p.tail_split;
+  int w = blockIdx.x;
+  if (w >= total) return;
+  TileWork tw = tile_work(p, w);
+  int m0 = tw.tm * BM, n0 = tw.tn * BN;
+  int kbeg = tw.kbeg, kend = tw.kend;
+  int nk = (kend - kbeg + kBK64 - 1) / kBK64;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -749,32 +818,30 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
   const i32x4_t rb = rsrc_words(p.B, (uint32_t)((int64_t)p.K * p.N * 2));
   OA oa;
   OB ob;
-  oa.init(wave, lane);
-  ob.init(wave, lane);
-
-  int aoff[4][FM], boff[4][FN];
+  constexpr int AN = A_KC ? 4 : FM, BN_ = B_KC ? 4 : FN;
+  int abase[AN], bbase[BN_];
+  // Per-lane offsets, (re)computed for every work item from an opaque copy of
+  // the lane id so that they are not kept live across the epilogue.
+  auto lane_setup = [&]() {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    oa.init(wave, ln);
+    ob.init(wave, ln);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+    for (int e = 0; e < AN; ++e)
+      abase[e] = A_KC ? kc64_frag_off(wm * FM, e, ln) : mn_frag_off<OA::RB>(wm * FM + e, 0, ln);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      aoff[s][i] = A_KC ? kc64_frag_off(wm * FM + i, s, lane) : mn_frag_off<OA::RB>(wm * FM + i, s, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      boff[s][j] = SA + (B_KC ? kc64_frag_off(wn * FN + j, s, lane) : mn_frag_off<OB::RB>(wn * FN + j, s, lane));
-  }
+    for (int e = 0; e < BN_; ++e)
+      bbase[e] = SA + (B_KC ? kc64_frag_off(wn * FN, e, ln) : mn_frag_off<OB::RB>(wn * FN + e, 0, ln));
+  };
+  auto aoff = [&](int s, int i) { return A_KC ? abase[s] + i * 4096 : abase[i] + s * 16 * OA::RB; };
+  auto boff = [&](int s, int j) { return B_KC ? bbase[s] + j * 4096 : bbase[j] + s * 16 * OB::RB; };
 
   f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   uint4 af[2][FM], bfr[2][FN];
   // fragments are read in the order the MFMAs consume them: a0, b0 .. b(FN-1), a1 .. a(FM-1)
   auto read_a = [&](const char* st, int s, int buf, int i) {
-    const char* q = st + aoff[s][i];
+    const char* q = st + aoff(s, i);
     if (A_KC) {
       af[buf][i] = *reinterpret_cast<const uint4*>(q);
     } else {
@@ -783,7 +850,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
     }
   };
   auto read_b = [&](const char* st, int s, int buf, int j) {
-    const char* q = st + boff[s][j];
+    const char* q = st + boff(s, j);
     if (B_KC) {
       bfr[buf][j] = *reinterpret_cast<const uint4*>(q);
     } else {
@@ -798,12 +865,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
 #pragma unroll
     for (int i = 1; i < FM; ++i) read_a(st, s, buf, i);
   };
-  auto issue = [&](int t) {
+  // every wave's share of K-tile t of the tile at (tm0, tn0) from k offset kb
+  auto issue = [&](int t, int tm0, int tn0, int kb, int ke) {
     const uint32_t st = lds0 + (uint32_t)((t & 1) * SS);
 #pragma unroll
-    for (int u = 0; u < OA::PER_WAVE; ++u) oa.load_one(u, ra, p.lda, m0, p.M, kbeg + t * kBK64, kend, st, wave);
+    for (int u = 0; u < OA::PER_WAVE; ++u) oa.load_one(u, ra, p.lda, tm0, p.M, kb + t * kBK64, ke, st, wave);
 #pragma unroll
-    for (int u = 0; u < OB::PER_WAVE; ++u) ob.load_one(u, rb, p.ldb, n0, p.N, kbeg + t * kBK64, kend, st + SA, wave);
+    for (int u = 0; u < OB::PER_WAVE; ++u) ob.load_one(u, rb, p.ldb, tn0, p.N, kb + t * kBK64, ke, st + SA, wave);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
@@ -829,88 +897,123 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
   // waves go round-robin over the 4 SIMDs), each issuing its own share and
   // that of wave + NW/2, so a wave stalled on a full address queue leaves the
   // other wave of its SIMD free to issue MFMAs (+1% on the layer's shapes).
-  OA oa2;
-  OB ob2;
-  oa2.init(wave + NW / 2, lane);
-  ob2.init(wave + NW / 2, lane);
   auto load_u = [&](int t, int u) {  // the u-th load of tile t: own A, own B, partner A, partner B
     const uint32_t st = lds0 + (uint32_t)((t & 1) * SS);
     const int k0 = kbeg + t * kBK64;
     constexpr int PA = OA::PER_WAVE, PB = OB::PER_WAVE;
+    constexpr int QA = NW / 2 * PA, QB = NW / 2 * PB;  // the partner's loads, as offsets of this wave's
     if (u < PA) oa.load_one(u, ra, p.lda, m0, p.M, k0, kend, st, wave);
     else if (u < PA + PB) ob.load_one(u - PA, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave);
-    else if (u < 2 * PA + PB) oa2.load_one(u - PA - PB, ra, p.lda, m0, p.M, k0, kend, st, wave + NW / 2);
-    else ob2.load_one(u - 2 * PA - PB, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave + NW / 2);
+    else if (u < 2 * PA + PB) oa.template load_one<QA>(u - PA - PB, ra, p.lda, m0, p.M, k0, kend, st, wave);
+    else ob.template load_one<QB>(u - 2 * PA - PB, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave);
   };
   constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // loads per tile per wave when every wave loads
   constexpr int NL2 = 2 * NL;                      // per loading wave in the loop
   const bool loader = wave < NW / 2;
 
-  // prologue: tiles 0 and 1 in flight, wait for tile 0
-  if (nk > 0) {
-    issue(0);
-    if (nk > 1) {
-      issue(1);
-      MTNLG_VMCNT(NL);
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-    __syncthreads();
-    read_frags(smem, 0, 0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* st = smem + (kt & 1) * SS;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      read_frags(st, s + 1, (s + 1) & 1);
-      mfmas(s & 1);
-      interleave();
-    }
-    // Substep 3: its fragments are in registers. Publish tile kt+1 (loaded
-    // since substep 3 of the previous tile) and free this stage; then the
-    // first reads of tile kt+1 and the loads of tile kt+2 into this stage are
-    // woven into the last MFMAs of tile kt.
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    Mfma<bf16_t>::run(af[1][0], bfr[1][0], acc[0][0]);
-    __builtin_amdgcn_sched_barrier(0);
-    // (after the last tile this reads a stale stage; the values are unused)
-    read_frags(smem + ((kt + 1) & 1) * SS, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool more = kt + 2 < nk;
-#pragma unroll
-    for (int idx = 1; idx < NM; ++idx) {
-      Mfma<bf16_t>::run(af[1][idx / FN], bfr[1][idx % FN], acc[idx / FN][idx % FN]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more && loader) {
-        // NL2 loads over MFMAs 1 .. NM-1
-        const int lo = (idx - 1) * NL2 / (NM - 1), hi = idx * NL2 / (NM - 1);
-#pragma unroll
-        for (int u = lo; u < hi; ++u) load_u(kt + 2, u);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  constexpr int SROW = TN + 4;
-  static_assert(NW * 32 * SROW * 4 <= 2 * SS, "epilogue staging exceeds the ring");
-  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
+  // K-tiles 0 and 1 of the first work item; later items have theirs issued
+  // before the previous item's epilogue.
+  lane_setup();
+  if (nk > 0) issue(0, m0, n0, kbeg, kend);
+  if (nk > 1) issue(1, m0, n0, kbeg, kend);
+  bool first = true;
+  float* const slab = reinterpret_cast<float*>(smem + 2 * SS) + wave * ESLAB;
   const int lrow = lane & 31, lg = lane >> 5;
+
+  for (;;) {
+    if (!first) lane_setup();
+    float* const pt = tw.split >= 0 ? p.part + ((int64_t)tw.split * p.tail_tiles + tw.tl) * BM * BN : nullptr;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    if (nk > 0) {
+      if (first && nk > 1) MTNLG_VMCNT(NL);              // tile 0 of the prologue landed
+      else __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): also the last epilogue's stores
+      __syncthreads();
+      read_frags(smem, 0, 0);
+    }
+    first = false;
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* st = smem + (kt & 1) * SS;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) stage[(8 * blk + 4 * lg + r) * SROW + j * 32 + lrow] = acc[i][j][blk * 4 + r];
+      for (int s = 0; s < 3; ++s) {
+        read_frags(st, s + 1, (s + 1) & 1);
+        mfmas(s & 1);
+        interleave();
+      }
+      // Substep 3: its fragments are in registers. Publish tile kt+1 (loaded
+      // since substep 3 of the previous tile) and free this stage; then the
+      // first reads of tile kt+1 and the loads of tile kt+2 into this stage are
+      // woven into the last MFMAs of tile kt.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      Mfma<bf16_t>::run(af[1][0], bfr[1][0], acc[0][0]);
+      __builtin_amdgcn_sched_barrier(0);
+      // (after the last tile this reads a stale stage; the values are unused)
+      read_frags(smem + ((kt + 1) & 1) * SS, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool more = kt + 2 < nk;
+#pragma unroll
+      for (int idx = 1; idx < NM; ++idx) {
+        Mfma<bf16_t>::run(af[1][idx / FN], bfr[1][idx % FN], acc[idx / FN][idx % FN]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more && loader) {
+          // NL2 loads over MFMAs 1 .. NM-1
+          const int lo = (idx - 1) * NL2 / (NM - 1), hi = idx * NL2 / (NM - 1);
+#pragma unroll
+          for (int u = lo; u < hi; ++u) load_u(kt + 2, u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // Every wave is done with the ring (its last reads waited, then a
+    // barrier): K-tiles 0 and 1 of the next work item go in flight now and
+    // land while this item's epilogue runs from the per-wave slabs.
+    const int wnext = w + (int)gridDim.x;
+    const bool has_next = wnext < total;
+    const int m0c = m0, n0c = n0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __syncthreads();
-    epilogue_slab<bf16_t, TN, SROW, BN>(p, stage, m0, n0, wm * TM + i * 32, wn * TN, lane, pt);
-    __syncthreads();
+    if (has_next) {
+      lane_setup();
+      tw = tile_work(p, wnext);
+      m0 = tw.tm * BM;
+      n0 = tw.tn * BN;
+      kbeg = tw.kbeg;
+      kend = tw.kend;
+      nk = (kend - kbeg + kBK64 - 1) / kBK64;
+      if (nk > 0) issue(0, m0, n0, kbeg, kend);
+      if (nk > 1) issue(1, m0, n0, kbeg, kend);
+    }
+
+    // Epilogue in 16-row slabs through this wave's private LDS slab (no
+    // workgroup barrier): column c of slab row r sits at c ^ (32 * ((r >> 2) & 1)),
+    // so the two row groups of one MFMA accumulator write disjoint banks.
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = 8 * b + 4 * lg + r;
+              slab[row * TN + ((j * 32 + lrow) ^ (32 * ((row >> 2) & 1)))] = acc[i][j][(2 * hh + b) * 4 + r];
+            }
+        epilogue_slab16<bf16_t, TN, BN>(p, slab, m0c, n0c, wm * TM + i * 32 + hh * 16, wn * TN, lane, pt);
+      }
+    }
+    if (!has_next) break;
+    w = wnext;
   }
 }
 
@@ -923,8 +1026,9 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(GemmArgs p) {
   if (gid >= (int64_t)p.tail_tiles * VPT) return;
   const int tl = (int)(gid / VPT), v = (int)(gid % VPT);
   const int rl = v / (BN / 8), cl = (v % (BN / 8)) * 8;
-  const TileWork tw = tile_work(p, p.nfull + tl);  // split 0 of tail tile tl
-  const int row = tw.tm * BM + rl, col = tw.tn * BN + cl;
+  int tm, tn;
+  tile_pos(p, p.nfull + tl, tm, tn);
+  const int row = tm * BM + rl, col = tn * BN + cl;
   if (row >= p.M || col >= p.N) return;
   float s[8];
   const float* base = p.part + (int64_t)tl * BM * BN + (int64_t)rl * BN + cl;
@@ -947,8 +1051,10 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
 
 template <int BM, int BN, bool AK, bool BKc>
 hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
-  dim3 grid(a.nfull + a.tail_tiles * a.tail_split);
-    if (BM >= 256) {  // 64-deep K tiles, 8 waves (2 x 4, 128 x 64 each)
+  const int total = a.nfull + a.tail_tiles * a.tail_split;
+  dim3 grid(total);
+  if constexpr (BM >= 256) {  // 64-deep K tiles, 8 waves (2 x 4, 128 x 64 each); persistent, one workgroup per CU
+    grid.x = std::min(total, kPersistentGrid);
     hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<BM, BN, AK, BKc, 2, 4>), grid, dim3(512), 0, st, a);
   } else {           // 32-deep K tiles, 4 waves (2 x 2)
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc, 2, 2>), grid, dim3(256), 0, st, a);
