@@ -36,6 +36,11 @@ int stream_grid(int64_t units, int64_t max_blocks = 256 * 8) {
 // more bytes in flight; the norm and update passes use non-temporal accesses
 // (measured faster there, slower for the accumulation).
 constexpr int64_t kOptBlocks = 256 * 128;
+// Streams that write no per-workgroup partials launch one thread per vector
+// group (each thread's loop runs once): on MI355X that streams 10-25% faster
+// than a grid-stride loop over a few thousand workgroups (measured: copy
+// 6.5 vs 5.1 TB/s, the update's 4-read/4-write mix 5.6 vs 5.0 TB/s).
+constexpr int64_t kOneShotBlocks = int64_t(1) << 30;
 typedef float nf4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 ld_nt(const float4* p) {
   const nf4_t v = __builtin_nontemporal_load(reinterpret_cast<const nf4_t*>(p));
@@ -454,7 +459,7 @@ int acc_grid(int64_t n) { return stream_grid(n / 16 + 1, kOptBlocks); }
 
 hipError_t grad_accumulate(int64_t n, int dtype, const void* grad, float* acc, bool overwrite, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  const int grid = acc_grid(n);
+  const int grid = stream_grid(n / 16 + 1, kOneShotBlocks);
   if (dtype == kBF16)
     hipLaunchKernelGGL((grad_acc_kernel<bf16_t, false>), dim3(grid), dim3(kStreamThreads), 0, st, n,
                        static_cast<const bf16_t*>(grad), acc, (int)overwrite, 1.0f, nullptr, nullptr);
@@ -491,7 +496,7 @@ hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, flo
                      c.max_grad_norm, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n == 0) return e;
-  const int grid = stream_grid(n / 8 + 1, kOptBlocks);
+  const int grid = stream_grid(n / 8 + 1, kOneShotBlocks);
   hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
                      static_cast<bf16_t*>(w_bf16), stats);
   return hipGetLastError();
