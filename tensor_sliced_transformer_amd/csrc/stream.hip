@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, con
   const int64_t units = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 2;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x;
-  double sq = 0.0;
+  double sq2[2] = {0.0, 0.0};  // one fp64 sum per unit slot: shorter dependency chains
   int bad = 0;
   for (int64_t u0 = t0; u0 < units; u0 += stride) {
     float v[2][8], a[2][8];
@@ -226,16 +226,19 @@ __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, con
         }
         store8(acc + u * 8, v[k]);
         if (NORM) {
+          double q[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float t = v[k][e] * s;
             bad |= !isfinite(t);
-            sq += (double)t * t;
+            q[e] = (double)t * t;
           }
+          sq2[k] += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
         }
       }
     }
   }
+  double sq = sq2[0] + sq2[1];
   const int64_t s1 = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = units * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += s1) {
     const float v = Elem<T>::to_f(g[i]);
@@ -269,22 +272,26 @@ __global__ __launch_bounds__(kStreamThreads) void adam_norm_kernel(int64_t n, co
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n4 = n / 4;
-  double acc = 0.0;
+  // four 16-byte loads in flight per thread and two independent fp64 sums
+  // (a fixed order, so the result is deterministic)
+  constexpr int U = 4;
+  double acc2[2] = {0.0, 0.0};
   int bad = 0;
-  for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x; u0 < n4; u0 += 2 * stride) {
-    float4 g[2];
+  for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x; u0 < n4; u0 += U * stride) {
+    float4 g[U];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < U; ++k) {
       const int64_t u = u0 + (int64_t)k * blockDim.x;
       g[k] = u < n4 ? ld_nt(reinterpret_cast<const float4*>(grad) + u) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < U; ++k) {
       const float a = g[k].x * s, b = g[k].y * s, c = g[k].z * s, d = g[k].w * s;
       bad |= !isfinite(a) | !isfinite(b) | !isfinite(c) | !isfinite(d);
-      acc += (double)a * a + (double)b * b + (double)c * c + (double)d * d;
+      acc2[k & 1] += ((double)a * a + (double)b * b) + ((double)c * c + (double)d * d);
     }
   }
+  double acc = acc2[0] + acc2[1];
   for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
     const float a = grad[i] * s;
     bad |= !isfinite(a);
@@ -398,7 +405,7 @@ hipError_t reduce_partials(int dtype, int64_t rows, int64_t cols, const void* co
   if (total == 0) return hipSuccess;
   PartialPtrs pp{};
   for (int j = 0; j < n; ++j) pp.p[j] = parts[j];
-  const int grid = stream_grid(total / 8);
+  const int grid = stream_grid(total / 8, kOneShotBlocks);
   if (dtype == kBF16)
     hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, pp, n, total, cols,
                        static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(bias),
@@ -429,7 +436,7 @@ hipError_t reduce_partials_dropout(int dtype, int64_t rows, int64_t cols, const 
   PartialPtrs pp{};
   for (int j = 0; j < n; ++j) pp.p[j] = parts[j];
   const DropoutArgs d = dropout_args(seed, site, thr);
-  const int grid = stream_grid((total + 15) / 16);
+  const int grid = stream_grid((total + 15) / 16, kOneShotBlocks);
   if (dtype == kBF16)
     hipLaunchKernelGGL(reduce_dropout_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, pp, n, total, cols,
                        static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(bias),
@@ -445,7 +452,7 @@ hipError_t dropout_bwd(int dtype, int64_t total, const void* dy, void* dz, uint6
                        uint32_t thr, hipStream_t st) {
   if (total == 0) return hipSuccess;
   const DropoutArgs d = dropout_args(seed, site, thr);
-  const int grid = stream_grid((total + 15) / 16);
+  const int grid = stream_grid((total + 15) / 16, kOneShotBlocks);
   if (dtype == kBF16)
     hipLaunchKernelGGL(dropout_bwd_kernel<bf16_t>, dim3(grid), dim3(kStreamThreads), 0, st, total,
                        static_cast<const bf16_t*>(dy), static_cast<bf16_t*>(dz), d);
