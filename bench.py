@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -532,15 +533,17 @@ def component_bench(torch, tst, dev, T, h, heads, head_dim, reps=20):
         return (torch.randn(*shape, device=dev, generator=gen) * scale).to(bf)
 
     def timed(fn):
+        # median of per-launch event intervals: one stall of the GPU (seen once
+        # at 36 ms) must not stand in for the kernel's time
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
             fn()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
 
     x, gy, part = rn(T, h), rn(T, h), rn(T, h)
     gamma, beta, bias = rn(h, scale=0.02), rn(h, scale=0.02), rn(h, scale=0.02)
