@@ -82,6 +82,26 @@ def test_gemm_large_tiles_layouts_short_and_ragged_k(ta, tb, M, N, K):
     assert_close("C", to_np(c), A @ B + bias.astype(np.float64)[None, :], "bf16")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(4096, 8192, 64), (4104, 8200, 136)])
+def test_gemm_persistent_several_items_per_workgroup(ta, tb, M, N, K):
+    """The persistent 256x256-tile kernel with two or three work items per
+    workgroup (512 tiles; 17 x 33 = 561 ragged tiles): each item's first K
+    tiles are loaded while the previous item's epilogue runs, and every item
+    starts from zeroed accumulators and its own per-lane offsets."""
+    print(f"gemm persistent ta={ta} tb={tb} {M}x{N}x{K}", flush=True)
+    a = inputs(27, (K, M) if ta else (M, K), "bf16")
+    b = inputs(28, (N, K) if tb else (K, N), "bf16")
+    bias = inputs(29, (N,), "bf16")
+    c = empty((M, N), "bf16")
+    ws = empty_bytes(tst.gemm_workspace_bytes(tst.BF16, M, N, K))
+    tst.gemm(to_gpu(a, "bf16"), to_gpu(b, "bf16"), c, bool(ta), bool(tb), bias=to_gpu(bias, "bf16"), ws=ws)
+    torch.cuda.synchronize()
+    A = a.astype(np.float64).T if ta else a.astype(np.float64)
+    B = b.astype(np.float64).T if tb else b.astype(np.float64)
+    assert_close("C", to_np(c), A @ B + bias.astype(np.float64)[None, :], "bf16")
+
+
 # ------------------------------------------------------------------ LayerNorm
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rows,cols", [(64, 256), (37, 4096), (9, 20480), (5, 264)])
