@@ -22,7 +22,7 @@ Also measured in the same run:
     for the roofline of the GEMM kernel;
   * the float64 CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam] [--no-recompute] [--no-stage] [--no-components]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-adam] [--no-recompute] [--no-stage] [--no-layers] [--no-components]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--adam-reps", type=int, default=5)
     ap.add_argument("--no-recompute", action="store_true")
     ap.add_argument("--no-stage", action="store_true")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the GPT-style h4096 layer and the full MT-NLG layer as 8 slices")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the LayerNorm / partial-sum / attention kernels timed alone")
     ap.add_argument("--no-clock", action="store_true", help="skip the amdsmi clock and power sample")
@@ -250,6 +252,13 @@ def main():
         result["stage"] = stage_bench(torch, tst, dev, args.stage_steps, 1, flops, False)
         result["stage_recompute"] = stage_bench(torch, tst, dev, args.stage_steps, 1, flops, True)
 
+    if not args.no_layers:
+        torch.cuda.empty_cache()
+        result["gpt_layer_h4096"] = layer_bench(torch, tst, dev, 2, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        result["full_layer_8_slices_b4"] = layer_bench(torch, tst, dev, 5, 3, 1)
+        torch.cuda.empty_cache()
+
     if not args.no_components:
         result["components"] = component_bench(torch, tst, dev, T, h, w.local_heads, w.head_dim)
 
@@ -376,6 +385,89 @@ def shard_fwd_flops(tokens, hidden, heads_local, head_dim, ffn_local, seq, batch
     pairs = seq * (seq + 1) / 2.0 if causal else float(seq) * seq
     attn = 4.0 * batch * heads_local * head_dim * pairs
     return gemm + attn
+
+
+def layer_bench(torch, tst, dev, wi, steps, warmup):
+    """A layer (or one slice of it) as a step over its slices in turn: the
+    forward of every slice's attention half, their partials summed with the
+    bias and residual, the same for the MLP half, then the backward of the MLP
+    halves and of the attention halves, each followed by the sum of the slices'
+    input-gradient partials; the slices' LayerNorm gradients are summed too.
+    Weights and inputs are drawn on the GPU with the workload's distributions
+    (seeded; throughput does not depend on their values)."""
+    from synth.inputs import WORKLOADS, half_param_shapes
+    w = WORKLOADS[wi]
+    T, h = w.tokens, w.hidden
+    log(f"layer workload {w.name}: {len(w.slices)} slice(s), {T} tokens")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5000 + wi)
+    bf = torch.bfloat16
+
+    def rn(shape, std, mean=0.0):
+        return (torch.randn(shape, device=dev, generator=gen) * std + mean).to(bf)
+
+    def params(half):
+        return {k: rn(shp, 0.02, 1.0 if k == "ln_g" else 0.0) for k, shp in half_param_shapes(w, half).items()}
+
+    descs = [tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, i, tst.BF16, 1e-5) for i in w.slices]
+    pa = [params("attn") for _ in w.slices]
+    pm = [params("mlp") for _ in w.slices]
+    for p in pa[1:]:  # LayerNorm parameters and the row-sliced bias are replicated across slices
+        for k in ("ln_g", "ln_b", "b_out"):
+            p[k] = pa[0][k]
+    for p in pm[1:]:
+        for k in ("ln_g", "ln_b", "b_out"):
+            p[k] = pm[0][k]
+    pa_call = [{k: v for k, v in p.items() if k != "b_out"} for p in pa]
+    pm_call = [{k: v for k, v in p.items() if k != "b_out"} for p in pm]
+    ga = [{k: torch.empty_like(v) for k, v in p.items()} for p in pa]
+    gm = [{k: torch.empty_like(v) for k, v in p.items()} for p in pm]
+    d0 = descs[0]
+    sav_a = [torch.empty(tst.saved_bytes(d0, tst.ATTN), dtype=torch.uint8, device=dev) for _ in w.slices]
+    sav_m = [torch.empty(tst.saved_bytes(d0, tst.MLP), dtype=torch.uint8, device=dev) for _ in w.slices]
+    ws = torch.empty(max(tst.workspace_bytes(d0, tst.ATTN), tst.workspace_bytes(d0, tst.MLP)),
+                     dtype=torch.uint8, device=dev)
+    x, g = rn((T, h), 1.0), rn((T, h), 1.0)
+    parts = [torch.empty((T, h), dtype=bf, device=dev) for _ in w.slices]
+    x1, out, g1, dx = (torch.empty((T, h), dtype=bf, device=dev) for _ in range(4))
+    lng = {k: torch.empty((1, h), dtype=bf, device=dev) for k in ("a_g", "a_b", "m_g", "m_b")}
+    n = len(w.slices)
+
+    def step():
+        for i in range(n):
+            tst.layer_fwd(descs[i], tst.ATTN, pa_call[i], x, parts[i], sav_a[i], ws)
+        tst.reduce_partials(parts, x1, residual=x, bias=pa[0]["b_out"])
+        for i in range(n):
+            tst.layer_fwd(descs[i], tst.MLP, pm_call[i], x1, parts[i], sav_m[i], ws)
+        tst.reduce_partials(parts, out, residual=x1, bias=pm[0]["b_out"])
+        for i in range(n):
+            tst.layer_bwd(descs[i], tst.MLP, pm_call[i], x1, sav_m[i], g, parts[i], gm[i], ws)
+        tst.reduce_partials(parts, g1, residual=g)
+        for i in range(n):
+            tst.layer_bwd(descs[i], tst.ATTN, pa_call[i], x, sav_a[i], g1, parts[i], ga[i], ws)
+        tst.reduce_partials(parts, dx, residual=g1)
+        if n > 1:
+            for key, gs, name in (("a_g", ga, "ln_g"), ("a_b", ga, "ln_b"), ("m_g", gm, "ln_g"), ("m_b", gm, "ln_b")):
+                tst.reduce_partials([q[name].view(1, h) for q in gs], lng[key])
+
+    flop = 3.0 * n * shard_fwd_flops(T, h, w.local_heads, w.head_dim, w.local_ffn, w.seq, w.batch)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        evs[i].record()
+        step()
+    evs[-1].record()
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    tf = flop / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms:.3f} ms per fwd+bwd step = {tf:.1f} TFLOP/s")
+    res = {"workload": w.name, "slices": n, "tokens": T, "hidden": h, "heads": w.heads, "ffn": w.ffn,
+           "steps": steps, "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+           "mfma_peak_frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_per_step": flop}
+    del pa, pm, pa_call, pm_call, ga, gm, sav_a, sav_m, ws, parts
+    return res
 
 
 def gemm_breakdown(torch, tst, dev, T, h, wl, fl, reps=10):
