@@ -31,10 +31,12 @@ int stream_grid(int64_t units, int64_t max_blocks = 256 * 8) {
   return (int)(b < 1 ? 1 : (b > max_blocks ? max_blocks : b));
 }
 
-// The optimizer streams (accumulation, norm, update) touch every byte once:
-// two vectors per thread per iteration and up to 128 workgroups per CU keep
-// more bytes in flight; the norm and update passes use non-temporal accesses
-// (measured faster there, slower for the accumulation).
+// The optimizer streams (accumulation, norm, update) touch every byte once.
+// The passes that leave one fp64 partial per workgroup (the norm, the
+// accumulation that also forms it) are capped at kOptBlocks workgroups, the
+// size of the partials in the optimizer workspace; the norm and update passes
+// use non-temporal accesses (measured faster there, slower for the
+// accumulation).
 constexpr int64_t kOptBlocks = 256 * 128;
 // Streams that write no per-workgroup partials launch one thread per vector
 // group (each thread's loop runs once): on MI355X that streams 10-25% faster
