@@ -80,7 +80,11 @@ typedef enum { MTNLG_ATTN = 0, MTNLG_MLP = 1 } mtnlg_half;
  * 0 <= tp_rank < tp_size; head_dim in {64, 128, 160} (bf16) or {64, 128}
  * (f32); hidden and ffn/tp_size multiples of 16; hidden <= 32768; seq a
  * multiple of 128; one sequence of the slice's QKV activations
- * (seq * 3 * hidden/tp_size elements) below 2 GiB; dtype F32 or BF16;
+ * (seq * 3 * hidden/tp_size elements) below 2 GiB; every GEMM operand of the
+ * slice below 2 GiB in bytes of dtype (batch*seq tokens x the widest of
+ * hidden, 3*hidden/tp_size and ffn/tp_size; hidden x the wider of
+ * 3*hidden/tp_size and ffn/tp_size), the range of the GEMM's 32-bit buffer
+ * offsets (bf16 at hidden 20480: at most 52428 tokens); dtype F32 or BF16;
  * ln_eps > 0 and finite. Violations return MTNLG_ERR_SHAPE, MTNLG_ERR_DTYPE
  * or MTNLG_ERR_ARG before any launch. */
 typedef struct {
@@ -349,7 +353,9 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
  * every linear of the layer runs on.
  *   trans_a = 0: A is [M, K] row-major; 1: A is stored [K, M] (op(A) = A^T).
  *   trans_b = 0: B is [K, N] row-major; 1: B is stored [N, K] (op(B) = B^T).
- *   bias nullable. M, N, K multiples of 8, each operand below 2 GiB.
+ *   bias nullable. M, N, K multiples of 8; each operand (A, B and C) below
+ *   2 GiB in bytes of dtype, else MTNLG_ERR_SHAPE (operands are addressed
+ *   through 32-bit buffer offsets).
  *   ws: mtnlg_gemm_workspace_bytes(...) bytes (fp32 partials of the tiles
  *   that are split along K to fill the last round of workgroups); may be NULL
  *   when that size is 0. */

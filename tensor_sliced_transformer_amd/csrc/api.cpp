@@ -58,7 +58,15 @@ int validate_desc(const mtnlg_layer_desc* desc, int32_t half, Dims* out) {
     return fail(MTNLG_ERR_SHAPE, "one sequence of the QKV activations must stay below 2 GiB");
   if (!(D.ln_eps > 0.0f) || !isfinite(D.ln_eps)) return fail(MTNLG_ERR_ARG, "ln_eps must be positive and finite");
   const int64_t T = (int64_t)D.batch * D.seq;
-  if (T * (int64_t)std::max(D.hidden, D.ffn) > (int64_t)1 << 40) return fail(MTNLG_ERR_SHAPE, "problem too large");
+  {
+    // every GEMM operand of the layer (activations T x width, weights) must
+    // stay below 2 GiB, the range of the GEMM's 32-bit buffer offsets
+    const int64_t eb = elem_bytes(D.dtype), lim = (int64_t)1 << 31;
+    const int64_t w3 = 3LL * (D.hidden / D.heads) * (D.heads / D.tp_size), fl = D.ffn / D.tp_size;
+    const int64_t widest = std::max<int64_t>(std::max<int64_t>(D.hidden, w3), fl);
+    if (T >= lim || T * widest * eb >= lim || (int64_t)D.hidden * std::max(w3, fl) * eb >= lim)
+      return fail(MTNLG_ERR_SHAPE, "every GEMM operand (tokens x width, hidden x width) must stay below 2 GiB");
+  }
   if (out) {
     out->T = T;
     out->h = D.hidden;
@@ -542,14 +550,16 @@ int mtnlg_adam_update(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float
   return MTNLG_OK;
 }
 
-static bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
-  // every operand must stay below 2 GiB (32-bit buffer offsets)
-  return M >= 8 && N >= 8 && K >= 8 && M % 8 == 0 && N % 8 == 0 && K % 8 == 0 && M * K < (1LL << 30) &&
-         K * N < (1LL << 30) && M * N < (1LL << 30);
+static bool gemm_shape_ok(int32_t dtype, int64_t M, int64_t N, int64_t K) {
+  // every operand must stay below 2 GiB: the kernels address operands through
+  // 32-bit buffer offsets and mark out-of-range elements with offset 2^31
+  const int64_t eb = elem_bytes(dtype), lim = (int64_t)1 << 31;
+  return M >= 8 && N >= 8 && K >= 8 && M % 8 == 0 && N % 8 == 0 && K % 8 == 0 && M < lim && N < lim && K < lim &&
+         M * K * eb < lim && K * N * eb < lim && M * N * eb < lim;
 }
 
 size_t mtnlg_gemm_workspace_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K) {
-  if ((dtype != MTNLG_F32 && dtype != MTNLG_BF16) || !gemm_shape_ok(M, N, K)) return 0;
+  if ((dtype != MTNLG_F32 && dtype != MTNLG_BF16) || !gemm_shape_ok(dtype, M, N, K)) return 0;
   return gemm_workspace_bytes(plan_gemm(dtype, M, N, K, true), M, N);
 }
 
@@ -557,7 +567,7 @@ int mtnlg_gemm(int32_t dtype, int32_t trans_a, int32_t trans_b, int64_t M, int64
                const void* B, void* C, const void* bias, void* ws, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   if (dtype != MTNLG_F32 && dtype != MTNLG_BF16) return fail(MTNLG_ERR_DTYPE, "dtype %d unsupported", dtype);
-  if (!gemm_shape_ok(M, N, K))
+  if (!gemm_shape_ok(dtype, M, N, K))
     return fail(MTNLG_ERR_SHAPE, "M, N, K must be positive multiples of 8 with operands below 2 GiB");
   CHECK_PTR(A);
   CHECK_PTR(B);

@@ -86,6 +86,8 @@ def test_saved_bytes_mtnlg_shard():
     (dict(seq=100), -2),
     (dict(ln_eps=0.0), -1),
     (dict(batch=0), -2),
+    (dict(batch=26), -2),            # 53248 tokens x hidden 20480 x 2 B >= 2 GiB (32-bit GEMM offsets)
+    (dict(dtype=_lib.F32, hidden=16384, heads=128, ffn=65536, batch=16), -2),   # 32768 x 16384 x 4 B = 2 GiB
 ])
 def test_invalid_descriptor_rejected(bad, status):
     L = lib()
@@ -95,6 +97,25 @@ def test_invalid_descriptor_rejected(bad, status):
     st = L.mtnlg_layer_fwd(ctypes.byref(d), _lib.ATTN, ctypes.byref(p), A, A, A, None, 0, None)
     assert st == status, L.mtnlg_last_error()
     assert L.mtnlg_last_error()
+
+
+def test_largest_layer_accepted():
+    """25 sequences of 2048 at hidden 20480 keep every GEMM operand of the slice below 2 GiB."""
+    L = lib()
+    d = desc(batch=25)
+    assert L.mtnlg_saved_bytes(ctypes.byref(d), _lib.ATTN) > 0
+    assert L.mtnlg_saved_bytes(ctypes.byref(d), _lib.MLP) > 0
+
+
+def test_gemm_operands_of_2_gib_rejected():
+    """The GEMM addresses operands through 32-bit buffer offsets: an operand of
+    2 GiB or more (counted in bytes of its dtype) is a shape error."""
+    L = lib()
+    assert L.mtnlg_gemm(_lib.F32, 0, 0, 65536, 256, 8192, A, A, A, None, None, 0, None) == -2    # A: 2 GiB fp32
+    assert L.mtnlg_gemm(_lib.BF16, 0, 0, 65536, 256, 16384, A, A, A, None, None, 0, None) == -2  # A: 2 GiB bf16
+    assert L.mtnlg_gemm(_lib.BF16, 0, 1, 256, 65536, 16384, A, A, A, None, None, 0, None) == -2  # B: 2 GiB
+    assert L.mtnlg_gemm(_lib.F32, 0, 0, 32768, 16384, 64, A, A, A, None, None, 0, None) == -2    # C: 2 GiB fp32
+    assert b"2 GiB" in L.mtnlg_last_error()
 
 
 def test_null_and_misaligned_pointers():

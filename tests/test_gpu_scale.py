@@ -22,6 +22,12 @@
   layer-level entry points: bit-identical outputs, input gradients,
   accumulator, master weights, bf16 weights and optimizer statistics.
 
+* The GEMM at its largest operand: A of 131064 x 8192 bf16 (2,147,352,576
+  bytes, just below the 2 GiB that 32-bit buffer offsets address), stored
+  K-contiguous and M-contiguous, times B of 8192 x 256: 512 tiles with a
+  ragged last tile row, two work items per workgroup; 64 seeded rows of C
+  (always the first and the last) against float64. Tolerance 2e-2.
+
 Inputs at these sizes are drawn with torch's seeded generator on the GPU
 (numpy would need minutes for 1.9e9 or 5e9 values), with the distributions of
 the other workloads: activations N(0,1), weights and biases N(0,0.02),
@@ -284,3 +290,28 @@ def test_stage_full_shard_matches_layer_calls():
                        ("master", res["master"], master2), ("w", res["w"], w2), ("stats", res["stats"], stats2)):
         assert torch.equal(a, b), name
     print(f"stage full shard: bit-identical; norm {res['stats'][0].item():.6g}", flush=True)
+
+
+@pytest.mark.parametrize("ta", [0, 1])
+def test_gemm_largest_operand(ta):
+    M, N, K = 131064, 256, 8192
+    assert M * K * 2 < 2 ** 31 <= (M + 256) * K * 2
+    print(f"gemm largest operand ta={ta} {M}x{N}x{K}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9100 + ta)
+    a = torch.randn((K, M) if ta else (M, K), device="cuda", generator=gen).to(torch.bfloat16)
+    b = (torch.randn((K, N), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    nws = tst.gemm_workspace_bytes(tst.BF16, M, N, K)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+    tst.gemm(a, b, c, bool(ta), False, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9200 + ta)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 62, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    a_rows = (a[:, idx].t() if ta else a[idx]).float().cpu().numpy().astype(np.float64)
+    ref = a_rows @ b.float().cpu().numpy().astype(np.float64)
+    got = c[idx].float().cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    print(f"  rel err {err:.2e} over {len(rows)} rows", flush=True)
+    assert err < 2e-2
