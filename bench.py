@@ -774,6 +774,33 @@ def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=2048):
     dta = time.perf_counter() - t1
     adam_gbs = 34.0 * nc / dta / 1e9
     log(f"cpu baseline adam: {dta:.2f}s for 2^22 parameters = {adam_gbs:.2f} GB/s")
+    # the tiny layer (hidden 256, 4 heads of 64, MLP 1024, 2 sequences of 128,
+    # its t = 2 slices in turn), fwd+bwd through the oracle on one BLAS thread
+    # and on all of them (best of 5 passes each)
+    from threadpoolctl import threadpool_limits
+    tsh = OL.LayerShape(batch=2, seq=128, hidden=256, heads=4, ffn=1024, tp=2)
+    trng = np.random.Generator(np.random.PCG64(1001))
+    tfull = {k: (1.0 if k.endswith("_g") else 0.0) + trng.standard_normal(shp) * 0.02
+             for k, shp in OL.full_param_shapes(tsh).items()}
+    tx, tg = trng.standard_normal((256, 256)), trng.standard_normal((256, 256))
+
+    def tiny_pass():
+        out, state = OL.layer_fwd(tsh, tx, tfull)
+        OL.layer_bwd(tsh, tg, tfull, state)
+
+    def best_of(k=5):
+        best = float("inf")
+        for _ in range(k):
+            t2 = time.perf_counter()
+            tiny_pass()
+            best = min(best, time.perf_counter() - t2)
+        return best
+
+    tiny_fl = 2 * 3.0 * shard_fwd_flops(256, 256, 2, 64, 512, 128, 2)
+    with threadpool_limits(limits=1):
+        t_one = best_of()
+    t_all = best_of()
+    log(f"cpu baseline tiny layer: {t_one * 1e3:.1f} ms on one thread, {t_all * 1e3:.1f} ms on {threads}")
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 oracle fwd+bwd of the same 1/8 slice on the first {sample_tokens} tokens "
                       f"of the workload, {reps} passes ({fl / 1e12:.3f} TFLOP), {dt:.1f} s",
@@ -781,7 +808,12 @@ def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=2048):
             "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
             "blas": [{k: i.get(k) for k in ("internal_api", "version", "num_threads")} for i in info],
             "adam": {"value": round(adam_gbs, 3), "unit": "GB/s", "sample": "float64 oracle Adam step over 2^22 "
-                     "parameters (34 B/param accounting)", "seconds": round(dta, 3)}}
+                     "parameters (34 B/param accounting)", "seconds": round(dta, 3)},
+            "tiny_layer": {"sample": "float64 oracle fwd+bwd of the tiny layer (hidden 256, 4 heads of 64, MLP 1024, "
+                           "2 x 128 tokens, 2 slices in turn; best of 5)", "flop": tiny_fl,
+                           "one_core_ms": round(t_one * 1e3, 3), "all_cores_ms": round(t_all * 1e3, 3),
+                           "one_core_gflops": round(tiny_fl / t_one / 1e9, 3),
+                           "all_cores_gflops": round(tiny_fl / t_all / 1e9, 3)}}
 
 
 def _cpu_model():
