@@ -659,7 +659,10 @@ def component_bench(torch, tst, dev, T, h, heads, head_dim, reps=20):
     bw("reduce_partials", timed(lambda: tst.reduce_partials([part], out, residual=x, bias=bias)),
        3 * tb, "one partial and the residual read, the sum written")
     wl = heads * head_dim
-    qkv = rn(T, 3 * wl, scale=2.9)
+    q32 = torch.randn(T, 3 * wl, device=dev, generator=gen) * 2.9
+    # the bf16 path's storage of the attention input: Q and K in fp16, V in bf16
+    qkv = torch.cat([q32[:, :2 * wl].to(torch.float16).view(bf), q32[:, 2 * wl:].to(bf)], dim=1).contiguous()
+    del q32
     o = torch.empty(T, wl, dtype=bf, device=dev)
     lse = torch.empty(heads, T, dtype=torch.float32, device=dev)
     do, dqkv = rn(T, wl), torch.empty_like(qkv)

@@ -115,7 +115,9 @@ typedef struct { void *ln_g, *ln_b, *w_in, *b_in, *w_out, *b_out; } mtnlg_half_g
  * reads for this descriptor and half; 0 if the descriptor is invalid.
  * Layout (each region starts on a 256-byte boundary, in this order):
  *   ATTN: ln_out [T, hidden] dtype | mean [T] f32 | rstd [T] f32 |
- *         qkv [T, 3w] dtype | o [T, w] dtype | lse [local heads, T] f32
+ *         qkv [T, 3w] (F32: f32; BF16: the Q and K columns [0, 2w) as IEEE
+ *         binary16, the V columns as bf16) | o [T, w] dtype |
+ *         lse [local heads, T] f32
  *   MLP:  ln_out [T, hidden] dtype | mean [T] f32 | rstd [T] f32 |
  *         u [T, f] dtype (pre-activation) | y [T, f] dtype (GeLU(u))
  * with T = batch*seq. lse is the natural log of the softmax normaliser of
@@ -126,7 +128,13 @@ size_t mtnlg_saved_bytes(const mtnlg_layer_desc* desc, int32_t half);
  * this descriptor and half (one size serves both); 0 if invalid. */
 size_t mtnlg_workspace_bytes(const mtnlg_layer_desc* desc, int32_t half);
 
-/* Forward of one slice of one half.
+/* Forward of one slice of one half. Defined by the Megatron example of the
+ * STRONGHOLD slide deck (slides 7-8): the half's first linear is split by
+ * columns (QKV by whole heads, MLP-up A by columns, Y_i = GeLU(X A_i)), its
+ * second by rows (W_o, MLP-down B: Z_i = Y_i B_i), so one slice runs
+ * LayerNorm, its column slice, attention over its heads or GeLU, and its row
+ * slice, whose output is the partial that operator g sums; the left-to-right
+ * decoder (Elamur summary, Summary) makes the attention causal.
  *   x          [T, hidden] dtype: the half's input (X for ATTN, X1 for MLP)
  *   y_partial  [T, hidden] dtype: this slice's row-parallel output WITHOUT
  *              bias or residual -- ATTN: Attn_i(LN1(x)) W_o,i;
@@ -139,7 +147,11 @@ int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
                     const void* x, void* y_partial, void* saved, void* ws, size_t ws_bytes,
                     void* stream);
 
-/* Backward of one slice of one half for L = <output, dy>.
+/* Backward of one slice of one half for L = <output, dy>. The conjugate
+ * operators of the STRONGHOLD slide deck (slides 7-8) fix what each slice
+ * receives and returns: g's backward is the identity, so every slice gets the
+ * same dy; f's backward is an all-reduce, so each slice returns its own
+ * input-gradient partial. The gradients are those of the forward above.
  *   x          the same input that was passed to layer_fwd (unchanged)
  *   saved      what layer_fwd wrote for the same x and params
  *   dy         [T, hidden] dtype: gradient of the half's output (g's
@@ -173,7 +185,10 @@ int mtnlg_layer_bwd_recompute(const mtnlg_layer_desc* desc, int32_t half, const 
                               void* ws, size_t ws_bytes, void* stream);
 
 /* out = residual + bias + sum_{j<n} partials[j], summed in fp32 and rounded
- * once (the g all-reduce, or f's backward, done locally on one device).
+ * once (the g all-reduce, or f's backward, done locally on one device). The
+ * sum of the row slices' partials is the layer output in the STRONGHOLD
+ * slide deck's Megatron example (slides 7-8: Z = sum_i Y_i B_i); the
+ * residual and the row-sliced bias are added here, once.
  *   partials   HOST array of n DEVICE pointers, each [rows, cols] dtype; 1 <= n <= 16
  *   residual   [rows, cols] dtype, nullable (treated as zero)
  *   bias       [cols] dtype, nullable
@@ -233,7 +248,10 @@ typedef struct {
 /* Scratch bytes mtnlg_adam_step needs for n parameters. */
 size_t mtnlg_adam_workspace_bytes(int64_t n);
 
-/* Fused mixed-precision Adam step over one GPU's flat share of n params:
+/* Fused mixed-precision Adam step over one GPU's flat share of n params, the
+ * fp32 master weights and two fp32 moments of the mixed-precision Adam that
+ * the Elamur summary (Key points) counts at about 20 bytes per parameter,
+ * with Adam as in its References (Kingma and Ba):
  *   g_hat = grad * inv_loss_scale; norm = ||g_hat||_2 over all n;
  *   found_inf = any non-finite g_hat; coef = max_norm / (norm + 1e-6) if
  *   that is below 1, else 1. If found_inf, NOTHING is written except
@@ -336,9 +354,13 @@ size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
  *           stream), the gradient of each layer of every micro-batch but the
  *           last is accumulated on it as soon as that layer's backward is
  *           done, overlapping the accumulation with the rest of the work;
- *           ordering between the two streams uses events the call creates and
- *           releases itself. Results are identical with and without it. All
- *           of the step's work is complete once `stream` has passed it.
+ *           ordering between the two streams uses 2 * layers events that
+ *           the library creates on first use and keeps, per calling thread
+ *           and device, until the process ends (a later call on the same
+ *           thread records them again; a stream wait refers to the record
+ *           made before it, so reuse does not change the ordering). Results are
+ *           identical with and without it. All of the step's work is
+ *           complete once `stream` has passed it.
  * n = mtnlg_stage_param_count(desc). All arguments are validated before
  * anything is enqueued; errors as the calls it makes (MTNLG_ERR_HIP also
  * when an event cannot be created). */
@@ -386,7 +408,13 @@ int mtnlg_layernorm_bwd(int32_t dtype, int64_t rows, int64_t cols, const void* g
  * keys 0..r of its own sequence (the left-to-right decoder of the MT-NLG
  * paper summary, Summary, and of the STRONGHOLD slides, slide 8).
  * Requires seq % 128 == 0, head_dim in {64, 128, 160} (bf16) or {64, 128}
- * (f32), and seq*3*heads*head_dim elements below 2 GiB. */
+ * (f32), and seq*3*heads*head_dim elements below 2 GiB.
+ * BF16: the Q and K columns of qkv hold IEEE binary16 values (the V columns
+ * bf16), as the layer's QKV product stores them: with scores of standard
+ * deviation near 8 (the MT-NLG slice at its initialisation) the softmax
+ * magnifies the rounding of Q and K, and binary16 carries three more
+ * fraction bits; |Q|, |K| must stay below 65504, binary16's largest finite
+ * value. S = Q K^T runs on the fp16 matrix cores; o, do_ and dqkv are bf16. */
 int mtnlg_attention_fwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads,
                         int32_t head_dim, const void* qkv, void* o, float* lse, void* stream);
 

@@ -244,15 +244,34 @@ def mlp_slice(sh: LayerShape, full: dict, i: int) -> dict:
 # The two halves of one slice (between g all-reduces)
 # --------------------------------------------------------------------------
 
-def attn_half_fwd(sh: LayerShape, x: np.ndarray, p: dict):
+def _keep(a: np.ndarray) -> np.ndarray:
+    return a
+
+
+def attn_half_fwd(sh: LayerShape, x: np.ndarray, p: dict, store=None, store_qk=None):
     """Attention half of slice i. Returns (partial, saved).
 
     partial = Attn_i(LN1(x)) W_o,i, without bias or residual: the operand of
     the forward all-reduce g.
+
+    store: None for the definition itself (every intermediate in float64).
+    Diagnostic mode: a rounding function (e.g. oracle.bf16.round_to_bf16)
+    applied to each tensor a mixed-precision run keeps between its steps --
+    LN1(x), QKV and the attention output O, the saved activations a bf16
+    library hands from its forward to its backward. The rest stays float64.
+    Comparing a GPU result with both modes separates the error that comes
+    from storing those tensors in bf16 from the error of the kernels.
+    store_qk, if given, rounds the Q and K columns of QKV instead of store
+    (a library may keep them in another 16-bit format).
     """
+    rnd = store or _keep
     y, mean, rstd, xhat = layernorm_fwd(x, p["ln_g"], p["ln_b"], sh.eps)
+    y = rnd(y)
     qkv = y @ p["w_in"] + p["b_in"][None, :]
+    qk = 2 * sh.local_width
+    qkv = np.concatenate([(store_qk or rnd)(qkv[:, :qk]), rnd(qkv[:, qk:])], axis=1)
     o, prob, lse = attention_fwd(qkv, sh.batch, sh.seq, sh.local_heads, sh.head_dim)
+    o = rnd(o)
     partial = o @ p["w_out"]
     saved = {"ln_out": y, "mean": mean, "rstd": rstd, "xhat": xhat,
              "qkv": qkv, "o": o, "p": prob, "lse": lse}
@@ -283,11 +302,19 @@ def attn_half_bwd(sh: LayerShape, g: np.ndarray, p: dict, saved: dict):
     return dx, grads, inter
 
 
-def mlp_half_fwd(sh: LayerShape, x1: np.ndarray, p: dict):
-    """MLP half of slice i: partial = GeLU(LN2(x1) A_i + a_i) B_i (no bias, no residual)."""
+def mlp_half_fwd(sh: LayerShape, x1: np.ndarray, p: dict, store=None):
+    """MLP half of slice i: partial = GeLU(LN2(x1) A_i + a_i) B_i (no bias, no residual).
+
+    store: as in attn_half_fwd; the kept tensors are LN2(x1), the
+    pre-activation U and Y = GeLU(U) (Y formed from the unrounded U, then
+    rounded, as a bias+GeLU epilogue does).
+    """
+    rnd = store or _keep
     y, mean, rstd, xhat = layernorm_fwd(x1, p["ln_g"], p["ln_b"], sh.eps)
+    y = rnd(y)
     u = y @ p["w_in"] + p["b_in"][None, :]
-    act = gelu(u)
+    act = rnd(gelu(u))
+    u = rnd(u)
     partial = act @ p["w_out"]
     saved = {"ln_out": y, "mean": mean, "rstd": rstd, "xhat": xhat, "u": u, "y": act}
     return partial, saved

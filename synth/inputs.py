@@ -19,7 +19,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["randn", "to_bf16_bits", "bf16_bits_to_f32", "round_f32_to_bf16",
+__all__ = ["randn", "to_bf16_bits", "bf16_bits_to_f32", "round_f32_to_bf16", "qkv_bits",
            "Workload", "WORKLOADS", "half_param_shapes", "make_half_params",
            "make_activation", "make_adam_state"]
 
@@ -59,6 +59,22 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 def round_f32_to_bf16(x: np.ndarray) -> np.ndarray:
     """float32 values rounded to bfloat16 (returned as float32)."""
     return bf16_bits_to_f32(to_bf16_bits(x))
+
+
+def qkv_bits(x: np.ndarray, qk_cols: int):
+    """The 16-bit storage of an attention input [T, 3w] in the library's bf16
+    path: the first qk_cols columns (Q and K) as IEEE binary16, the rest (V) as
+    bfloat16, both rounded to nearest even. Returns (values as float32, uint16
+    bit patterns)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    qk = x[:, :qk_cols].astype(np.float16)
+    vals = np.empty_like(x)
+    vals[:, :qk_cols] = qk.astype(np.float32)
+    vals[:, qk_cols:] = round_f32_to_bf16(x[:, qk_cols:])
+    bits = np.empty(x.shape, dtype=np.uint16)
+    bits[:, :qk_cols] = qk.view(np.uint16)
+    bits[:, qk_cols:] = to_bf16_bits(x[:, qk_cols:])
+    return vals, bits
 
 
 @dataclass(frozen=True)

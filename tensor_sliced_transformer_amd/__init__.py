@@ -72,6 +72,57 @@ def workspace_bytes(desc: LayerDesc, half: int) -> int:
     return int(load().mtnlg_workspace_bytes(ctypes.byref(desc), half))
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _expect(name, t, shape, dtype) -> None:
+    """Size checks on the host side of the boundary: the C ABI takes bare
+    pointers, so a tensor smaller than the descriptor implies would be written
+    past its end on the device."""
+    if t is None:
+        raise ValueError(f"{name} is None")
+    if tuple(t.shape) != tuple(shape) and t.numel() != _prod(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _prod(shape) -> int:
+    n = 1
+    for s in shape:
+        n *= int(s)
+    return n
+
+
+def _half_shapes(desc: LayerDesc, half: int) -> dict:
+    h = desc.hidden
+    if half == ATTN:
+        w = desc.heads // desc.tp_size * (desc.hidden // desc.heads)
+        win, wout = 3 * w, w
+    else:
+        win = wout = desc.ffn // desc.tp_size
+    return {"ln_g": (h,), "ln_b": (h,), "w_in": (h, win), "b_in": (win,), "w_out": (wout, h), "b_out": (h,)}
+
+
+def _check_half(desc, half, params=None, grads=None, acts=(), saved=None, ws=None, ws_need=None):
+    dt = torch_dtype(desc.dtype)
+    shapes = _half_shapes(desc, half)
+    if params is not None:
+        for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out"):
+            _expect(f"params[{k}]", params[k], shapes[k], dt)
+    if grads is not None:
+        for k, s in shapes.items():
+            _expect(f"grads[{k}]", grads[k], s, dt)
+    tok = (desc.batch * desc.seq, desc.hidden)
+    for name, t in acts:
+        _expect(name, t, tok, dt)
+    if saved is not None and _nbytes(saved) < saved_bytes(desc, half):
+        raise ValueError(f"saved: {_nbytes(saved)} bytes < {saved_bytes(desc, half)} required")
+    if ws_need is not None and (0 if ws is None else _nbytes(ws)) < ws_need:
+        raise ValueError(f"ws: {0 if ws is None else _nbytes(ws)} bytes < {ws_need} required")
+
+
 def _params(p: dict) -> HalfParams:
     return HalfParams(*(_ptr(p[k]) for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out")))
 
@@ -82,6 +133,7 @@ def _grads(g: dict) -> HalfGrads:
 
 def layer_fwd(desc, half, params: dict, x, y_partial, saved, ws=None, stream=None) -> None:
     """One slice's half forward (mtnlg_layer_fwd); params keys ln_g ln_b w_in b_in w_out."""
+    _check_half(desc, half, params=params, acts=(("x", x), ("y_partial", y_partial)), saved=saved)
     p = _params(params)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     check(load().mtnlg_layer_fwd(ctypes.byref(desc), half, ctypes.byref(p), _ptr(x), _ptr(y_partial),
@@ -90,6 +142,8 @@ def layer_fwd(desc, half, params: dict, x, y_partial, saved, ws=None, stream=Non
 
 def layer_bwd(desc, half, params: dict, x, saved, dy, dx_partial, grads: dict, ws, stream=None) -> None:
     """One slice's half backward (mtnlg_layer_bwd); grads keys ln_g ln_b w_in b_in w_out b_out."""
+    _check_half(desc, half, params=params, grads=grads, acts=(("x", x), ("dy", dy), ("dx_partial", dx_partial)),
+                saved=saved)
     p = _params(params)
     g = _grads(grads)
     check(load().mtnlg_layer_bwd(ctypes.byref(desc), half, ctypes.byref(p), _ptr(x), _ptr(saved), _ptr(dy),
@@ -104,6 +158,7 @@ def recompute_workspace_bytes(desc: LayerDesc, half: int) -> int:
 def layer_bwd_recompute(desc, half, params: dict, x, dy, dx_partial, grads: dict, ws, stream=None) -> None:
     """One slice's half backward that first recomputes its saved activations from x
     (mtnlg_layer_bwd_recompute); ws of recompute_workspace_bytes(desc, half) bytes."""
+    _check_half(desc, half, params=params, grads=grads, acts=(("x", x), ("dy", dy), ("dx_partial", dx_partial)))
     p = _params(params)
     g = _grads(grads)
     check(load().mtnlg_layer_bwd_recompute(ctypes.byref(desc), half, ctypes.byref(p), _ptr(x), _ptr(dy),
@@ -112,9 +167,20 @@ def layer_bwd_recompute(desc, half, params: dict, x, dy, dx_partial, grads: dict
           "mtnlg_layer_bwd_recompute")
 
 
+def _check_reduce(partials, out, residual, bias) -> None:
+    rows, cols = out.shape
+    for j, t in enumerate(partials):
+        _expect(f"partials[{j}]", t, (rows, cols), out.dtype)
+    if residual is not None:
+        _expect("residual", residual, (rows, cols), out.dtype)
+    if bias is not None:
+        _expect("bias", bias, (cols,), out.dtype)
+
+
 def reduce_partials(partials, out, residual=None, bias=None, stream=None) -> None:
     """out = residual + bias + sum(partials) (mtnlg_reduce_partials)."""
     rows, cols = out.shape
+    _check_reduce(partials, out, residual, bias)
     arr = (ctypes.c_void_p * len(partials))(*[p.data_ptr() for p in partials])
     for p in partials:
         _ptr(p)
@@ -126,6 +192,7 @@ def reduce_partials_dropout(partials, out, p: float, seed: int, site: int, resid
                             stream=None) -> None:
     """out = residual + keep * scale * (sum(partials) + bias) (mtnlg_reduce_partials_dropout)."""
     rows, cols = out.shape
+    _check_reduce(partials, out, residual, bias)
     arr = (ctypes.c_void_p * len(partials))(*[t.data_ptr() for t in partials])
     for t in partials:
         _ptr(t)

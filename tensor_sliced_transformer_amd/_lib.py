@@ -10,7 +10,9 @@ import os
 from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p, c_char_p, POINTER
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmtnlg.so")
+# MTNLG_LIBRARY may name another build of the same sources (the host-sanitizer
+# build that the host ABI tests run against); the default is the in-tree build.
+LIB_PATH = os.environ.get("MTNLG_LIBRARY") or os.path.join(HERE, "libmtnlg.so")
 
 MTNLG_OK = 0
 STATUS = {0: "MTNLG_OK", -1: "MTNLG_ERR_ARG", -2: "MTNLG_ERR_SHAPE", -3: "MTNLG_ERR_DTYPE",

@@ -70,12 +70,55 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+# Host-sanitizer build: the host-side sources (argument validation, layouts and
+# launch sequences) with AddressSanitizer and UndefinedBehaviorSanitizer on the
+# host pass only, linked with the ordinary device objects. The host ABI tests
+# run against it on the CPU (no kernel is launched there).
+HOST_SOURCES = ["api.cpp", "stage.cpp"]
+SAN_LIB = os.path.join(HERE, "libmtnlg_hostsan.so")
+SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-omit-frame-pointer -Xarch_host -fno-sanitize-recover=undefined").split()
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to preload into python)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the compiler's AddressSanitizer runtime was not found")
+    return path
+
+
+def build_host_sanitized() -> str:
+    """libmtnlg_hostsan.so: needs the device objects of build() in _build/."""
+    objs = []
+    for src in HOST_SOURCES:
+        out = os.path.join(BUILD, os.path.splitext(src)[0] + ".hostsan.o")
+        cmd = [hipcc(), "-x", "hip", *COMMON, "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(out)
+    dev = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    tmp = SAN_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *SAN_FLAGS[:4], "-Xarch_host", "-shared-libsan",
+           *objs, *dev, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--host-sanitized", action="store_true", help="also build libmtnlg_hostsan.so")
     a = ap.parse_args()
     print(build(a.jobs, a.verbose))
+    if a.host_sanitized:
+        print(build_host_sanitized())
 
 
 if __name__ == "__main__":

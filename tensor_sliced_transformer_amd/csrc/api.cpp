@@ -169,8 +169,11 @@ int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mt
     void* o = at(saved, L.b);
     float* lse = reinterpret_cast<float*>(at(saved, L.c));
     const int64_t n3 = 3 * d.w;
-    MTNLG_HIP(gemm(d.dtype, true, false, d.T, n3, d.h, ln_out, d.h, params->w_in, n3, qkv, n3, EPI_BIAS,
-                   params->b_in, nullptr, nullptr, plan_gemm(d.dtype, d.T, n3, d.h, true), gws, st),
+    // bf16: Q and K leave the product in fp16 (see the attention kernels)
+    const bool f16qk = d.dtype == MTNLG_BF16;
+    MTNLG_HIP(gemm(d.dtype, true, false, d.T, n3, d.h, ln_out, d.h, params->w_in, n3, qkv, n3,
+                   f16qk ? EPI_BIAS_F16LO : EPI_BIAS, params->b_in, nullptr, nullptr,
+                   plan_gemm(d.dtype, d.T, n3, d.h, true), gws, st, f16qk ? (int)(2 * d.w) : 0),
               "qkv gemm");
     MTNLG_HIP(attention_fwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, st),
               "attention_fwd");

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
     f32x16_t s;
     zero(s);
 #pragma unroll
-    for (int st = 0; st < SUB; ++st) s = mma(frag_row(sk, 32 * kh + lq, st, g), qf[st], s);
+    for (int st = 0; st < SUB; ++st) s = mma_f16(frag_row(sk, 32 * kh + lq, st, g), qf[st], s);
     if (kw0 == qw0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
     zero(dp);
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
-      s = mma(frag_row(sk, 32 * kh + lq, st, g), qf[st], s);
+      s = mma_f16(frag_row(sk, 32 * kh + lq, st, g), qf[st], s);
       dp = mma(frag_row(sv, 32 * kh + lq, st, g), df[st], dp);
     }
 #pragma unroll
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
     for (int t = 0; t < 2; ++t) {
       const bf16x8_t db = pack_slots(dp, t);
 #pragma unroll
-      for (int e = 0; e < EB; ++e) dq[e] = mma(frag_tr(sk, e, 32 * kh, t, lane), db, dq[e]);
+      for (int e = 0; e < EB; ++e) dq[e] = mma(f16_to_bf16(frag_tr(sk, e, 32 * kh, t, lane)), db, dq[e]);
     }
   });
 

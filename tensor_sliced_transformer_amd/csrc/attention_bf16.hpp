@@ -76,6 +76,28 @@ __device__ __forceinline__ f32x16_t mma(const bf16x8_t& a, const bf16x8_t& b, co
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Q and K are kept in IEEE binary16 (the QKV product writes them so): the
+// scores' softmax magnifies their rounding (at the MT-NLG slice the scores
+// have a standard deviation near 8), and fp16 carries three more fraction
+// bits than bf16. S = Q K^T runs on the fp16 MFMA; a fragment holds the 16-bit
+// patterns either way.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16_t mma_f16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+// An fp16 fragment (of Q or K) as bf16, round to nearest even, for the products
+// that pair it with bf16 data (dQ = dS K, dK = dS^T Q).
+__device__ __forceinline__ bf16x8_t f16_to_bf16(const bf16x8_t& x) {
+  const f16x8_t h = __builtin_bit_cast(f16x8_t, x);
+  uint4 u;
+  u.x = pack_bf16x2((float)h[0], (float)h[1]);
+  u.y = pack_bf16x2((float)h[2], (float)h[3]);
+  u.z = pack_bf16x2((float)h[4], (float)h[5]);
+  u.w = pack_bf16x2((float)h[6], (float)h[7]);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 __device__ __forceinline__ void zero(f32x16_t& a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) a[i] = 0.0f;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
     zero(dp);
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
-      s = mma(frag_row(sq, 32 * qh + lq, st, g), kf[st], s);
+      s = mma_f16(frag_row(sq, 32 * qh + lq, st, g), kf[st], s);
       dp = mma(frag_row(so, 32 * qh + lq, st, g), vf[st], dp);
     }
 #pragma unroll
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
         dv[e] = mma(frag_tr(so, e, 32 * qh, t, lane), pb, dv[e]);
-        dk[e] = mma(frag_tr(sq, e, 32 * qh, t, lane), db, dk[e]);
+        dk[e] = mma(f16_to_bf16(frag_tr(sq, e, 32 * qh, t, lane)), db, dk[e]);
       }
     }
   });

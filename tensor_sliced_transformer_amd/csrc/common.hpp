@@ -69,6 +69,20 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* v) {
   u.w = pack_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = u;
 }
+// 8 floats -> 8 IEEE binary16 values, round to nearest even.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+__device__ __forceinline__ void store8_f16(uint16_t* p, const float* v) {
+  uint4 u;
+  u.x = pack_f16x2(v[0], v[1]);
+  u.y = pack_f16x2(v[2], v[3]);
+  u.z = pack_f16x2(v[4], v[5]);
+  u.w = pack_f16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
 __device__ __forceinline__ void store8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);

@@ -35,6 +35,9 @@
 //   * The 256x256 kernel is persistent (one workgroup per CU looping over work
 //     items): the first two K tiles of its next item are loaded while the
 //     current item's epilogue runs from a private 16-row LDS slab per wave.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,9 +48,7 @@ namespace {
 constexpr int kCH = 8;        // 16-byte chunks per LDS row
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
-// Workgroups of the persistent 256x256 kernel: one per CU of MI355X (a
-// multiple of the 8 XCDs, so a workgroup's items all map to its own XCD).
-constexpr int kPersistentGrid = 256;
+constexpr int kXcds = 8;  // MI355X: work-group ids go round-robin over 8 XCDs
 
 __device__ __forceinline__ float gelu_f(float u) {
   return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
@@ -198,6 +199,15 @@ __device__ __forceinline__ void apply_epi_store(const GemmArgs& p, int row, int 
       store8(static_cast<T*>(p.C) + off, v);
       break;
     }
+    case EPI_BIAS_F16LO: {
+      float b8[8];
+      load8(static_cast<const T*>(p.bias) + col, b8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += b8[e];
+      if (col < p.f16_cols) store8_f16(reinterpret_cast<uint16_t*>(static_cast<T*>(p.C) + off), v);
+      else store8(static_cast<T*>(p.C) + off, v);
+      break;
+    }
     default:
       store8(static_cast<T*>(p.C) + off, v);
   }
@@ -235,7 +245,7 @@ __device__ __forceinline__ void epilogue_slab(const GemmArgs& p, const float* st
 template <typename T, int WN, int BN>
 __device__ __forceinline__ void epilogue_slab16(const GemmArgs& p, const float* slab, int m0, int n0, int rl0,
                                                 int cl0, int lane, float* pt) {
-  static_assert(WN == 64, "slab swizzle assumes two 32-column halves");
+  static_assert(WN % 64 == 0, "slab swizzle assumes pairs of 32-column halves");
   constexpr int VPR = WN / 8;
 #pragma unroll 1
   for (int u = lane; u < 16 * VPR; u += kWave) {
@@ -766,20 +776,22 @@ struct Dtl64 {
       for (int e = 0; e < 2; ++e) cpar[e] = 8 * (slot ^ (4 * (2 * e + lane / 32)));
     }
   }
+  // byte offset in the operand of load u (+ QOFF) of the K-tile at k0 (kOob outside it)
+  template <int QOFF = 0>
+  __device__ __forceinline__ uint32_t goff(int u, int64_t ld, int rb0, int rmax, int k0, int kend) const {
+    const int r = r0 + (u + QOFF) * STEP, c = cpar[u & 1];
+    if (KC) {
+      const int m = rb0 + r, k = k0 + c;
+      return (m < rmax && k < kend) ? (uint32_t)(((int64_t)m * ld + k) * 2) : kOob;
+    }
+    const int k = k0 + r, m = rb0 + c;
+    return (m < rmax && k < kend) ? (uint32_t)(((int64_t)k * ld + m) * 2) : kOob;
+  }
   // issue load u (+ QOFF, an even count of loads of other waves) of the K-tile at k0 into the stage at dst
   template <int QOFF = 0>
   __device__ __forceinline__ void load_one(int u, i32x4_t rs, int64_t ld, int rb0, int rmax, int k0, int kend,
                                            uint32_t dst, int wave) const {
-    const int r = r0 + (u + QOFF) * STEP, c = cpar[u & 1];
-    uint32_t off;
-    if (KC) {
-      const int m = rb0 + r, k = k0 + c;
-      off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)m * ld + k) * 2) : kOob;
-    } else {
-      const int k = k0 + r, m = rb0 + c;
-      off = (m < rmax && k < kend) ? (uint32_t)(((int64_t)k * ld + m) * 2) : kOob;
-    }
-    dtl16_at(rs, dst + (uint32_t)(wave * PER_WAVE + u + QOFF) * 1024u, off);
+    dtl16_at(rs, dst + (uint32_t)(wave * PER_WAVE + u + QOFF) * 1024u, goff<QOFF>(u, ld, rb0, rmax, k0, kend));
   }
 };
 
@@ -1053,8 +1065,8 @@ template <int BM, int BN, bool AK, bool BKc>
 hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
   const int total = a.nfull + a.tail_tiles * a.tail_split;
   dim3 grid(total);
-  if constexpr (BM >= 256) {  // 64-deep K tiles, 8 waves (2 x 4, 128 x 64 each); persistent, one workgroup per CU
-    grid.x = std::min(total, kPersistentGrid);
+  if constexpr (BM >= 256) {  // 64-deep K tiles; persistent, one workgroup per CU
+    grid.x = std::min(total, persistent_grid());
     hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<BM, BN, AK, BKc, 2, 4>), grid, dim3(512), 0, st, a);
   } else {           // 32-deep K tiles, 4 waves (2 x 2)
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc, 2, 2>), grid, dim3(256), 0, st, a);
@@ -1082,9 +1094,28 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int persistent_grid() { return std::max(kXcds, device_cus() / kXcds * kXcds); }
+
 GemmPlan plan_gemm(int dtype, int64_t M, int64_t N, int64_t K, bool allow_split) {
   GemmPlan pl;
-  const int num_cu = 256;
+  const int num_cu = persistent_grid();
   if (dtype == kBF16) {
     const int64_t big = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int kt_big = ceil_div(K, kBK64);
@@ -1128,8 +1159,9 @@ size_t gemm_workspace_bytes(const GemmPlan& pl, int64_t, int64_t) {
 hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int epi,
                 const void* bias, void* C2, const void* aux, const GemmPlan& pl, void* ws,
-                hipStream_t st) {
+                hipStream_t st, int f16_cols) {
   GemmArgs a{};
+  a.f16_cols = f16_cols;
   a.A = A; a.B = B; a.C = C;
   a.M = (int)M; a.N = (int)N; a.K = (int)K;
   a.lda = lda; a.ldb = ldb; a.ldc = ldc;

@@ -12,12 +12,21 @@ constexpr int kBF16 = 1;
 
 inline size_t elem_bytes(int dtype) { return dtype == kBF16 ? 2 : 4; }
 
+// Compute units of the current device (queried once per device and kept;
+// 256 on MI355X). Used to size the GEMM's rounds of work and its persistent
+// grid; 256 when no device can be queried (host-only size queries).
+int device_cus();
+// The persistent GEMM grid: the CU count rounded down to a multiple of the 8
+// XCDs, so that every work item of a workgroup maps to the XCD it runs on.
+int persistent_grid();
+
 // ---------------------------------------------------------------- GEMM
 enum GemmEpi {
   EPI_STORE = 0,       // C = acc
   EPI_BIAS = 1,        // C = acc + bias[n]
   EPI_BIAS_GELU = 2,   // C = u = acc + bias[n]; C2 = GeLU(u)
-  EPI_GELU_GRAD = 3    // C = acc * GeLU'(aux[m, n])
+  EPI_GELU_GRAD = 3,   // C = acc * GeLU'(aux[m, n])
+  EPI_BIAS_F16LO = 4   // C = acc + bias[n]; columns n < f16_cols stored as fp16, the rest as bf16
 };
 
 struct GemmArgs {
@@ -38,6 +47,7 @@ struct GemmArgs {
   // passes through the epilogue.
   int nfull, tail_tiles, tail_split, k_chunk;
   float* part;
+  int f16_cols;  // EPI_BIAS_F16LO: the leading columns kept in fp16 (a multiple of 8)
 };
 
 struct GemmPlan {
@@ -52,7 +62,7 @@ size_t gemm_workspace_bytes(const GemmPlan& pl, int64_t M, int64_t N);
 hipError_t gemm(int dtype, bool a_kc, bool b_kc, int64_t M, int64_t N, int64_t K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int epi,
                 const void* bias, void* C2, const void* aux, const GemmPlan& pl, void* ws,
-                hipStream_t st);
+                hipStream_t st, int f16_cols = 0);
 
 // ---------------------------------------------------------------- LayerNorm
 hipError_t layernorm_fwd(int dtype, int64_t rows, int64_t cols, const void* x, const void* gamma,

@@ -104,23 +104,34 @@ StageWs stage_ws(const mtnlg_stage_desc* sd, const StageDims& d, int64_t n) {
   return w;
 }
 
-// Events of one stage step, released when the step's work is enqueued (the
-// runtime frees an event whose last record is still pending once it completes).
-struct EventSet {
-  std::vector<hipEvent_t> e;
-  hipError_t create(int count) {
-    for (int i = 0; i < count; ++i) {
-      hipEvent_t ev;
-      const hipError_t r = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+// Events that order the stage step's two streams, created on first use and
+// kept, per thread and device, until the process ends: a step records and
+// waits on them in issue order, and a later step on the same thread records
+// them again (a stream wait refers to the record made before it, so the reuse
+// is safe). Only a step with more layers than any before it on this thread
+// and device creates events; the others allocate nothing on the host.
+constexpr int kMaxDevices = 64;
+struct EventPool {
+  std::vector<hipEvent_t> ev[kMaxDevices];
+  // 2 * layers events of the current device: [0, layers) "backward done",
+  // [layers, 2 * layers) "accumulation done"
+  hipError_t get(int layers, hipEvent_t** out) {
+    int dev = 0;
+    hipError_t r = hipGetDevice(&dev);
+    if (r != hipSuccess) return r;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::vector<hipEvent_t>& v = ev[dev];
+    while (v.size() < (size_t)(2 * layers)) {
+      hipEvent_t e;
+      r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
       if (r != hipSuccess) return r;
-      e.push_back(ev);
+      v.push_back(e);
     }
+    *out = v.data();
     return hipSuccess;
   }
-  ~EventSet() {
-    for (hipEvent_t ev : e) (void)hipEventDestroy(ev);
-  }
 };
+thread_local EventPool t_events;
 
 #define STAGE_CALL(call)          \
   do {                            \
@@ -182,11 +193,10 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
   const int nl = desc->layers, mb = desc->micro_batches;
   hipStream_t S = static_cast<hipStream_t>(stream), A = static_cast<hipStream_t>(aux_stream);
   const bool overlap = A != nullptr && A != S && mb > 1;
-  EventSet bwd_done, acc_done;
-  if (overlap) {
-    MTNLG_HIP(bwd_done.create(nl), "hipEventCreateWithFlags");
-    MTNLG_HIP(acc_done.create(nl), "hipEventCreateWithFlags");
-  }
+  hipEvent_t* events = nullptr;
+  if (overlap) MTNLG_HIP(t_events.get(nl, &events), "hipEventCreateWithFlags");
+  hipEvent_t* const bwd_done = events;
+  hipEvent_t* const acc_done = events ? events + nl : nullptr;
 
   const mtnlg_layer_desc* L = &desc->layer;
   const size_t act = (size_t)d.act * 2;
@@ -242,7 +252,7 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
       layer_offsets(d, l, o);
       // layer l's gradient buffer is rewritten below: the previous micro-batch's
       // accumulation of it must be done
-      if (overlap && k > 0) MTNLG_HIP(hipStreamWaitEvent(S, acc_done.e[l], 0), "hipStreamWaitEvent");
+      if (overlap && k > 0) MTNLG_HIP(hipStreamWaitEvent(S, acc_done[l], 0), "hipStreamWaitEvent");
       const void* in[2] = {xin(l, k), mid(l)};
       for (int half = 1; half >= 0; --half) {
         const int64_t* t = o[half];
@@ -269,10 +279,10 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
       }
       if (overlap && k + 1 < mb) {
         const int64_t lo = (int64_t)l * d.per_layer;
-        MTNLG_HIP(hipEventRecord(bwd_done.e[l], S), "hipEventRecord");
-        MTNLG_HIP(hipStreamWaitEvent(A, bwd_done.e[l], 0), "hipStreamWaitEvent");
+        MTNLG_HIP(hipEventRecord(bwd_done[l], S), "hipEventRecord");
+        MTNLG_HIP(hipStreamWaitEvent(A, bwd_done[l], 0), "hipStreamWaitEvent");
         STAGE_CALL(mtnlg_grad_accumulate(d.per_layer, MTNLG_BF16, gb + 2 * lo, acc + lo, k == 0, A));
-        MTNLG_HIP(hipEventRecord(acc_done.e[l], A), "hipEventRecord");
+        MTNLG_HIP(hipEventRecord(acc_done[l], A), "hipEventRecord");
       }
     }
     const bool first = k == 0;

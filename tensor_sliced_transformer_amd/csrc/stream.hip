@@ -512,16 +512,26 @@ hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, flo
 }
 }  // namespace
 
-hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
-                     void* w_bf16, float* stats, void* ws, hipStream_t st) {
-  double* part = static_cast<double*>(ws);
-  int* flag = reinterpret_cast<int*>(part + kOptBlocks);
+namespace {
+// (1) + (2) + (3) with the norm partials in `part` and `flag` (at least
+// kNormBlocks entries each)
+hipError_t adam_step_parts(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                           void* w_bf16, float* stats, double* part, int* flag, hipStream_t st) {
   const int nb = n == 0 ? 1 : std::min<int>(kNormBlocks, stream_grid(n / 8 + 1, kNormBlocks));
   hipLaunchKernelGGL(adam_norm_kernel, dim3(nb), dim3(kStreamThreads), 0, st, n, grad, c.inv_loss_scale, part,
                      flag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return finish_and_update(c, n, master, m, v, grad, w_bf16, stats, part, flag, nb, st);
+}
+
+}  // namespace
+
+hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                     void* w_bf16, float* stats, void* ws, hipStream_t st) {
+  double* part = static_cast<double*>(ws);
+  return adam_step_parts(c, n, master, m, v, grad, w_bf16, stats, part, reinterpret_cast<int*>(part + kOptBlocks),
+                         st);
 }
 
 hipError_t adam_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,

@@ -62,3 +62,10 @@ def assert_bf16_copy(w_gpu, master_gpu, rw, rp):
     assert np.array_equal(w_gpu, round_f32_to_bf16(master_gpu.astype(np.float32)).astype(np.float64))
     allow = np.abs(rw) * 2.0 ** -7 + 2.0 * np.abs(master_gpu - rp) + 1e-38
     assert np.all(np.abs(w_gpu - rw) <= allow)
+
+
+def round_to_f16(a):
+    """Nearest IEEE binary16 value of each element (ties to even), as float64:
+    the storage of Q and K in the library's bf16 path (numpy's conversion)."""
+    return np.asarray(a, dtype=np.float64).astype(np.float16).astype(np.float64)
+

@@ -185,7 +185,10 @@ def test_gemm_and_attention_write_inside_their_buffers(M, N, K, ta, tb):
     bufs = {"c": c, "gemm_ws": ws}
     if M == 2048:
         B, S, H, D = 1, 2048, 16, 160
-        qkv = (torch.randn((B * S, 3 * H * D), device="cuda", generator=gen) * 2.9).to(torch.bfloat16)
+        qkv32 = torch.randn((B * S, 3 * H * D), device="cuda", generator=gen) * 2.9
+        # Q and K in fp16, V in bf16 (the bf16 path's storage of the attention input)
+        qkv = torch.cat([qkv32[:, :2 * H * D].to(torch.float16).view(torch.bfloat16),
+                         qkv32[:, 2 * H * D:].to(torch.bfloat16)], dim=1).contiguous()
         do = torch.randn((B * S, H * D), device="cuda", generator=gen).to(torch.bfloat16)
         o = Guarded((B * S, H * D), torch.bfloat16)
         lse = Guarded((H, B * S), torch.float32)

@@ -348,3 +348,51 @@ def test_layernorm_bwd_finite_differences():
         bp = bet.copy(); bp[j] += delta
         bm = bet.copy(); bm[j] -= delta
         assert abs((f(x, gam, bp) - f(x, gam, bm)) / (2 * delta) - db[j]) < 1e-8
+
+
+# --------------------------------------------------------------------------
+# diagnostic mode: the tensors a bf16 library keeps between its steps rounded
+# --------------------------------------------------------------------------
+
+def _diag_setup():
+    sh = L.LayerShape(batch=2, seq=8, hidden=32, heads=4, ffn=64, tp=2)
+    full = make_full(sh, seed=40, scale=0.3)
+    x = rng(41).standard_normal((sh.tokens, sh.hidden))
+    return sh, full, x
+
+
+def test_diagnostic_mode_identity_store_is_the_definition():
+    sh, full, x = _diag_setup()
+    for fwd, sl in ((L.attn_half_fwd, L.attn_slice), (L.mlp_half_fwd, L.mlp_slice)):
+        p = sl(sh, full, 1)
+        a, sa = fwd(sh, x, p)
+        b, sb = fwd(sh, x, p, store=lambda t: t)
+        assert np.array_equal(a, b)
+        for k in sa:
+            assert np.array_equal(sa[k], sb[k]), k
+
+
+def test_diagnostic_mode_rounds_only_the_kept_tensors():
+    """With bf16 rounding, LN output, QKV, O (attention) and LN output, U, Y
+    (MLP) are bf16 values; the LayerNorm statistics are not rounded; Y is the
+    rounding of GeLU of the unrounded U; and the partial moves away from the
+    definition by no more than a few bf16 half-ulps carried through two
+    products (well below 2^-4 relative), but does move."""
+    from oracle.bf16 import round_to_bf16
+    sh, full, x = _diag_setup()
+    for fwd, sl, kept in ((L.attn_half_fwd, L.attn_slice, ("ln_out", "qkv", "o")),
+                          (L.mlp_half_fwd, L.mlp_slice, ("ln_out", "u", "y"))):
+        p = sl(sh, full, 0)
+        exact, se = fwd(sh, x, p)
+        diag, sd = fwd(sh, x, p, store=round_to_bf16)
+        for k in kept:
+            assert np.array_equal(round_to_bf16(sd[k]), sd[k]), k
+            assert not np.array_equal(sd[k], se[k]), k
+            assert rel(sd[k], se[k]) <= 2.0 ** -8 * 4, k
+        assert np.array_equal(sd["rstd"], se["rstd"]) and np.array_equal(sd["mean"], se["mean"])
+        assert not np.array_equal(round_to_bf16(sd["rstd"]), sd["rstd"])
+        if "u" in kept:
+            u_exact = sd["ln_out"] @ p["w_in"] + p["b_in"][None, :]
+            assert np.array_equal(sd["y"], round_to_bf16(L.gelu(u_exact)))
+        e = rel(diag, exact)
+        assert 0.0 < e < 2.0 ** -4, e
