@@ -267,6 +267,25 @@ int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* 
                     const float* grad, void* w_bf16, float* stats, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* mtnlg_adam_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and result, bit for bit, with no workspace argument. The
+ * norm pass's per-workgroup partials go to the library's own static scratch
+ * of mtnlg_adam_static_scratch_bytes() bytes (96 KiB: one fp64 partial and
+ * one flag for each of at most 8192 norm workgroups; every n fits, as the
+ * norm pass never launches more), one copy per GPU, held until the process
+ * ends. Its device address is looked up once per device, on the first call
+ * with that device current. Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race and give wrong results; calls on one stream are ordered.
+ * Nothing in the scratch needs to start at zero (every partial the finish
+ * reads is written first by the same call). The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine). Arguments,
+ * semantics and errors as mtnlg_adam_step without ws and ws_bytes. */
+size_t mtnlg_adam_static_scratch_bytes(void);
+int mtnlg_adam_step_noalloc(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v,
+                            const float* grad, void* w_bf16, float* stats, void* stream);
+
 /* The optimizer's norm pass folded into the last micro-batch's accumulation
  * (Elamur summary, Key points: micro-batch gradient accumulation; the norm and
  * clip are this library's reading): one pass does

@@ -17,7 +17,8 @@ from ._lib import ATTN, MLP, BF16, F32, AdamCfg, HalfGrads, HalfParams, LayerDes
 
 __all__ = ["ATTN", "MLP", "BF16", "F32", "LayerDesc", "AdamCfg", "MtnlgError", "load", "make_desc",
            "saved_bytes", "workspace_bytes", "layer_fwd", "layer_bwd", "reduce_partials",
-           "grad_accumulate", "adam_workspace_bytes", "adam_step", "grad_accumulate_norm", "adam_update",
+           "grad_accumulate", "adam_workspace_bytes", "adam_step", "adam_static_scratch_bytes", "adam_step_noalloc",
+           "grad_accumulate_norm", "adam_update",
            "reduce_partials_dropout", "dropout_bwd",
            "recompute_workspace_bytes", "layer_bwd_recompute", "StageDesc", "make_stage_desc",
            "stage_param_count", "stage_param_offsets", "stage_workspace_bytes", "stage_step", "gemm", "gemm_workspace_bytes", "layernorm_fwd",
@@ -223,6 +224,18 @@ def adam_step(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None) 
     check(load().mtnlg_adam_step(ctypes.byref(cfg), master.numel(), _ptr(master), _ptr(m), _ptr(v), _ptr(grad),
                                  _ptr(w_bf16), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "mtnlg_adam_step")
+
+
+def adam_static_scratch_bytes() -> int:
+    return int(load().mtnlg_adam_static_scratch_bytes())
+
+
+def adam_step_noalloc(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, stream=None) -> None:
+    """adam_step with its scratch in the library's static per-GPU buffer
+    (mtnlg_adam_step_noalloc): allocates nothing; overlapping calls on one GPU race."""
+    check(load().mtnlg_adam_step_noalloc(ctypes.byref(cfg), master.numel(), _ptr(master), _ptr(m), _ptr(v),
+                                         _ptr(grad), _ptr(w_bf16), _ptr(stats), _stream(stream)),
+          "mtnlg_adam_step_noalloc")
 
 
 def grad_accumulate_norm(grad, acc, overwrite: bool, inv_loss_scale: float, ws, stream=None) -> None:

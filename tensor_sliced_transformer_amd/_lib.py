@@ -71,6 +71,9 @@ SIGNATURES = {
     "mtnlg_adam_workspace_bytes": (c_size_t, [c_int64]),
     "mtnlg_adam_step": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mtnlg_adam_static_scratch_bytes": (c_size_t, []),
+    "mtnlg_adam_step_noalloc": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_void_p]),
     "mtnlg_grad_accumulate_norm": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                                              c_size_t, c_void_p]),
     "mtnlg_adam_update": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -52,7 +52,9 @@ inline int check_ptr(const void* p, const char* name) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Validates an Adam step's arguments (cfg ranges, pointers, workspace size for
-// n parameters) and fills the device scalars; MTNLG_OK or a failure status.
+// n parameters; no workspace check when ws is kNoWorkspace) and fills the
+// device scalars; MTNLG_OK or a failure status.
+inline const void* const kNoWorkspace = reinterpret_cast<const void*>(~uintptr_t(0));
 int adam_args(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
               void* w_bf16, float* stats, const void* ws, size_t ws_bytes, AdamScalars* c);
 

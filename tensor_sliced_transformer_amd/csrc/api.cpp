@@ -495,9 +495,11 @@ int adam_args(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, flo
   CHECK_PTR(v);
   CHECK_PTR(grad);
   CHECK_PTR(stats);
-  CHECK_PTR(ws);
+  if (ws != kNoWorkspace) {
+    CHECK_PTR(ws);
+    if (ws_bytes < adam_ws(n)) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, adam_ws(n));
+  }
   if (w_bf16) CHECK_PTR(w_bf16);
-  if (ws_bytes < adam_ws(n)) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, adam_ws(n));
   c->lr = cfg->lr;
   c->beta1 = cfg->beta1;
   c->beta2 = cfg->beta2;
@@ -521,6 +523,19 @@ int mtnlg_adam_step(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* 
   const int s = adam_args(cfg, n, master, m, v, grad, w_bf16, stats, ws, ws_bytes, &c);
   if (s != MTNLG_OK) return s;
   MTNLG_HIP(adam_step(c, n, master, m, v, grad, w_bf16, stats, ws, static_cast<hipStream_t>(stream)), "adam_step");
+  return MTNLG_OK;
+}
+
+size_t mtnlg_adam_static_scratch_bytes(void) { return adam_static_scratch_bytes(); }
+
+int mtnlg_adam_step_noalloc(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v,
+                            const float* grad, void* w_bf16, float* stats, void* stream) {
+  g_last_error[0] = 0;
+  AdamScalars c{};
+  const int s = adam_args(cfg, n, master, m, v, grad, w_bf16, stats, kNoWorkspace, 0, &c);
+  if (s != MTNLG_OK) return s;
+  MTNLG_HIP(adam_step_static(c, n, master, m, v, grad, w_bf16, stats, static_cast<hipStream_t>(stream)),
+            "adam_step_static");
   return MTNLG_OK;
 }
 

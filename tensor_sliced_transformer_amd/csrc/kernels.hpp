@@ -111,6 +111,12 @@ struct AdamScalars {
 };
 hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v,
                      const float* grad, void* w_bf16, float* stats, void* ws, hipStream_t st);
+// adam_step with its norm partials in the library's static per-device scratch
+// (adam_static_scratch_bytes() bytes) instead of a caller workspace: nothing is
+// allocated; calls that overlap on one device share that scratch.
+size_t adam_static_scratch_bytes();
+hipError_t adam_step_static(const AdamScalars& c, int64_t n, float* master, float* m, float* v,
+                            const float* grad, void* w_bf16, float* stats, hipStream_t st);
 // The accumulation that also leaves the norm partials in ws (adam_ws bytes),
 // and the Adam step that takes them from there instead of its own norm pass.
 hipError_t grad_accumulate_norm(int64_t n, int dtype, const void* grad, float* acc, bool overwrite,

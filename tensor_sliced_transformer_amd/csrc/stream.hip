@@ -17,6 +17,9 @@
 //   then adam_update runs (2) and (3)).
 // Grid-stride loops over 16-byte vectors; all pointers are 16-byte aligned
 // (checked on the host) and the ragged tail is done per element.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -525,12 +528,53 @@ hipError_t adam_step_parts(const AdamScalars& c, int64_t n, float* master, float
   return finish_and_update(c, n, master, m, v, grad, w_bf16, stats, part, flag, nb, st);
 }
 
+// The optimizer scratch of adam_step_static: one fp64 partial and one flag
+// per norm workgroup (96 KiB), in the library's own device memory, one copy
+// per GPU, held until the process ends. Host code must not use this name as
+// an address (it is a host-side stand-in): kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kNormBlocks * (sizeof(double) + sizeof(int))];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up on first use.
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 }  // namespace
+
+size_t adam_static_scratch_bytes() { return sizeof(scratch); }
 
 hipError_t adam_step(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
                      void* w_bf16, float* stats, void* ws, hipStream_t st) {
   double* part = static_cast<double*>(ws);
   return adam_step_parts(c, n, master, m, v, grad, w_bf16, stats, part, reinterpret_cast<int*>(part + kOptBlocks),
+                         st);
+}
+
+hipError_t adam_step_static(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+                            void* w_bf16, float* stats, hipStream_t st) {
+  void* p = nullptr;
+  const hipError_t e = scratch_ptr(&p);
+  if (e != hipSuccess) return e;
+  double* part = static_cast<double*>(p);
+  return adam_step_parts(c, n, master, m, v, grad, w_bf16, stats, part, reinterpret_cast<int*>(part + kNormBlocks),
                          st);
 }
 
