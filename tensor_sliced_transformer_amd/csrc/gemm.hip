@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
 //   while the current item's epilogue runs from per-wave slabs beside the
 //   ring.
 // ---------------------------------------------------------------------------
-template <int WM, int WN, bool A_KC, bool B_KC>
+template <int WM, int WN, bool A_KC, bool B_KC, bool FULLK>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) {
   constexpr int BM = 256, BN = 256, NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -1129,11 +1129,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
 #pragma unroll
     for (int i = 1; i < FM; ++i) read_a(st, s, buf, i);
   };
-  // global load u of K tile t of the current work item into staging register u
+  // global load u of K tile t of the current work item into staging register u.
+  // FULLK (every K tile of every item is whole, K % 64 == 0): the lane's offset
+  // of tile 0 is kept per item and tile t adds t times the tile's byte step as
+  // the instruction's scalar offset, so a load costs no vector arithmetic; past
+  // the item's last tile a resource of zero bytes makes every load return zero.
+  // Otherwise every load computes its offset with the K bound (kOob past it).
+  uint32_t voff[FULLK ? NL : 1];
+  const uint32_t kstep_a = A_KC ? 2u * kBK64 : (uint32_t)(2 * kBK64 * p.lda);
+  const uint32_t kstep_b = B_KC ? 2u * kBK64 : (uint32_t)(2 * kBK64 * p.ldb);
+  const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(p.A, 0u), rb0 = make_rsrc(p.B, 0u);
+  auto item_offsets = [&]() {
+    if constexpr (FULLK) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u)
+        voff[u] = u < PA ? oa.goff(u, p.lda, m0, p.M, kbeg, kend) : ob.goff(u - PA, p.ldb, n0, p.N, kbeg, kend);
+    }
+  };
   auto gload = [&](int u, int t) {
-    const int k0 = kbeg + t * kBK64;
-    if (u < PA) stg[u] = buf_load16(ra, oa.goff(u, p.lda, m0, p.M, k0, kend));
-    else stg[u] = buf_load16(rb, ob.goff(u - PA, p.ldb, n0, p.N, k0, kend));
+    if constexpr (FULLK) {
+      const bool in = t < nk;
+      if (u < PA)
+        stg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(in ? ra : ra0, voff[u],
+                                                                                 (uint32_t)t * kstep_a, 0));
+      else
+        stg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(in ? rb : rb0, voff[u],
+                                                                                 (uint32_t)t * kstep_b, 0));
+    } else {
+      const int k0 = kbeg + t * kBK64;
+      if (u < PA) stg[u] = buf_load16(ra, oa.goff(u, p.lda, m0, p.M, k0, kend));
+      else stg[u] = buf_load16(rb, ob.goff(u - PA, p.ldb, n0, p.N, k0, kend));
+    }
   };
   // staging register u into LDS stage `stage`, where the direct-to-LDS kernel's
   // load u of this wave would have put it
@@ -1152,6 +1178,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
 
   // first work item: tile 0 into stage 0, tile 1 into the staging registers
   lane_setup();
+  item_offsets();
 #pragma unroll
   for (int u = 0; u < NL; ++u) gload(u, 0);
 #pragma unroll
@@ -1234,6 +1261,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
       kbeg = tw.kbeg;
       kend = tw.kend;
       nk = (kend - kbeg + kBK64 - 1) / kBK64;
+      item_offsets();
 #pragma unroll
       for (int u = 0; u < NL; ++u) gload(u, 0);
     }
@@ -1307,9 +1335,15 @@ hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
     // when both are M/N-contiguous (the weight-gradient products, where the
     // staging writes share the LDS with twice as many transposing reads and
     // measured 2-4.5% slower).
-    if constexpr (AK || BKc)
-      hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc>), grid, dim3(512), 0, st, a);
-    else
+    // Whole K tiles everywhere (K and the pieces' K range multiples of 64) let
+    // the loads use scalar offsets (+1-4% measured).
+    const bool fullk = a.K % kBK64 == 0 && a.k_chunk % kBK64 == 0;
+    if constexpr (AK || BKc) {
+      if (fullk)
+        hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, true>), grid, dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, false>), grid, dim3(512), 0, st, a);
+    } else
       hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<BM, BN, AK, BKc, 2, 4>), grid, dim3(512), 0, st, a);
   } else {           // 32-deep K tiles, 4 waves (2 x 2)
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc, 2, 2>), grid, dim3(256), 0, st, a);

@@ -361,34 +361,21 @@ __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n4 = n / 4;
-  for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * 2 + threadIdx.x; u0 < n4; u0 += 2 * stride) {
-    float4 p[2], mm[2], vv[2], g[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t u = u0 + (int64_t)k * blockDim.x;
-      if (u < n4) {
-        p[k] = ld_nt(reinterpret_cast<const float4*>(master) + u);
-        mm[k] = ld_nt(reinterpret_cast<const float4*>(m) + u);
-        vv[k] = ld_nt(reinterpret_cast<const float4*>(v) + u);
-        g[k] = ld_nt(reinterpret_cast<const float4*>(grad) + u);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int64_t u = u0 + (int64_t)k * blockDim.x;
-      if (u < n4) {
-        adam_one(p[k].x, mm[k].x, vv[k].x, g[k].x * gs, c);
-        adam_one(p[k].y, mm[k].y, vv[k].y, g[k].y * gs, c);
-        adam_one(p[k].z, mm[k].z, vv[k].z, g[k].z * gs, c);
-        adam_one(p[k].w, mm[k].w, vv[k].w, g[k].w * gs, c);
-        st_nt(reinterpret_cast<float4*>(master) + u, p[k]);
-        st_nt(reinterpret_cast<float4*>(m) + u, mm[k]);
-        st_nt(reinterpret_cast<float4*>(v) + u, vv[k]);
-        if (w)
-          st_nt(reinterpret_cast<uint2*>(w) + u,
-                make_uint2(pack_bf16x2(p[k].x, p[k].y), pack_bf16x2(p[k].z, p[k].w)));
-      }
-    }
+  // one 16-byte group of each stream per thread (the launch covers n/4 threads):
+  // measured faster than two groups per thread (5.8 vs 5.4 TB/s at 1.9e9)
+  for (int64_t u = t0; u < n4; u += stride) {
+    float4 p = ld_nt(reinterpret_cast<const float4*>(master) + u);
+    float4 mm = ld_nt(reinterpret_cast<const float4*>(m) + u);
+    float4 vv = ld_nt(reinterpret_cast<const float4*>(v) + u);
+    const float4 g = ld_nt(reinterpret_cast<const float4*>(grad) + u);
+    adam_one(p.x, mm.x, vv.x, g.x * gs, c);
+    adam_one(p.y, mm.y, vv.y, g.y * gs, c);
+    adam_one(p.z, mm.z, vv.z, g.z * gs, c);
+    adam_one(p.w, mm.w, vv.w, g.w * gs, c);
+    st_nt(reinterpret_cast<float4*>(master) + u, p);
+    st_nt(reinterpret_cast<float4*>(m) + u, mm);
+    st_nt(reinterpret_cast<float4*>(v) + u, vv);
+    if (w) st_nt(reinterpret_cast<uint2*>(w) + u, make_uint2(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w)));
   }
   for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
     float p = master[i], mm = m[i], vv = v[i];
@@ -508,7 +495,7 @@ hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, flo
                      c.max_grad_norm, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n == 0) return e;
-  const int grid = stream_grid(n / 8 + 1, kOneShotBlocks);
+  const int grid = stream_grid(n / 4 + 1, kOneShotBlocks);
   hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
                      static_cast<bf16_t*>(w_bf16), stats);
   return hipGetLastError();
