@@ -275,6 +275,9 @@ def main():
         "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic_bytes(),
         "traffic_unit": "bytes per launch (average over the 12 launches)",
+        "traffic_source": "profiles/gemm_traffic.json: two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) "
+                          "over the same 12 launches, scaled by a plain copy's readings; recorded with the "
+                          "sha256 of gemm.hip and reported as null when the source has changed since",
         "algorithmic_bytes": sum(2 * (r["M"] * r["K"] + r["K"] * r["N"] + r["M"] * r["N"])
                                  for r in gemm_rows) / len(gemm_rows),
         "launches": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in gemm_rows]}
@@ -477,12 +480,18 @@ def gemm_breakdown(torch, tst, dev, T, h, wl, fl, reps=10):
               ("mlp_down", T, h, fl, 0, 0), ("mlp_dY", T, fl, h, 0, 1), ("mlp_dB", fl, h, T, 1, 0),
               ("mlp_dA", h, fl, T, 1, 0), ("mlp_dX", T, h, fl, 0, 1), ("attn_dO", T, wl, h, 0, 1),
               ("attn_dWo", wl, h, T, 1, 0), ("attn_dWqkv", h, 3 * wl, T, 1, 0), ("attn_dX", T, h, 3 * wl, 0, 1)]
+    # operand distributions of the step (MFMA power, and with it the clock,
+    # depends on the data): the B operand is a weight, N(0, 0.02), in the
+    # forward and input-gradient products; both operands are activations or
+    # gradients, N(0, 1), in the weight-gradient products
+    weight_b = {"qkv", "out_proj", "mlp_up", "mlp_down", "mlp_dY", "mlp_dX", "attn_dO", "attn_dX"}
     rows = []
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
     for name, M, N, K, ta, tb in shapes:
         a = torch.randn((K, M) if ta else (M, K), device=dev, generator=gen).to(torch.bfloat16)
-        b = torch.randn((N, K) if tb else (K, N), device=dev, generator=gen).to(torch.bfloat16)
+        b = torch.randn((N, K) if tb else (K, N), device=dev, generator=gen)
+        b = (b * 0.02 if name in weight_b else b).to(torch.bfloat16)
         c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(tst.gemm_workspace_bytes(tst.BF16, M, N, K), 16), dtype=torch.uint8, device=dev)
         for _ in range(2):
@@ -604,7 +613,8 @@ def adam_bench(torch, tst, dev, reps):
                           "hbm_frac": round(copy_gbs / PEAK_HBM_GBS, 4),
                           "step_vs_copy": round(step_gbs / copy_gbs, 4),
                           "accumulate_vs_copy": round(acc_gbs / copy_gbs, 4),
-                          "note": "torch copy_ of 2 GiB fp32 (read + write counted)"}
+                          "note": "torch's copy_ of 2 GiB fp32 (read + write counted), for context only: "
+                                  "it is not the memory system's ceiling (hand-written streams copy faster)"}
     log(f"plain device copy: {copy_gbs:.0f} GB/s; Adam step at {100 * step_gbs / copy_gbs:.0f}% of it, "
         f"accumulation at {100 * acc_gbs / copy_gbs:.0f}%")
     del src, dst
@@ -762,12 +772,59 @@ def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=2048):
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     log(f"cpu baseline {dt:.1f}s, {fl / dt / 1e12:.3f} TFLOP/s on {threads} threads")
 
-    # the oracle's optimizer step on a 2^22-element chunk of the same workload, as
+    # the GPT-style layer (hidden 4096, 32 heads of 128, MLP 16384, 2048 tokens,
+    # one slice) in full: both halves forward and backward
+    from synth.inputs import WORKLOADS, make_activation, make_half_params
+    w2 = WORKLOADS[2]
+    sh2 = OL.LayerShape(batch=1, seq=w2.seq, hidden=w2.hidden, heads=w2.heads, ffn=w2.ffn, tp=1)
+    pa2 = {k: v.astype(np.float64) for k, v in make_half_params(w2, "attn", 0).items()}
+    pm2 = {k: v.astype(np.float64) for k, v in make_half_params(w2, "mlp", 0).items()}
+    x2 = make_activation(w2, 1).astype(np.float64)
+    g2 = make_activation(w2, 2).astype(np.float64)
+    t2 = time.perf_counter()
+    a_part, a_sv = OL.attn_half_fwd(sh2, x2, pa2)
+    x21 = OL.reduce_partials([a_part], x2, pa2["b_out"])
+    m_part, m_sv = OL.mlp_half_fwd(sh2, x21, pm2)
+    dx2m, _, _ = OL.mlp_half_bwd(sh2, g2, pm2, m_sv)
+    OL.attn_half_bwd(sh2, OL.reduce_partials([dx2m], g2, None), pa2, a_sv)
+    dt2 = time.perf_counter() - t2
+    fl2 = 3.0 * shard_fwd_flops(w2.tokens, w2.hidden, w2.heads, w2.head_dim, w2.ffn, w2.seq, 1)
+    del pa2, pm2, x2, g2, a_sv, m_sv, x21, a_part, m_part, dx2m
+    log(f"cpu baseline GPT-style layer: {dt2:.1f}s, {fl2 / dt2 / 1e12:.3f} TFLOP/s")
+
+    # the full layer (8 slices' worth, 128 heads) on its sampled rows: 32 seeded
+    # positions of one sequence (always its first and last), the forward of the
+    # unsliced layer; keys and values of every position up to the last one
+    w5 = WORKLOADS[5]
+    sh5 = OL.LayerShape(batch=1, seq=w5.seq, hidden=w5.hidden, heads=w5.heads, ffn=w5.ffn, tp=1)
+    r5 = np.random.Generator(np.random.PCG64(5050))
+    # 5e9 parameters: a 2^22-value N(0, 0.02) pool repeated to every weight's
+    # shape, float32 (the oracle's time does not depend on the values; drawing
+    # them all would take longer than the oracle itself)
+    pool = r5.standard_normal(1 << 22, dtype=np.float32) * np.float32(0.02)
+    full5 = {k: np.resize(pool, shp) for k, shp in OL.full_param_shapes(sh5).items()}
+    for k in ("ln1_g", "ln2_g"):
+        full5[k] += np.float32(1.0)
+    x5 = r5.standard_normal((w5.seq, w5.hidden), dtype=np.float32).astype(np.float64)
+    rows5 = sorted({0, w5.seq - 1, *r5.integers(1, w5.seq - 1, size=30).tolist()})
+    t5 = time.perf_counter()
+    OL.layer_fwd_rows(sh5, x5, full5, rows5)
+    dt5 = time.perf_counter() - t5
+    h5, s5 = w5.hidden, w5.seq
+    nr = len(rows5)
+    # K and V of all positions, then per sampled row: Q, scores and weighted sum
+    # over its visible keys (causal), output projection, MLP
+    fl5 = (2.0 * s5 * h5 * 2 * h5 + 2.0 * nr * h5 * h5 + sum(4.0 * h5 * (r + 1) for r in rows5)
+           + 2.0 * nr * h5 * h5 + 4.0 * nr * h5 * w5.ffn)
+    del full5, x5
+    log(f"cpu baseline full layer, {nr} sampled rows of one sequence: {dt5:.1f}s")
+
+    # the oracle's optimizer step on a 2^24-element chunk of the same workload, as
     # GB/s with the step's 34 bytes per parameter (accumulator, master, m, v read;
     # master, m, v and the bf16 copy written; the norm pass)
     from oracle import adam as OA
     rng = np.random.Generator(np.random.PCG64(4040))
-    nc = 1 << 22
+    nc = 1 << 24
     p0 = rng.standard_normal(nc) * 0.02
     m0 = rng.standard_normal(nc) * 1e-3
     v0 = (rng.standard_normal(nc) * 1e-3) ** 2
@@ -776,7 +833,7 @@ def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=2048):
     OA.adam_step(p0, m0, v0, a0, OA.AdamConfig(step=100))
     dta = time.perf_counter() - t1
     adam_gbs = 34.0 * nc / dta / 1e9
-    log(f"cpu baseline adam: {dta:.2f}s for 2^22 parameters = {adam_gbs:.2f} GB/s")
+    log(f"cpu baseline adam: {dta:.2f}s for 2^24 parameters = {adam_gbs:.2f} GB/s")
     # the tiny layer (hidden 256, 4 heads of 64, MLP 1024, 2 sequences of 128,
     # its t = 2 slices in turn), fwd+bwd through the oracle on one BLAS thread
     # and on all of them (best of 5 passes each)
@@ -810,8 +867,18 @@ def cpu_baseline(pa_np, pm_np, x_np, g_np, sample_tokens=2048):
             "seconds": round(dt, 2),
             "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
             "blas": [{k: i.get(k) for k in ("internal_api", "version", "num_threads")} for i in info],
-            "adam": {"value": round(adam_gbs, 3), "unit": "GB/s", "sample": "float64 oracle Adam step over 2^22 "
-                     "parameters (34 B/param accounting)", "seconds": round(dta, 3)},
+            "adam": {"value": round(adam_gbs, 3), "unit": "GB/s", "sample": "float64 oracle Adam step over one "
+                     "2^24-parameter chunk of the 1.887e9-parameter share (34 B/param accounting; the whole share "
+                     "would take about 113 chunks)", "seconds": round(dta, 3)},
+            "gpt_layer_h4096": {"value": round(fl2 / dt2 / 1e12, 4), "unit": "TFLOP/s", "seconds": round(dt2, 2),
+                                "sample": "float64 oracle fwd+bwd of the GPT-style layer (hidden 4096, 32 heads of "
+                                          "128, MLP 16384, 2048 tokens, one slice) in full", "flop": fl2},
+            "full_layer_sampled_rows": {"value": round(fl5 / dt5 / 1e12, 4), "unit": "TFLOP/s",
+                                        "seconds": round(dt5, 2), "flop": fl5,
+                                        "sample": f"float64 oracle forward of the unsliced full layer (hidden "
+                                                  f"20480, 128 heads, MLP 81920; float32 weights from a repeated "
+                                                  f"random pool) on {nr} sampled positions of one 2048-token "
+                                                  f"sequence (keys and values of every position)"},
             "tiny_layer": {"sample": "float64 oracle fwd+bwd of the tiny layer (hidden 256, 4 heads of 64, MLP 1024, "
                            "2 x 128 tokens, 2 slices in turn; best of 5)", "flop": tiny_fl,
                            "one_core_ms": round(t_one * 1e3, 3), "all_cores_ms": round(t_all * 1e3, 3),
