@@ -271,7 +271,7 @@ def main():
     log(f"GEMMs alone: {g_ms:.3f} ms of the step, {gemm_tflops:.1f} TFLOP/s")
     result["roofline"] = {
         "bound": "mfma",
-        "kernel": "gemm_bf16_dtl64_kernel + tail_reduce_kernel (the 12 GEMM launches of one step)",
+        "kernel": "gemm_bf16_rs_kernel (NN, NT) and gemm_bf16_dtl64_kernel (TN), + tail_reduce_kernel (the 12 GEMM launches of one step)",
         "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic_bytes(),
         "traffic_unit": "bytes per launch (average over the 12 launches)",

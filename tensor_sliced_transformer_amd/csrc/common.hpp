@@ -130,6 +130,46 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 // A buffer-load offset past any num_records used here: the load returns zeros.
 constexpr uint32_t kOobOffset = 0x80000000u;
 
+// 128-bit buffer resource over `bytes` bytes from p (raw, stride 0): a load at
+// an offset past num_records returns zeros and a store there is dropped, so
+// ragged edges need no branch around the memory instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                         off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
+}
+
+// DPP lane permutation of a float (every source lane valid for the patterns used).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 64 lanes of a wavefront without LDS traffic: butterflies over
+// pairs and quads (quad_perm), then 8 and 16 lanes (row_half_mirror,
+// row_mirror; each pair of partners adds the same two values, so every lane
+// of a 16-lane row holds the same sum), then the four row sums in order.
+// The result is uniform across the wavefront.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Buffer resource as four words: 48-bit base, stride 0, num_records bytes,
 // and the raw-buffer format word.
 __device__ __forceinline__ i32x4_t rsrc_words(const void* p, uint32_t bytes) {

@@ -95,16 +95,11 @@ __device__ __forceinline__ void transpose_block(const uint4* in, uint4* out, flo
 // picks the half of a 256-byte bank period, the XOR picks the slot in it).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// 128-bit buffer resource over a whole operand; loads at offsets beyond
-// num_records return zero, which is how ragged tiles are handled without
-// branches (an out-of-range element gets the offset kOob).
-constexpr uint32_t kOob = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
+// Operands are read through buffer resources (make_rsrc) over the whole
+// operand; loads at offsets beyond num_records return zero, which is how
+// ragged tiles are handled without branches (an out-of-range element gets the
+// offset kOob).
+constexpr uint32_t kOob = kOobOffset;
 
 // Loader of one operand tile (R rows of the M or N dimension, BK of K) into
 // LDS rows of K. KC: source is K-contiguous (elem(r,k) = p[r*ld + k]),

@@ -2,9 +2,10 @@
 //
 // Forward: y = gamma * (x - mean) * rstd + beta with mean and biased variance
 // over the row, statistics in fp32 (mean, rstd saved for backward). One row
-// per workgroup; each thread keeps its 8-element chunks in registers, so x is
-// read once and y written once; the row's mean and variance come from one
-// workgroup reduction of per-thread (count, mean, squared deviations).
+// at a time per workgroup, the workgroups persistent over the rows; each
+// thread keeps its 8-element chunks in registers, so x is read once and y
+// written once; the row's mean, then its centred sum of squares, come from
+// two workgroup sums (the two-pass form of the definition).
 //
 // Backward on an upstream gradient gy (linear in gy, so a tensor slice may
 // apply it to its own partial): with gh = gy * gamma and xhat recomputed from
@@ -15,6 +16,8 @@
 // columns in each row, so it accumulates its dgamma/dbeta share in registers
 // and writes one fp32 partial row per workgroup; a column reduction in fixed
 // order finishes them (deterministic, no atomics).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,101 +49,97 @@ template <> struct Raw8<float> {
   }
 };
 
-// Count, mean and sum of squared deviations of a set of values; two sets
-// combine exactly (up to rounding) by the pairwise update of Chan, Golub and
-// LeVeque, so a row's variance comes out of one reduction without the
-// cancellation of E[x^2] - E[x]^2.
-struct Moments {
-  float n, mean, m2;
-};
-__device__ __forceinline__ Moments combine(const Moments& a, const Moments& b) {
-  const float n = a.n + b.n;
-  if (n == 0.0f) return a;
-  const float d = b.mean - a.mean;
-  const float wb = b.n / n;
-  return {n, a.mean + d * wb, a.m2 + b.m2 + d * d * a.n * wb};
-}
-// Combined moments of the whole workgroup; every thread gets the same value
-// (lanes combine in lane order, waves in wave order).
+// Sum of v over the workgroup (NT threads) through the NT/64 slots of `red`;
+// every thread gets the same value (waves added in order).
 template <int NT>
-__device__ __forceinline__ Moments block_moments(Moments m, float* red) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    Moments o;
-    o.n = __shfl_xor(m.n, off, kWave);
-    o.mean = __shfl_xor(m.mean, off, kWave);
-    o.m2 = __shfl_xor(m.m2, off, kWave);
-    m = (lane & off) ? combine(o, m) : combine(m, o);
-  }
-  if (lane == 0) {
-    red[3 * w] = m.n;
-    red[3 * w + 1] = m.mean;
-    red[3 * w + 2] = m.m2;
-  }
+__device__ __forceinline__ float block_total(float v, float* red) {
+  const float w = wave_sum_dpp(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = w;
   __syncthreads();
-  Moments t = {red[0], red[1], red[2]};
+  float t = red[0];
 #pragma unroll
-  for (int i = 1; i < NT / kWave; ++i) t = combine(t, Moments{red[3 * i], red[3 * i + 1], red[3 * i + 2]});
+  for (int i = 1; i < NT / kWave; ++i) t += red[i];
   return t;
 }
 
+// Persistent, one workgroup per CU: workgroup b normalises rows b, b + G,
+// b + 2G, ... (G workgroups). gamma and beta are loaded once and stay in
+// registers; the next row's x is loaded while the current row is reduced.
+// Wave sums move through DPP rather than LDS, which made the kernel a quarter
+// faster than one row per workgroup with LDS shuffles (the reductions, not
+// the memory traffic, bounded it). The reductions of consecutive rows use
+// alternating LDS slots: a thread can only overwrite a slot after the
+// barriers of the row in between, which every thread reaches only after
+// reading that slot.
 template <int NT, typename T, int CPT>
 __global__ __launch_bounds__(NT) void ln_fwd_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                                                     const T* __restrict__ beta, float eps, T* __restrict__ y,
                                                     float* __restrict__ mean_out, float* __restrict__ rstd_out,
-                                                    int cols) {
-  __shared__ float red[3 * (NT / kWave)];
-  const int64_t row = blockIdx.x;
-  const T* xr = x + row * cols;
+                                                    int64_t rows, int cols) {
+  constexpr int NW = NT / kWave;
+  __shared__ float red[2][2 * NW];
   const int nch = cols / 8;
   const int tid = threadIdx.x;
-  Raw8<T> xv[CPT], gv[CPT], bv[CPT];
+  const int64_t step = gridDim.x;
+  Raw8<T> gv[CPT], bv[CPT], nx[CPT];
+  int64_t row = blockIdx.x;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * NT;
     if (ch < nch) {
-      xv[c].load(xr + ch * 8);
-      gv[c].load(gamma + ch * 8);  // issued before the reduction so its latency hides under it
+      nx[c].load(x + row * cols + ch * 8);
+      gv[c].load(gamma + ch * 8);
       bv[c].load(beta + ch * 8);
     }
   }
-  float n = 0.0f, s = 0.0f;
+  int parity = 0;
+  for (; row < rows; row += step) {
+    Raw8<T> xv[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
-    if (tid + c * NT < nch) {
-      n += 8.0f;
+    for (int c = 0; c < CPT; ++c) xv[c] = nx[c];
+    if (row + step < rows) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += xv[c][e];
-    }
-  const float mt = n > 0.0f ? s / n : 0.0f;
-  float m2 = 0.0f;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c)
-    if (tid + c * NT < nch) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = xv[c][e] - mt;
-        m2 += d * d;
+      for (int c = 0; c < CPT; ++c) {
+        const int ch = tid + c * NT;
+        if (ch < nch) nx[c].load(x + (row + step) * cols + ch * 8);
       }
     }
-  const Moments t = block_moments<NT>(Moments{n, mt, m2}, red);
-  const float mu = t.mean;
-  const float rs = 1.0f / sqrtf(t.m2 / (float)cols + eps);
-  T* yr = y + row * cols;
+    float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = tid + c * NT;
-    if (ch < nch) {
-      float o[8];
+    for (int c = 0; c < CPT; ++c)
+      if (tid + c * NT < nch) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = gv[c][e] * ((xv[c][e] - mu) * rs) + bv[c][e];
-      store8(yr + ch * 8, o);
+        for (int e = 0; e < 8; ++e) s += xv[c][e];
+      }
+    const float inv_cols = 1.0f / (float)cols;
+    const float mu = block_total<NT>(s, red[parity]) * inv_cols;
+    float m2 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (tid + c * NT < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = xv[c][e] - mu;
+          m2 += d * d;
+        }
+      }
+    const float rs = 1.0f / sqrtf(block_total<NT>(m2, red[parity] + NW) * inv_cols + eps);
+    parity ^= 1;
+    T* yr = y + row * cols;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * NT;
+      if (ch < nch) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = gv[c][e] * ((xv[c][e] - mu) * rs) + bv[c][e];
+        store8(yr + ch * 8, o);
+      }
     }
-  }
-  if (tid == 0) {
-    mean_out[row] = mu;
-    rstd_out[row] = rs;
+    if (tid == 0) {
+      mean_out[row] = mu;
+      rstd_out[row] = rs;
+    }
   }
 }
 
@@ -217,8 +216,8 @@ __global__ __launch_bounds__(NT) void ln_bwd_kernel(const G* __restrict__ gy, co
         }
       }
     }
-    sa = wave_sum(sa);
-    sb = wave_sum(sb);
+    sa = wave_sum_dpp(sa);
+    sb = wave_sum_dpp(sb);
     if (lane == 0) {
       red[parity][w] = sa;
       red[parity][NW + w] = sb;
@@ -362,10 +361,13 @@ template <int NT, typename T>
 hipError_t ln_fwd_launch(int64_t rows, int cols, const void* x, const void* g, const void* b, float eps,
                          void* y, float* mean, float* rstd, hipStream_t st) {
   const int cpt = ln_cpt(cols / 8, NT);
+  // one 512-thread workgroup per CU (its registers at the MT-NLG width leave
+  // no room for a second)
+  const unsigned grid = (unsigned)std::min<int64_t>(rows, (int64_t)device_cus() * std::max(1, 512 / NT));
 #define MTNLG_LNF(C)                                                                                    \
-  hipLaunchKernelGGL((ln_fwd_kernel<NT, T, C>), dim3(rows), dim3(NT), 0, st, static_cast<const T*>(x), \
+  hipLaunchKernelGGL((ln_fwd_kernel<NT, T, C>), dim3(grid), dim3(NT), 0, st, static_cast<const T*>(x), \
                      static_cast<const T*>(g), static_cast<const T*>(b), eps, static_cast<T*>(y), mean,  \
-                     rstd, cols)
+                     rstd, rows, cols)
   if (cpt <= 1) MTNLG_LNF(1);
   else if (cpt <= 2) MTNLG_LNF(2);
   else if (cpt <= 3) MTNLG_LNF(3);
