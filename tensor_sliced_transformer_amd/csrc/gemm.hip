@@ -240,30 +240,158 @@ __device__ __forceinline__ void epilogue_slab(const GemmArgs& p, const float* st
   }
 }
 
-// Epilogue over one wave's private 16 x 64 fp32 slab (row r's column c stored
-// at c ^ (32 * ((r >> 2) & 1))) whose first element is tile-local (rl0, cl0).
-template <typename T, int WN, int BN>
-__device__ __forceinline__ void epilogue_slab16(const GemmArgs& p, const float* slab, int m0, int n0, int rl0,
-                                                int cl0, int lane, float* pt) {
-  static_assert(WN % 64 == 0, "slab swizzle assumes pairs of 32-column halves");
-  constexpr int VPR = WN / 8;
-#pragma unroll 1
-  for (int u = lane; u < 16 * VPR; u += kWave) {
-    const int rr = u / VPR, cc = (u % VPR) * 8;
-    const float* q = slab + rr * WN + (cc ^ (32 * ((rr >> 2) & 1)));
-    float v[8];
-    const float4 a = *reinterpret_cast<const float4*>(q);
-    const float4 b = *reinterpret_cast<const float4*>(q + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    if (pt) {
-      store8(pt + (int64_t)(rl0 + rr) * BN + cl0 + cc, v);
-      continue;
-    }
-    const int row = m0 + rl0 + rr, col = n0 + cl0 + cc;
-    if (row >= p.M || col >= p.N) continue;
-    apply_epi_store<T>(p, row, col, v);
+// ---- epilogue of a 256 x 256 work item (register-staged and direct-to-LDS
+// kernels): kind = the launch's GemmArgs::epi for a whole tile, kEpiPart for
+// a tail piece (its raw fp32 sums into the piece's slot).
+//
+// A wave's 128 x 64 block leaves its accumulators in 8 passes of 16 rows
+// through the wave's private slab (row r's column c at c ^ (32 * ((r >> 2) &
+// 1)), so the two row groups of an accumulator write disjoint banks); lane l
+// then takes rows l/8 and l/8 + 8 of the pass, columns 8*(l%8) .. +7, which
+// stay the lane's columns for the whole tile. Every global access goes
+// through a buffer resource whose range ends at the last row (an offset past
+// the last column is moved out of range), so no branch surrounds a memory
+// instruction: the pass loop is straight-line, the bias is loaded once per
+// tile, the GeLU' input of the next pass is loaded before this pass's
+// stores, and no pass waits for the stores of the one before.
+constexpr int kEpiPart = 100;
+
+// vector-memory instructions one lane issues in the epilogue of a tile
+template <int KIND>
+constexpr int epi_vm_ops() {
+  return (KIND == EPI_BIAS_GELU || KIND == EPI_GELU_GRAD || KIND == kEpiPart) ? 32 : 16;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
+}
+__device__ __forceinline__ uint4 pack_bf16x8(const float* v) {
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+__device__ __forceinline__ uint4 pack_f16x8(const float* v) {
+  return make_uint4(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                    pack_f16x2(v[6], v[7]));
+}
+
+// The lane's 8 bias values of a tile (loaded before the K loop; zeros past N).
+__device__ __forceinline__ uint4 epi_bias_load(const GemmArgs& p, int n0, int wn, int lane) {
+  const int col = n0 + wn * 64 + (lane & 7) * 8;
+  return buf_load16(make_rsrc(p.bias, (uint32_t)p.N * 2u), col < p.N ? (uint32_t)col * 2u : kOob);
+}
+
+// A buffer resource over a bf16 M x ldc matrix from row r0 on (none past M).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, const GemmArgs& p, int r0) {
+  const bf16_t* b = static_cast<const bf16_t*>(base) + (int64_t)r0 * p.ldc;
+  return make_rsrc(b, r0 < p.M ? (uint32_t)((int64_t)(p.M - r0) * p.ldc * 2) : 0u);
+}
+
+// mid() runs before pass FM (halfway): the register-staged kernel writes the
+// next item's first K tile to LDS there.
+template <int KIND, int FM, int FN, int TN, int BN, typename Mid>
+__device__ __forceinline__ void epilogue256(const GemmArgs& p, f32x16_t (&acc)[FM][FN], float* slab, int m0,
+                                           int n0, int wm, int wn, int lane, float* pt, uint4 bias_raw,
+                                           Mid&& mid) {
+  static_assert(TN == 64, "lane columns assume 64-column wave blocks");
+  constexpr int TM = FM * 32;
+  const int lrow = lane & 31, lg = lane >> 5;
+  const int rr = lane >> 3, cc = (lane & 7) * 8;
+  const int col = n0 + wn * TN + cc;
+  const int row_w = m0 + wm * TM;
+  uint32_t vo[2];  // bytes from a pass's first row, rows rr and rr + 8 (bf16 outputs and aux)
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    vo[q] = col < p.N ? (uint32_t)(((int64_t)(rr + 8 * q) * p.ldc + col) * 2) : kOob;
+  float bias[8];
+  unpack_bf16x8(bias_raw, bias);
+  const bool f16 = col < p.f16_cols;
+  uint4 ax[2][2];  // GeLU' inputs of a pass, double-buffered by pass parity
+  auto aux_load = [&](int pass, uint4* dst) {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(p.aux, p, row_w + 16 * pass);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dst[q] = buf_load16(r, vo[q]);
+  };
+  if constexpr (KIND == EPI_GELU_GRAD) aux_load(0, ax[0]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (i == FM / 2) mid();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int pass = 2 * i + hh;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 8 * b + 4 * lg + r;
+            slab[row * TN + ((j * 32 + lrow) ^ (32 * ((row >> 2) & 1)))] = acc[i][j][(2 * hh + b) * 4 + r];
+          }
+      if constexpr (KIND == EPI_GELU_GRAD)
+        if (pass + 1 < 2 * FM) aux_load(pass + 1, ax[(pass + 1) & 1]);
+      const int prow = row_w + 16 * pass;
+      __amdgpu_buffer_rsrc_t rc;
+      if constexpr (KIND == kEpiPart)
+        rc = make_rsrc(pt, 256u * BN * 4u);
+      else
+        rc = rows_rsrc(p.C, p, prow);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int sr = rr + 8 * q;
+        const float* sp = slab + sr * TN + (cc ^ (32 * ((sr >> 2) & 1)));
+        const float4 a = *reinterpret_cast<const float4*>(sp);
+        const float4 c = *reinterpret_cast<const float4*>(sp + 4);
+        float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        if constexpr (KIND == kEpiPart) {
+          const uint32_t po = (uint32_t)(((wm * TM + 16 * pass + sr) * BN + wn * TN + cc) * 4);
+          buf_store16(rc, po, __builtin_bit_cast(uint4, a));
+          buf_store16(rc, po + 16, __builtin_bit_cast(uint4, c));
+        } else if constexpr (KIND == EPI_GELU_GRAD) {
+          float u[8];
+          unpack_bf16x8(ax[pass & 1][q], u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] *= gelu_grad_f(u[e]);
+          buf_store16(rc, vo[q], pack_bf16x8(v));
+        } else if constexpr (KIND == EPI_BIAS_GELU) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] += bias[e];
+            y[e] = gelu_f(v[e]);
+          }
+          buf_store16(rc, vo[q], pack_bf16x8(v));
+          buf_store16(rows_rsrc(p.C2, p, prow), vo[q], pack_bf16x8(y));
+        } else if constexpr (KIND == EPI_BIAS || KIND == EPI_BIAS_F16LO) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += bias[e];
+          if constexpr (KIND == EPI_BIAS_F16LO)
+            buf_store16(rc, vo[q], f16 ? pack_f16x8(v) : pack_bf16x8(v));
+          else
+            buf_store16(rc, vo[q], pack_bf16x8(v));
+        } else {
+          buf_store16(rc, vo[q], pack_bf16x8(v));
+        }
+      }
+    }
+  }
+}
+
+// Runs body(integral_constant<kind>) for a work item of a kernel built for
+// epilogue EPI: EPI itself for a whole tile, kEpiPart for a tail piece. (The
+// kind is a kernel template parameter: one kernel holding every kind's code
+// spilled registers around the epilogue, and a spill reload waits for every
+// store in flight.)
+template <int EPI, typename Body>
+__device__ __forceinline__ void epi_dispatch(bool piece, Body&& body) {
+  if (piece)
+    body(std::integral_constant<int, kEpiPart>{});
+  else
+    body(std::integral_constant<int, EPI>{});
 }
 
 // Tile position of tile index L: groups of kGroupM tile rows, walked column by column.
@@ -801,7 +929,7 @@ __device__ __forceinline__ int kc64_frag_off(int rb32, int s, int lane) {
   return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, int WM, int WN>
+template <int BM, int BN, bool A_KC, bool B_KC, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -930,7 +1058,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
   if (nk > 1) issue(1, m0, n0, kbeg, kend);
   bool first = true;
   float* const slab = reinterpret_cast<float*>(smem + 2 * SS) + wave * ESLAB;
-  const int lrow = lane & 31, lg = lane >> 5;
 
   for (;;) {
     if (!first) lane_setup();
@@ -943,8 +1070,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     if (nk > 0) {
-      if (first && nk > 1) MTNLG_VMCNT(NL);              // tile 0 of the prologue landed
-      else __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): also the last epilogue's stores
+      // tile 0 landed (for later items the previous epilogue waited for it)
+      if (first) {
+        if (nk > 1) MTNLG_VMCNT(NL);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      }
       __syncthreads();
       read_frags(smem, 0, 0);
     }
@@ -987,10 +1117,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
 
     // Every wave is done with the ring (its last reads waited, then a
     // barrier): K-tiles 0 and 1 of the next work item go in flight now and
-    // land while this item's epilogue runs from the per-wave slabs.
+    // land while this item's epilogue runs from the per-wave slabs. (The bias
+    // of bias kinds is waited for first: the loads below are invisible to the
+    // compiler's count, which would otherwise wait for them too.)
     const int wnext = w + (int)gridDim.x;
     const bool has_next = wnext < total;
     const int m0c = m0, n0c = n0;
+    constexpr bool kBias = EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F16LO;
+    const bool has_bias = kBias && pt == nullptr;
+    uint4 bias_raw = make_uint4(0u, 0u, 0u, 0u);
+    if (has_bias) {
+      bias_raw = epi_bias_load(p, n0c, wn, lane);
+      asm volatile("" : : "v"(bias_raw.x), "v"(bias_raw.y), "v"(bias_raw.z), "v"(bias_raw.w));
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __syncthreads();
     if (has_next) {
@@ -1005,25 +1144,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
       if (nk > 1) issue(1, m0, n0, kbeg, kend);
     }
 
-    // Epilogue in 16-row slabs through this wave's private LDS slab (no
-    // workgroup barrier): column c of slab row r sits at c ^ (32 * ((r >> 2) & 1)),
-    // so the two row groups of one MFMA accumulator write disjoint banks.
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = 8 * b + 4 * lg + r;
-              slab[row * TN + ((j * 32 + lrow) ^ (32 * ((row >> 2) & 1)))] = acc[i][j][(2 * hh + b) * 4 + r];
-            }
-        epilogue_slab16<bf16_t, TN, BN>(p, slab, m0c, n0c, wm * TM + i * 32 + hh * 16, wn * TN, lane, pt);
+    // Then tile 0 of the next item: the wait counts this epilogue's stores and
+    // the next item's tile 1 (issued after tile 0), so it does not wait for
+    // the stores to drain.
+    epi_dispatch<EPI>(pt != nullptr, [&](auto kind) {
+      constexpr int KIND = decltype(kind)::value;
+      epilogue256<KIND, FM, FN, TN, BN>(p, acc, slab, m0c, n0c, wm, wn, lane, pt, bias_raw, [] {});
+      constexpr int E = epi_vm_ops<KIND>();
+      static_assert(NL + E <= 63, "vmcnt is 6 bits");
+      if (has_next) {
+        if (nk > 1) MTNLG_VMCNT(NL + E);
+        else MTNLG_VMCNT(E);
       }
-    }
+    });
     if (!has_next) break;
     w = wnext;
   }
@@ -1053,7 +1186,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
 //   while the current item's epilogue runs from per-wave slabs beside the
 //   ring.
 // ---------------------------------------------------------------------------
-template <int WM, int WN, bool A_KC, bool B_KC, bool FULLK>
+template <int WM, int WN, bool A_KC, bool B_KC, bool FULLK, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) {
   constexpr int BM = 256, BN = 256, NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -1169,7 +1302,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
   static_assert(U0 + U1 + NL / 3 == NL && 2 * U0 + 1 <= NM, "interleave");
 
   float* const slab = reinterpret_cast<float*>(smem + 2 * SS) + wave * ESLAB;
-  const int lrow = lane & 31, lg = lane >> 5;
 
   // first work item: tile 0 into stage 0, tile 1 into the staging registers
   lane_setup();
@@ -1241,11 +1373,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
       __builtin_amdgcn_sched_group_barrier(0x008, NM - 1, 0);
     }
 
-    // every wave is done with the ring: load the next item's K tile 0, write
-    // it to stage 0 halfway through the epilogue, then load its tile 1
+    // every wave is done with the ring: load the bias of this tile's columns
+    // (bias kinds), then the next item's K tile 0, which is written to stage 0
+    // halfway through the epilogue, when its tile 1 is loaded
     const int wnext = w + (int)gridDim.x;
     const bool has_next = wnext < total;
     const int m0c = m0, n0c = n0;
+    constexpr bool kBias = EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_F16LO;
+    const bool has_bias = kBias && pt == nullptr;
+    const uint4 bias_raw = has_bias ? epi_bias_load(p, n0c, wn, lane) : make_uint4(0u, 0u, 0u, 0u);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __syncthreads();
     if (has_next) {
@@ -1260,28 +1396,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
 #pragma unroll
       for (int u = 0; u < NL; ++u) gload(u, 0);
     }
+    epi_dispatch<EPI>(pt != nullptr, [&](auto kind) {
+      epilogue256<decltype(kind)::value, FM, FN, TN, BN>(p, acc, slab, m0c, n0c, wm, wn, lane, pt, bias_raw, [&]() {
+        if (has_next) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i == FM / 2 && has_next) {
+          for (int u = 0; u < NL; ++u) swrite(u, 0);
 #pragma unroll
-        for (int u = 0; u < NL; ++u) swrite(u, 0);
-#pragma unroll
-        for (int u = 0; u < NL; ++u) gload(u, 1);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = 8 * b + 4 * lg + r;
-              slab[row * TN + ((j * 32 + lrow) ^ (32 * ((row >> 2) & 1)))] = acc[i][j][(2 * hh + b) * 4 + r];
-            }
-        epilogue_slab16<bf16_t, TN, BN>(p, slab, m0c, n0c, wm * TM + i * 32 + hh * 16, wn * TN, lane, pt);
-      }
-    }
+          for (int u = 0; u < NL; ++u) gload(u, 1);
+        }
+      });
+    });
     if (!has_next) break;
     w = wnext;
   }
@@ -1319,6 +1443,18 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool AK, bool BKc, int EPI>
+void launch_256(const GemmArgs& a, dim3 grid, bool fullk, hipStream_t st) {
+  if constexpr (AK || BKc) {
+    if (fullk)
+      hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, true, EPI>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, false, EPI>), grid, dim3(512), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<256, 256, AK, BKc, 2, 4, EPI>), grid, dim3(512), 0, st, a);
+  }
+}
+
 template <int BM, int BN, bool AK, bool BKc>
 hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
   const int total = a.nfull + a.tail_tiles * a.tail_split;
@@ -1333,13 +1469,13 @@ hipError_t launch_dtl(const GemmArgs& a, hipStream_t st) {
     // Whole K tiles everywhere (K and the pieces' K range multiples of 64) let
     // the loads use scalar offsets (+1-4% measured).
     const bool fullk = a.K % kBK64 == 0 && a.k_chunk % kBK64 == 0;
-    if constexpr (AK || BKc) {
-      if (fullk)
-        hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, true>), grid, dim3(512), 0, st, a);
-      else
-        hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, false>), grid, dim3(512), 0, st, a);
-    } else
-      hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<BM, BN, AK, BKc, 2, 4>), grid, dim3(512), 0, st, a);
+    switch (a.epi) {
+      case EPI_BIAS: launch_256<AK, BKc, EPI_BIAS>(a, grid, fullk, st); break;
+      case EPI_BIAS_GELU: launch_256<AK, BKc, EPI_BIAS_GELU>(a, grid, fullk, st); break;
+      case EPI_GELU_GRAD: launch_256<AK, BKc, EPI_GELU_GRAD>(a, grid, fullk, st); break;
+      case EPI_BIAS_F16LO: launch_256<AK, BKc, EPI_BIAS_F16LO>(a, grid, fullk, st); break;
+      default: launch_256<AK, BKc, EPI_STORE>(a, grid, fullk, st); break;
+    }
   } else {           // 32-deep K tiles, 4 waves (2 x 2)
     hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, AK, BKc, 2, 2>), grid, dim3(256), 0, st, a);
   }
