@@ -584,6 +584,26 @@ def adam_bench(torch, tst, dev, reps):
              "bytes_per_param": 66, "unfused_bytes_per_param": 70}
     log(f"norm folded into the last accumulation: {f_acc:.2f} + update {f_upd:.2f} ms "
         f"(unfused {t_acc:.2f} + {t_step:.2f} ms)")
+    # the update's ceiling: the same reads and writes (30 B per parameter), the
+    # same launch, no optimizer arithmetic (mtnlg_adam_stream_reference)
+    tst.adam_stream_reference(master, m, v, acc, wbf)
+    torch.cuda.synchronize()
+    t_ref = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        tst.adam_stream_reference(master, m, v, acc, wbf)
+        ev[1].record()
+        torch.cuda.synchronize()
+        t_ref += ev[0].elapsed_time(ev[1])
+    t_ref /= reps
+    ref_gbs = 30.0 * n / (t_ref * 1e-3) / 1e9
+    fused["stream_reference"] = {"ms": round(t_ref, 3), "GBps": round(ref_gbs, 1),
+                                 "hbm_frac": round(ref_gbs / PEAK_HBM_GBS, 4),
+                                 "update_vs_reference": round(fused["update_GBps"] / ref_gbs, 4),
+                                 "note": "the update's reads and writes with no arithmetic "
+                                         "(mtnlg_adam_stream_reference): the ceiling of that access mix"}
+    log(f"update {fused['update_GBps']:.0f} GB/s vs its stream reference {ref_gbs:.0f} GB/s "
+        f"({100 * fused['update_GBps'] / ref_gbs:.1f}%)")
     acc_gbs = 36.0 * n / (t_acc * 1e-3) / 1e9
     step_gbs = 34.0 * n / (t_step * 1e-3) / 1e9
     log(f"accumulate x4 {t_acc:.2f} ms = {acc_gbs:.0f} GB/s; step {t_step:.2f} ms = {step_gbs:.0f} GB/s; "

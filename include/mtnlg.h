@@ -312,6 +312,21 @@ int mtnlg_adam_update(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float
                       const float* grad, void* w_bf16, float* stats, const void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Measurement reference for the optimizer step (not part of training): the
+ * memory traffic of mtnlg_adam_update's element pass -- master, m, v and grad
+ * read, master, m, v and (if w_bf16 is not NULL) the bf16 copy written, 30
+ * bytes per parameter as the mixed-precision Adam state of the Elamur summary
+ * (Key points) is laid out here -- with the same launch and access order but
+ * no optimizer arithmetic: master, m and v are written back unchanged and
+ * w_bf16 receives bf16(master). Its rate is the memory system's rate for that
+ * access mix, the ceiling of the update.
+ *   master, m, v [n] f32 (rewritten with their own values), grad [n] f32
+ *   (read only), w_bf16 [n] bf16 or NULL; device memory, 16-byte aligned.
+ * n >= 0 (n == 0 does nothing). MTNLG_ERR_SHAPE for n < 0, MTNLG_ERR_ARG for a
+ * NULL pointer, MTNLG_ERR_ALIGN, MTNLG_ERR_HIP. */
+int mtnlg_adam_stream_reference(int64_t n, float* master, float* m, float* v, const float* grad,
+                                void* w_bf16, void* stream);
+
 /* ---- One pipeline stage on one GPU ----
  *
  * A stage is `layers` consecutive decoder layers, each held as the same slice

@@ -18,7 +18,7 @@ from ._lib import ATTN, MLP, BF16, F32, AdamCfg, HalfGrads, HalfParams, LayerDes
 __all__ = ["ATTN", "MLP", "BF16", "F32", "LayerDesc", "AdamCfg", "MtnlgError", "load", "make_desc",
            "saved_bytes", "workspace_bytes", "layer_fwd", "layer_bwd", "reduce_partials",
            "grad_accumulate", "adam_workspace_bytes", "adam_step", "adam_static_scratch_bytes", "adam_step_noalloc",
-           "grad_accumulate_norm", "adam_update",
+           "grad_accumulate_norm", "adam_update", "adam_stream_reference",
            "reduce_partials_dropout", "dropout_bwd",
            "recompute_workspace_bytes", "layer_bwd_recompute", "StageDesc", "make_stage_desc",
            "stage_param_count", "stage_param_offsets", "stage_workspace_bytes", "stage_step", "gemm", "gemm_workspace_bytes", "layernorm_fwd",
@@ -251,6 +251,21 @@ def adam_update(cfg: AdamCfg, master, m, v, grad, w_bf16, stats, ws, stream=None
     check(load().mtnlg_adam_update(ctypes.byref(cfg), master.numel(), _ptr(master), _ptr(m), _ptr(v), _ptr(grad),
                                    _ptr(w_bf16), _ptr(stats), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "mtnlg_adam_update")
+
+
+def adam_stream_reference(master, m, v, grad, w_bf16=None, stream=None) -> None:
+    """The Adam update's reads and writes with no optimizer arithmetic (master, m,
+    v rewritten unchanged, w_bf16 = bf16(master)): a measurement reference for the
+    update's rate (mtnlg_adam_stream_reference)."""
+    torch = _torch()
+    n = master.numel()
+    for name, t in (("master", master), ("m", m), ("v", v), ("grad", grad)):
+        _expect(name, t, (n,), torch.float32)
+    if w_bf16 is not None:
+        _expect("w_bf16", w_bf16, (n,), torch.bfloat16)
+    check(load().mtnlg_adam_stream_reference(n, _ptr(master), _ptr(m), _ptr(v), _ptr(grad),
+                                             _ptr(w_bf16) if w_bf16 is not None else None, _stream(stream)),
+          "mtnlg_adam_stream_reference")
 
 
 STAGE_TENSORS = ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out")

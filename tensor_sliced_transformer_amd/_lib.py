@@ -78,6 +78,8 @@ SIGNATURES = {
                                              c_size_t, c_void_p]),
     "mtnlg_adam_update": (c_int32, [POINTER(AdamCfg), c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mtnlg_adam_stream_reference": (c_int32, [c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p]),
     "mtnlg_stage_param_count": (c_int64, [POINTER(StageDesc)]),
     "mtnlg_stage_param_offsets": (c_int32, [POINTER(StageDesc), POINTER(c_int64)]),
     "mtnlg_stage_workspace_bytes": (c_size_t, [POINTER(StageDesc)]),

@@ -568,6 +568,20 @@ int mtnlg_adam_update(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float
   return MTNLG_OK;
 }
 
+int mtnlg_adam_stream_reference(int64_t n, float* master, float* m, float* v, const float* grad, void* w_bf16,
+                                void* stream) {
+  g_last_error[0] = 0;
+  if (n < 0) return fail(MTNLG_ERR_SHAPE, "n < 0");
+  if (n == 0) return MTNLG_OK;
+  CHECK_PTR(master);
+  CHECK_PTR(m);
+  CHECK_PTR(v);
+  CHECK_PTR(grad);
+  if (w_bf16) CHECK_PTR(w_bf16);
+  MTNLG_HIP(adam_streams(n, master, m, v, grad, w_bf16, static_cast<hipStream_t>(stream)), "adam_streams");
+  return MTNLG_OK;
+}
+
 static bool gemm_shape_ok(int32_t dtype, int64_t M, int64_t N, int64_t K) {
   // every operand must stay below 2 GiB: the kernels address operands through
   // 32-bit buffer offsets and mark out-of-range elements with offset 2^31

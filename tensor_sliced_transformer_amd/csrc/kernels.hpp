@@ -121,6 +121,9 @@ hipError_t adam_step_static(const AdamScalars& c, int64_t n, float* master, floa
 // and the Adam step that takes them from there instead of its own norm pass.
 hipError_t grad_accumulate_norm(int64_t n, int dtype, const void* grad, float* acc, bool overwrite,
                                 float inv_loss_scale, void* ws, hipStream_t st);
+// The update's reads and writes with its arithmetic left out (values unchanged).
+hipError_t adam_streams(int64_t n, float* master, float* m, float* v, const float* grad, void* w_bf16,
+                        hipStream_t st);
 hipError_t adam_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v,
                        const float* grad, void* w_bf16, float* stats, const void* ws, hipStream_t st);
 

@@ -387,6 +387,41 @@ __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars
   }
 }
 
+// The Adam update's memory traffic without its arithmetic: the same launch,
+// the same streams in the same order (master, m, v and the gradient read; master,
+// m, v and the bf16 copy written, with the same cache hints), each value written
+// back unchanged (the gradient is only waited for). Its rate is what the memory
+// system gives this access mix, the ceiling against which the update is judged.
+__global__ __launch_bounds__(kStreamThreads) void adam_streams_kernel(int64_t n, float* __restrict__ master,
+                                                                      float* __restrict__ m,
+                                                                      float* __restrict__ v,
+                                                                      const float* __restrict__ grad,
+                                                                      bf16_t* __restrict__ w) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = n / 4;
+  for (int64_t u = t0; u < n4; u += stride) {
+    const float4 p = ld_nt(reinterpret_cast<const float4*>(master) + u);
+    const float4 mm = ld_nt(reinterpret_cast<const float4*>(m) + u);
+    const float4 vv = ld_nt(reinterpret_cast<const float4*>(v) + u);
+    const float4 g = ld_nt(reinterpret_cast<const float4*>(grad) + u);
+    asm volatile("" : : "v"(g.x), "v"(g.y), "v"(g.z), "v"(g.w));
+    st_nt(reinterpret_cast<float4*>(master) + u, p);
+    st_nt(reinterpret_cast<float4*>(m) + u, mm);
+    st_nt(reinterpret_cast<float4*>(v) + u, vv);
+    if (w) st_nt(reinterpret_cast<uint2*>(w) + u, make_uint2(pack_bf16x2(p.x, p.y), pack_bf16x2(p.z, p.w)));
+  }
+  for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
+    const float g = grad[i];
+    asm volatile("" : : "v"(g));
+    const float p = master[i];
+    master[i] = p;
+    m[i] = m[i];
+    v[i] = v[i];
+    if (w) w[i] = f2bf(p);
+  }
+}
+
 constexpr int kNormBlocks = 8192;
 
 }  // namespace
@@ -563,6 +598,15 @@ hipError_t adam_step_static(const AdamScalars& c, int64_t n, float* master, floa
   double* part = static_cast<double*>(p);
   return adam_step_parts(c, n, master, m, v, grad, w_bf16, stats, part, reinterpret_cast<int*>(part + kNormBlocks),
                          st);
+}
+
+hipError_t adam_streams(int64_t n, float* master, float* m, float* v, const float* grad, void* w_bf16,
+                        hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int grid = stream_grid(n / 4 + 1, kOneShotBlocks);
+  hipLaunchKernelGGL(adam_streams_kernel, dim3(grid), dim3(kStreamThreads), 0, st, n, master, m, v, grad,
+                     static_cast<bf16_t*>(w_bf16));
+  return hipGetLastError();
 }
 
 hipError_t adam_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,

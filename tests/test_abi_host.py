@@ -201,6 +201,11 @@ def test_other_entry_points_validate():
     assert L.mtnlg_grad_accumulate_norm(16, _lib.BF16, A, A, 1, float("inf"), A, 1 << 20, None) == -1
     assert L.mtnlg_grad_accumulate_norm(16, _lib.BF16, None, A, 1, 1.0, A, 1 << 20, None) == -1
     assert L.mtnlg_grad_accumulate_norm(16, 7, A, A, 1, 1.0, A, 1 << 20, None) == -3
+    assert L.mtnlg_adam_stream_reference(-1, A, A, A, A, None, None) == -2
+    assert L.mtnlg_adam_stream_reference(0, None, None, None, None, None, None) == 0      # empty: no-op
+    assert L.mtnlg_adam_stream_reference(16, A, None, A, A, None, None) == -1
+    assert L.mtnlg_adam_stream_reference(16, A, A, A, ODD, None, None) == -4
+    assert L.mtnlg_adam_stream_reference(16, A, A, A, A, ODD, None) == -4
     assert L.mtnlg_gemm(_lib.BF16, 0, 0, 12, 16, 16, A, A, A, None, None, 0, None) == -2
     assert L.mtnlg_gemm(_lib.BF16, 0, 0, 16, 16, 16, None, A, A, None, None, 0, None) == -1
     # 2048 x 10240 tiles: the leftover round is split along K, so a workspace is required

@@ -281,6 +281,26 @@ def test_adam_step(n, max_norm):
     assert_bf16_copy(gw, gp, rw, rp)
 
 
+@pytest.mark.parametrize("n", [0, 5, 1000003])
+def test_adam_stream_reference_leaves_values(n):
+    """The measurement reference moves the update's bytes and changes nothing:
+    master, m and v are written back bit for bit, the bf16 copy is the
+    round-to-nearest-even rounding of master."""
+    master = randn(80, (n,), 0.02)
+    m = randn(81, (n,), 1e-3)
+    v = randn(82, (n,), 1e-3) ** 2
+    g = randn(83, (n,), 1e-3)
+    tm, tmm, tv, tg = (to_gpu(a, "f32") for a in (master, m, v, g))
+    w = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    tst.adam_stream_reference(tm, tmm, tv, tg, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(tm), master.astype(np.float64))
+    assert np.array_equal(to_np(tmm), m.astype(np.float64))
+    assert np.array_equal(to_np(tv), v.astype(np.float64))
+    assert np.array_equal(to_np(tg), g.astype(np.float64))
+    assert np.array_equal(to_np(w), round_f32_to_bf16(master).astype(np.float64))
+
+
 @pytest.mark.parametrize("n,mb", [(5, 1), (4096, 3), (1000003, 4)])
 def test_accumulate_norm_then_update(n, mb):
     """The norm folded into the last micro-batch's accumulation, then the update
