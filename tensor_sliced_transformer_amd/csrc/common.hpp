@@ -206,6 +206,16 @@ __device__ __forceinline__ void dtl16_at(i32x4_t rsrc, uint32_t lds_addr, uint32
                : "memory", "m0");
 }
 
+// As dtl16_at, with a wave-uniform byte offset `soff` added to every lane's `off`.
+__device__ __forceinline__ void dtl16_at_so(i32x4_t rsrc, uint32_t lds_addr, uint32_t off, uint32_t soff) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(off), "s"(rsrc), "s"(lds), "s"(so)
+               : "memory", "m0");
+}
+
 // As dtl16, with a wave-uniform byte offset `soff` added to every lane's `off`.
 __device__ __forceinline__ void dtl16_so(i32x4_t rsrc, const void* lds_base, uint32_t off, uint32_t soff) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MTNLG_LDS(lds_base));

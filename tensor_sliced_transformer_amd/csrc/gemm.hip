@@ -921,6 +921,25 @@ struct Dtl64 {
                                            uint32_t dst, int wave) const {
     dtl16_at(rs, dst + (uint32_t)(wave * PER_WAVE + u + QOFF) * 1024u, goff<QOFF>(u, ld, rb0, rmax, k0, kend));
   }
+  // Whole K tiles (every K tile of every item in range; M/N-contiguous
+  // layout): the lane's byte offset of its first k row at the item's first k,
+  // per column parity (kOob past rmax); load u (+ QOFF) of K tile t adds the
+  // wave-uniform rest, (64 t + (u + QOFF) STEP) rows, as the instruction's
+  // scalar offset, so a load costs no vector arithmetic.
+  uint32_t vbase[2];
+  __device__ __forceinline__ void item_base(int64_t ld, int rb0, int rmax, int kbeg) {
+    static_assert(!KC, "scalar-offset loads are for the M/N-contiguous layout");
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int m = rb0 + cpar[e];
+      vbase[e] = m < rmax ? (uint32_t)(((int64_t)(kbeg + r0) * ld + m) * 2) : kOob;
+    }
+  }
+  template <int QOFF = 0>
+  __device__ __forceinline__ void load_fullk(int u, i32x4_t rs, int64_t ld, int t, uint32_t dst, int wave) const {
+    const uint32_t so = (uint32_t)(((int64_t)t * kBK64 + (u + QOFF) * STEP) * ld * 2);
+    dtl16_at_so(rs, dst + (uint32_t)(wave * PER_WAVE + u + QOFF) * 1024u, vbase[u & 1], so);
+  }
 };
 
 __device__ __forceinline__ int kc64_frag_off(int rb32, int s, int lane) {
@@ -929,8 +948,9 @@ __device__ __forceinline__ int kc64_frag_off(int rb32, int s, int lane) {
   return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, int WM, int WN, int EPI>
+template <int BM, int BN, bool A_KC, bool B_KC, int WM, int WN, int EPI, bool FULLK>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs p) {
+  static_assert(!FULLK || (!A_KC && !B_KC), "scalar-offset loads only for M/N-contiguous operands");
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -1006,12 +1026,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
     for (int i = 1; i < FM; ++i) read_a(st, s, buf, i);
   };
   // every wave's share of K-tile t of the tile at (tm0, tn0) from k offset kb
+  // (FULLK: of the item whose bases item_base set)
   auto issue = [&](int t, int tm0, int tn0, int kb, int ke) {
     const uint32_t st = lds0 + (uint32_t)((t & 1) * SS);
 #pragma unroll
-    for (int u = 0; u < OA::PER_WAVE; ++u) oa.load_one(u, ra, p.lda, tm0, p.M, kb + t * kBK64, ke, st, wave);
+    for (int u = 0; u < OA::PER_WAVE; ++u) {
+      if constexpr (FULLK) oa.load_fullk(u, ra, p.lda, t, st, wave);
+      else oa.load_one(u, ra, p.lda, tm0, p.M, kb + t * kBK64, ke, st, wave);
+    }
 #pragma unroll
-    for (int u = 0; u < OB::PER_WAVE; ++u) ob.load_one(u, rb, p.ldb, tn0, p.N, kb + t * kBK64, ke, st + SA, wave);
+    for (int u = 0; u < OB::PER_WAVE; ++u) {
+      if constexpr (FULLK) ob.load_fullk(u, rb, p.ldb, t, st + SA, wave);
+      else ob.load_one(u, rb, p.ldb, tn0, p.N, kb + t * kBK64, ke, st + SA, wave);
+    }
+  };
+  auto item_bases = [&]() {
+    if constexpr (FULLK) {
+      oa.item_base(p.lda, m0, p.M, kbeg);
+      ob.item_base(p.ldb, n0, p.N, kbeg);
+    }
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
@@ -1042,10 +1075,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
     const int k0 = kbeg + t * kBK64;
     constexpr int PA = OA::PER_WAVE, PB = OB::PER_WAVE;
     constexpr int QA = NW / 2 * PA, QB = NW / 2 * PB;  // the partner's loads, as offsets of this wave's
-    if (u < PA) oa.load_one(u, ra, p.lda, m0, p.M, k0, kend, st, wave);
-    else if (u < PA + PB) ob.load_one(u - PA, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave);
-    else if (u < 2 * PA + PB) oa.template load_one<QA>(u - PA - PB, ra, p.lda, m0, p.M, k0, kend, st, wave);
-    else ob.template load_one<QB>(u - 2 * PA - PB, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave);
+    if constexpr (FULLK) {
+      if (u < PA) oa.load_fullk(u, ra, p.lda, t, st, wave);
+      else if (u < PA + PB) ob.load_fullk(u - PA, rb, p.ldb, t, st + SA, wave);
+      else if (u < 2 * PA + PB) oa.template load_fullk<QA>(u - PA - PB, ra, p.lda, t, st, wave);
+      else ob.template load_fullk<QB>(u - 2 * PA - PB, rb, p.ldb, t, st + SA, wave);
+    } else {
+      if (u < PA) oa.load_one(u, ra, p.lda, m0, p.M, k0, kend, st, wave);
+      else if (u < PA + PB) ob.load_one(u - PA, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave);
+      else if (u < 2 * PA + PB) oa.template load_one<QA>(u - PA - PB, ra, p.lda, m0, p.M, k0, kend, st, wave);
+      else ob.template load_one<QB>(u - 2 * PA - PB, rb, p.ldb, n0, p.N, k0, kend, st + SA, wave);
+    }
   };
   constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // loads per tile per wave when every wave loads
   constexpr int NL2 = 2 * NL;                      // per loading wave in the loop
@@ -1054,6 +1094,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
   // K-tiles 0 and 1 of the first work item; later items have theirs issued
   // before the previous item's epilogue.
   lane_setup();
+  item_bases();
   if (nk > 0) issue(0, m0, n0, kbeg, kend);
   if (nk > 1) issue(1, m0, n0, kbeg, kend);
   bool first = true;
@@ -1140,6 +1181,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dtl64_kernel(GemmArgs 
       kbeg = tw.kbeg;
       kend = tw.kend;
       nk = (kend - kbeg + kBK64 - 1) / kBK64;
+      item_bases();
       if (nk > 0) issue(0, m0, n0, kbeg, kend);
       if (nk > 1) issue(1, m0, n0, kbeg, kend);
     }
@@ -1450,8 +1492,10 @@ void launch_256(const GemmArgs& a, dim3 grid, bool fullk, hipStream_t st) {
       hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, true, EPI>), grid, dim3(512), 0, st, a);
     else
       hipLaunchKernelGGL((gemm_bf16_rs_kernel<2, 4, AK, BKc, false, EPI>), grid, dim3(512), 0, st, a);
+  } else if (fullk) {
+    hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<256, 256, AK, BKc, 2, 4, EPI, true>), grid, dim3(512), 0, st, a);
   } else {
-    hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<256, 256, AK, BKc, 2, 4, EPI>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_dtl64_kernel<256, 256, AK, BKc, 2, 4, EPI, false>), grid, dim3(512), 0, st, a);
   }
 }
 
