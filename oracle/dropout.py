@@ -118,6 +118,34 @@ def mask(shape, p: float, seed: int, site: int) -> np.ndarray:
     return (draws16(n, seed, site) >= threshold(p)).reshape(shape)
 
 
+def attention_keep(batch: int, heads, seq: int, p: float, seed: int, site: int) -> np.ndarray:
+    """Keep mask (bool [batch, len(heads), seq, seq]) of dropout on the
+    attention probabilities of the given (global) heads.
+
+    Reading: the pages name dropout only on the row-sliced output; the
+    attention probabilities get their own counter-based mask, keyed so that
+    one generator call serves a 4 x 4 block of (query, key) pairs. Element
+    (b, head, q, k) draws from Philox4x64-10 with counter
+    (q // 4, k // 4, head, b) and key (seed, site) the 16 bits at
+    16 * (k % 4) of word q % 4, and is kept when that draw is >= thr (as
+    ``mask``). The global head index makes the mask the same however the heads
+    are split into slices.
+    """
+    heads = np.asarray(heads, dtype=np.uint64)
+    nq = (seq + 3) // 4
+    qb, kb = np.meshgrid(np.arange(nq, dtype=np.uint64), np.arange(nq, dtype=np.uint64), indexing="ij")
+    thr = threshold(p)
+    out = np.empty((batch, len(heads), nq * 4, nq * 4), dtype=bool)
+    shifts = np.array([0, 16, 32, 48], dtype=np.uint64)
+    for b in range(batch):
+        for j, hg in enumerate(heads):
+            ctr = np.stack([qb, kb, np.full_like(qb, hg), np.full_like(qb, b)], axis=-1)   # [nq, nq, 4]
+            words = philox4x64(ctr, (seed, site))                                          # [nq, nq, 4]: word = q % 4
+            d = (words[:, :, :, None] >> shifts[None, None, None, :]) & np.uint64(0xFFFF)   # [qb, kb, q%4, k%4]
+            out[b, j] = (d >= thr).transpose(0, 2, 1, 3).reshape(nq * 4, nq * 4)
+    return out[:, :, :seq, :seq]
+
+
 def dropout_sum_fwd(partials, residual, bias, p: float, seed: int, site: int) -> np.ndarray:
     """out = residual + mask * scale * (sum of partials + bias)."""
     z = np.zeros_like(np.asarray(residual, dtype=np.float64))

@@ -155,13 +155,17 @@ def causal_mask(seq: int) -> np.ndarray:
     return np.tril(np.ones((seq, seq), dtype=bool))
 
 
-def attention_fwd(qkv: np.ndarray, batch: int, seq: int, nh: int, d: int):
+def attention_fwd(qkv: np.ndarray, batch: int, seq: int, nh: int, d: int, drop=None):
     """Causal multi-head attention of nh heads of width d.
 
     Per sequence and head: S = Q K^T / sqrt(d); S[r, c] = -inf for c > r;
     P = softmax over each row (max subtracted); O = P V. Returns
     (O [T, nh*d], P [batch, nh, seq, seq], lse [batch, nh, seq]) where
     lse = log sum_c exp(S[r, c]) over the visible keys.
+
+    drop: None, or (keep [batch, nh, seq, seq] bool, scale) for dropout on the
+    probabilities: O = (P * keep * scale) V. P and lse stay those of the
+    softmax itself (the normaliser is taken before dropout).
     """
     q, k, v = _split_qkv(qkv, batch, seq, nh, d)
     s = np.matmul(q, k.transpose(0, 1, 3, 2)) / np.sqrt(d)
@@ -170,22 +174,28 @@ def attention_fwd(qkv: np.ndarray, batch: int, seq: int, nh: int, d: int):
     e = np.exp(s - mx)
     z = e.sum(axis=-1, keepdims=True)
     p = e / z
-    o = np.matmul(p, v)
+    pd = p if drop is None else np.where(drop[0], p * drop[1], 0.0)
+    o = np.matmul(pd, v)
     lse = (mx + np.log(z))[..., 0]
     return _merge_heads(o), p, lse
 
 
 def attention_bwd(qkv: np.ndarray, p: np.ndarray, do: np.ndarray, batch: int, seq: int,
-                  nh: int, d: int) -> np.ndarray:
+                  nh: int, d: int, drop=None) -> np.ndarray:
     """Gradient of causal attention. Returns dQKV [T, 3*nh*d] (same column order).
 
-    dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(dP * P));
+    dV = P~^T dO with P~ = P (or P * keep * scale under dropout); the gradient
+    reaching the probabilities is dP = dO V^T (times keep * scale under
+    dropout); dS = P * (dP - rowsum(dP * P)) (softmax's own backward, on P);
     dQ = dS K / sqrt(d); dK = dS^T Q / sqrt(d).
     """
     q, k, v = _split_qkv(qkv, batch, seq, nh, d)
     dob = do.reshape(batch, seq, nh, d).transpose(0, 2, 1, 3)
-    dv = np.matmul(p.transpose(0, 1, 3, 2), dob)
+    pd = p if drop is None else np.where(drop[0], p * drop[1], 0.0)
+    dv = np.matmul(pd.transpose(0, 1, 3, 2), dob)
     dp = np.matmul(dob, v.transpose(0, 1, 3, 2))
+    if drop is not None:
+        dp = np.where(drop[0], dp * drop[1], 0.0)
     ds = p * (dp - (dp * p).sum(axis=-1, keepdims=True))
     scale = 1.0 / np.sqrt(d)
     dq = np.matmul(ds, k) * scale
@@ -248,7 +258,7 @@ def _keep(a: np.ndarray) -> np.ndarray:
     return a
 
 
-def attn_half_fwd(sh: LayerShape, x: np.ndarray, p: dict, store=None, store_qk=None):
+def attn_half_fwd(sh: LayerShape, x: np.ndarray, p: dict, store=None, store_qk=None, attn_drop=None):
     """Attention half of slice i. Returns (partial, saved).
 
     partial = Attn_i(LN1(x)) W_o,i, without bias or residual: the operand of
@@ -263,6 +273,9 @@ def attn_half_fwd(sh: LayerShape, x: np.ndarray, p: dict, store=None, store_qk=N
     from storing those tensors in bf16 from the error of the kernels.
     store_qk, if given, rounds the Q and K columns of QKV instead of store
     (a library may keep them in another 16-bit format).
+    attn_drop: None, or (p, seed, site, head0) for dropout on the attention
+    probabilities of this slice's heads head0 .. head0 + local_heads - 1
+    (global head indices; oracle.dropout.attention_keep).
     """
     rnd = store or _keep
     y, mean, rstd, xhat = layernorm_fwd(x, p["ln_g"], p["ln_b"], sh.eps)
@@ -270,11 +283,17 @@ def attn_half_fwd(sh: LayerShape, x: np.ndarray, p: dict, store=None, store_qk=N
     qkv = y @ p["w_in"] + p["b_in"][None, :]
     qk = 2 * sh.local_width
     qkv = np.concatenate([(store_qk or rnd)(qkv[:, :qk]), rnd(qkv[:, qk:])], axis=1)
-    o, prob, lse = attention_fwd(qkv, sh.batch, sh.seq, sh.local_heads, sh.head_dim)
+    drop = None
+    if attn_drop is not None and attn_drop[0] > 0.0:
+        from oracle import dropout as OD
+        rate, seed, site, head0 = attn_drop
+        heads = np.arange(head0, head0 + sh.local_heads)
+        drop = (OD.attention_keep(sh.batch, heads, sh.seq, rate, seed, site), OD.keep_scale(rate))
+    o, prob, lse = attention_fwd(qkv, sh.batch, sh.seq, sh.local_heads, sh.head_dim, drop)
     o = rnd(o)
     partial = o @ p["w_out"]
     saved = {"ln_out": y, "mean": mean, "rstd": rstd, "xhat": xhat,
-             "qkv": qkv, "o": o, "p": prob, "lse": lse}
+             "qkv": qkv, "o": o, "p": prob, "lse": lse, "drop": drop}
     return partial, saved
 
 
@@ -291,7 +310,7 @@ def attn_half_bwd(sh: LayerShape, g: np.ndarray, p: dict, saved: dict):
     do = g @ p["w_out"].T
     dw_out = saved["o"].T @ g
     dqkv = attention_bwd(saved["qkv"], saved["p"], do, sh.batch, sh.seq,
-                         sh.local_heads, sh.head_dim)
+                         sh.local_heads, sh.head_dim, saved.get("drop"))
     dw_in = saved["ln_out"].T @ dqkv
     db_in = dqkv.sum(axis=0)
     dln = dqkv @ p["w_in"].T
@@ -353,13 +372,18 @@ def reduce_partials(partials, residual: np.ndarray, bias: np.ndarray | None) -> 
     return out
 
 
-def layer_fwd(sh: LayerShape, x: np.ndarray, full: dict):
-    """Full layer output from sh.tp slices run in turn. Returns (out, state)."""
+def layer_fwd(sh: LayerShape, x: np.ndarray, full: dict, attn_drop=None):
+    """Full layer output from sh.tp slices run in turn. Returns (out, state).
+
+    attn_drop: None, or (p, seed, site) for dropout on the attention
+    probabilities (slice i's heads are global heads i*H/t .. (i+1)*H/t - 1).
+    """
     sh.check()
     t = sh.tp
     ap = [attn_slice(sh, full, i) for i in range(t)]
     mp = [mlp_slice(sh, full, i) for i in range(t)]
-    a_fwd = [attn_half_fwd(sh, x, ap[i]) for i in range(t)]
+    drops = [None if attn_drop is None else (*attn_drop, i * sh.local_heads) for i in range(t)]
+    a_fwd = [attn_half_fwd(sh, x, ap[i], attn_drop=drops[i]) for i in range(t)]
     x1 = reduce_partials([r[0] for r in a_fwd], x, full["b_o"])
     m_fwd = [mlp_half_fwd(sh, x1, mp[i]) for i in range(t)]
     out = reduce_partials([r[0] for r in m_fwd], x1, full["b_b"])
@@ -443,7 +467,7 @@ def layer_bwd(sh: LayerShape, g: np.ndarray, full: dict, state: dict):
     return dx, grads
 
 
-def layer_loss(sh: LayerShape, x: np.ndarray, full: dict, g: np.ndarray) -> float:
+def layer_loss(sh: LayerShape, x: np.ndarray, full: dict, g: np.ndarray, attn_drop=None) -> float:
     """L = <Out, g>: the upstream gradient g stands in for a loss (a single layer has none)."""
-    out, _ = layer_fwd(sh, x, full)
+    out, _ = layer_fwd(sh, x, full, attn_drop)
     return float((out * g).sum())

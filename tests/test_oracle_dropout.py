@@ -140,3 +140,93 @@ def test_layer_with_dropout_finite_differences():
     assert not np.allclose(out_p, out_0)
     out_z, _ = D.layer_fwd(sh, x, full, 0.0, seed)
     np.testing.assert_allclose(out_z, out_0, rtol=0, atol=1e-12)
+
+
+# ---- dropout on the attention probabilities ----
+
+def test_attention_keep_layout_follows_blocks():
+    """Element (b, head, q, k) takes bits 16*(k%4).. of word q%4 of the block at
+    counter (q//4, k//4, head, b)."""
+    keep_p = 0.5
+    thr = D.threshold(keep_p)
+    m = D.attention_keep(2, [3, 5], 12, keep_p, seed=21, site=4)
+    for (b, j, q, k) in ((0, 0, 0, 0), (1, 1, 11, 2), (0, 1, 7, 7), (1, 0, 4, 9), (0, 0, 10, 3)):
+        head = [3, 5][j]
+        w = D.philox4x64_scalar([q // 4, k // 4, head, b], (21, 4))[q % 4]
+        assert bool(m[b, j, q, k]) == (((w >> (16 * (k % 4))) & 0xFFFF) >= thr)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5])
+def test_attention_keep_fraction(p):
+    m = D.attention_keep(1, [0, 1, 2, 3], 256, p, seed=8, site=1)
+    n = m.size
+    q = 1.0 - D.threshold(p) / 65536.0
+    assert abs(m.mean() - q) <= 5.0 * np.sqrt(q * (1 - q) / n)
+    assert np.all(D.attention_keep(1, [0], 16, 0.0, 8, 1))
+    # heads and sites draw independently: agreement at the rate of independent coins
+    other = D.attention_keep(1, [4, 5, 6, 7], 256, p, seed=8, site=1)
+    site2 = D.attention_keep(1, [0, 1, 2, 3], 256, p, seed=8, site=2)
+    want = q * q + (1 - q) * (1 - q)
+    for y in (other, site2):
+        agree = float((m == y).mean())
+        assert abs(agree - want) <= 5.0 * np.sqrt(want * (1 - want) / n)
+
+
+def test_attention_dropout_rate_zero_and_expectation():
+    """A mask of all ones at scale 1 is attention itself; over many seeds the
+    dropped output averages to the undropped one (E[keep * scale] = 1)."""
+    r = np.random.default_rng(3)
+    b, s, nh, d = 1, 8, 1, 4
+    qkv = r.standard_normal((b * s, 3 * nh * d))
+    o0, p0, l0 = OL.attention_fwd(qkv, b, s, nh, d)
+    ones = (np.ones((b, nh, s, s), dtype=bool), 1.0)
+    o1, p1, l1 = OL.attention_fwd(qkv, b, s, nh, d, ones)
+    assert np.array_equal(o0, o1) and np.array_equal(p0, p1) and np.array_equal(l0, l1)
+    do = r.standard_normal((b * s, nh * d))
+    assert np.array_equal(OL.attention_bwd(qkv, p0, do, b, s, nh, d), OL.attention_bwd(qkv, p0, do, b, s, nh, d, ones))
+    p, n = 0.5, 4000
+    acc = np.zeros_like(o0)
+    for seed in range(n):
+        drop = (D.attention_keep(b, [0], s, p, seed, 0), D.keep_scale(p))
+        acc += OL.attention_fwd(qkv, b, s, nh, d, drop)[0]
+    # each output is a sum of at most 8 terms keep*scale*p*v; the mean of n
+    # independent draws is within a few standard errors of the expectation
+    sd = np.sqrt(np.matmul(p0.reshape(s, s) ** 2, (qkv[:, 2 * nh * d:] ** 2)) * (D.keep_scale(p) - 1.0))
+    assert np.all(np.abs(acc / n - o0) <= 6.0 * sd / np.sqrt(n) + 1e-12)
+
+
+def test_layer_with_attention_dropout_finite_differences_and_slicing():
+    """With the attention mask fixed by (seed, site), the layer is smooth: input
+    and QKV-weight gradients match central differences of L = <out, g>; and the
+    global head index makes the result independent of the slicing (t = 1 vs 2)."""
+    r = np.random.default_rng(11)
+    shapes = [OL.LayerShape(batch=2, seq=12, hidden=16, heads=4, ffn=32, tp=t) for t in (1, 2)]
+    sh = shapes[1]
+    full = {}
+    for k, s in OL.full_param_shapes(sh).items():
+        full[k] = (1.0 + 0.2 * r.standard_normal(s)) if k in ("ln1_g", "ln2_g") else 0.4 * r.standard_normal(s)
+    x = r.standard_normal((sh.tokens, sh.hidden))
+    g = r.standard_normal((sh.tokens, sh.hidden))
+    drop = (0.3, 1234, 5)
+    out2, st = OL.layer_fwd(sh, x, full, drop)
+    out1, _ = OL.layer_fwd(shapes[0], x, full, drop)
+    np.testing.assert_allclose(out1, out2, rtol=0, atol=1e-12)
+    out0, _ = OL.layer_fwd(sh, x, full)
+    assert not np.allclose(out0, out2)
+    dx, grads = OL.layer_bwd(sh, g, full, st)
+    delta = 1e-5
+    u = r.standard_normal(x.shape)
+    fd = (OL.layer_loss(sh, x + delta * u, full, g, drop) - OL.layer_loss(sh, x - delta * u, full, g, drop)) \
+        / (2 * delta)
+    an = float((dx * u).sum())
+    assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0)
+    uw = r.standard_normal(full["w_qkv"].shape)
+
+    def loss_w(s):
+        q = dict(full)
+        q["w_qkv"] = full["w_qkv"] + s * uw
+        return OL.layer_loss(sh, x, q, g, drop)
+
+    fd = (loss_w(delta) - loss_w(-delta)) / (2 * delta)
+    an = float((grads["w_qkv"] * uw).sum())
+    assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0)
