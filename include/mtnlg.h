@@ -86,12 +86,31 @@ typedef enum { MTNLG_ATTN = 0, MTNLG_MLP = 1 } mtnlg_half;
  * 3*hidden/tp_size and ffn/tp_size), the range of the GEMM's 32-bit buffer
  * offsets (bf16 at hidden 20480: at most 52428 tokens); dtype F32 or BF16;
  * ln_eps > 0 and finite. Violations return MTNLG_ERR_SHAPE, MTNLG_ERR_DTYPE
- * or MTNLG_ERR_ARG before any launch. */
+ * or MTNLG_ERR_ARG before any launch.
+ *
+ * Dropout on the attention probabilities (ATTN half; the MLP half ignores
+ * these fields): attn_dropout = rate p, 0 <= p < 1 (0: none; p must round to
+ * a threshold below 65536 as for mtnlg_reduce_partials_dropout), BF16 only
+ * (MTNLG_ERR_UNIMPLEMENTED for F32 with p > 0). The softmax normaliser is
+ * taken before dropout: O = (P * keep * scale) V with scale = 65536 /
+ * (65536 - thr), thr = round(p * 65536). Element (b, head, q, k) -- b the
+ * sequence, head the GLOBAL head index tp_rank * heads/tp_size + local head,
+ * q and k positions in the sequence -- is kept when the 16-bit draw at bits
+ * 16 * (k % 4) of word q % 4 of Philox4x64-10 at counter (q/4, k/4, head, b)
+ * under key (attn_dropout_seed, attn_dropout_site) is >= thr. This reading
+ * is the library's: the pages name dropout only on the row-sliced output
+ * (STRONGHOLD slide deck, slide 8). layer_bwd (and the recompute variant)
+ * regenerate the same mask from the same fields, so the forward and backward
+ * of one micro-batch must pass equal values; callers vary the site per layer
+ * and micro-batch. */
 typedef struct {
   int32_t batch, seq, hidden, heads, ffn;
   int32_t tp_size, tp_rank;
   int32_t dtype;       /* mtnlg_dtype */
   float ln_eps;
+  float attn_dropout;          /* rate on the attention probabilities (0: none) */
+  uint64_t attn_dropout_seed;  /* generator key, first word */
+  uint64_t attn_dropout_site;  /* generator key, second word */
 } mtnlg_layer_desc;
 
 /* Parameters of one slice of one half, all in desc->dtype:
@@ -349,6 +368,9 @@ typedef struct {
   uint64_t dropout_seed;   /* the generator key's first word; the site of micro-batch k,
                               layer l, half h is (k * layers + l) * 2 + h */
 } mtnlg_stage_desc;
+/* layer.attn_dropout > 0 also drops attention probabilities: micro-batch k,
+ * layer l keys its mask with (layer.attn_dropout_seed,
+ * layer.attn_dropout_site + k * layers + l), in its forward and its backward. */
 
 /* The stage's parameters live in ONE flat element array (the bf16 weights,
  * the bf16 gradients and the fp32 master, m, v and accumulator all share this

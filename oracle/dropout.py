@@ -163,15 +163,18 @@ def dropout_bwd(g, p: float, seed: int, site: int) -> np.ndarray:
     return np.where(keep, np.asarray(g, dtype=np.float64) * keep_scale(p), 0.0)
 
 
-def layer_fwd(sh, x, full, p: float, seed: int, sites=(0, 1)):
+def layer_fwd(sh, x, full, p: float, seed: int, sites=(0, 1), attn_drop=None):
     """The sliced layer of ``oracle.layer.layer_fwd`` with dropout on the output of
     each half (after the slices' partials and the row-sliced bias are summed,
-    before the residual). sites = (attention site, MLP site). Returns (out, state)."""
+    before the residual). sites = (attention site, MLP site). attn_drop: None,
+    or (rate, seed, site) for dropout on the attention probabilities as in
+    ``oracle.layer.layer_fwd``. Returns (out, state)."""
     from . import layer as OL
     t = sh.tp
     ap = [OL.attn_slice(sh, full, i) for i in range(t)]
     mp = [OL.mlp_slice(sh, full, i) for i in range(t)]
-    a_fwd = [OL.attn_half_fwd(sh, x, ap[i]) for i in range(t)]
+    drops = [None if attn_drop is None else (*attn_drop, i * sh.local_heads) for i in range(t)]
+    a_fwd = [OL.attn_half_fwd(sh, x, ap[i], attn_drop=drops[i]) for i in range(t)]
     x1 = dropout_sum_fwd([r[0] for r in a_fwd], x, full["b_o"], p, seed, sites[0])
     m_fwd = [OL.mlp_half_fwd(sh, x1, mp[i]) for i in range(t)]
     out = dropout_sum_fwd([r[0] for r in m_fwd], x1, full["b_b"], p, seed, sites[1])
@@ -195,6 +198,6 @@ def layer_bwd(sh, g, state, p: float, seed: int, sites=(0, 1)):
     return dx, [r[1] for r in a_b], [r[1] for r in m_b]
 
 
-def layer_loss(sh, x, full, g, p: float, seed: int, sites=(0, 1)) -> float:
-    out, _ = layer_fwd(sh, x, full, p, seed, sites)
+def layer_loss(sh, x, full, g, p: float, seed: int, sites=(0, 1), attn_drop=None) -> float:
+    out, _ = layer_fwd(sh, x, full, p, seed, sites, attn_drop)
     return float((out * g).sum())

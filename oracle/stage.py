@@ -26,6 +26,8 @@ Readings:
 * With dropout (``oracle.dropout``), each half's output of micro-batch k and
   layer l uses its own site, (k * layers + l) * 2 + half, so that no two
   dropout masks of a step coincide.
+* With dropout on the attention probabilities (rate, seed, site0), layer l of
+  micro-batch k keys its mask with (seed, site0 + k * layers + l).
 """
 from __future__ import annotations
 
@@ -41,12 +43,22 @@ FLAT_ORDER = (("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o"),
               ("ln2_g", "ln2_b", "w_a", "b_a", "w_b", "b_b"))
 
 
-def stage_fwd(sh: OL.LayerShape, layers: list, x: np.ndarray):
-    """Output of the chained layers for input x, and the per-layer states."""
+def attn_drops(n_layers: int, k: int, attn_dropout):
+    """Per-layer attention-probability dropout of micro-batch k: None each, or
+    (rate, seed, site0 + k * layers + l) for attn_dropout = (rate, seed, site0)."""
+    if attn_dropout is None or attn_dropout[0] <= 0.0:
+        return [None] * n_layers
+    rate, seed, site0 = attn_dropout
+    return [(rate, seed, site0 + k * n_layers + l) for l in range(n_layers)]
+
+
+def stage_fwd(sh: OL.LayerShape, layers: list, x: np.ndarray, drops=None):
+    """Output of the chained layers for input x, and the per-layer states.
+    drops: None, or each layer's attention-probability dropout (attn_drops)."""
     states = []
     h = x
-    for full in layers:
-        h, st = OL.layer_fwd(sh, h, full)
+    for l, full in enumerate(layers):
+        h, st = OL.layer_fwd(sh, h, full, None if drops is None else drops[l])
         states.append(st)
     return h, states
 
@@ -74,18 +86,18 @@ def flatten(layer_dicts: list) -> np.ndarray:
     return np.concatenate(parts)
 
 
-def _stage_dropout(sh: OL.LayerShape, layers: list, x, g, k: int, p: float, seed: int):
+def _stage_dropout(sh: OL.LayerShape, layers: list, x, g, k: int, p: float, seed: int, drops=None):
     """One micro-batch through the stage with dropout on every half's output
     (``oracle.dropout``): the site of micro-batch k, layer l, half h is
     (k * layers + l) * 2 + h. One slice (t = 1), so a slice's gradients are
-    the layer's."""
+    the layer's. drops: None, or each layer's attention-probability dropout."""
     from . import dropout as OD
     assert sh.tp == 1
     nl = len(layers)
     sites = [((k * nl + l) * 2, (k * nl + l) * 2 + 1) for l in range(nl)]
     states, h = [], x
     for l, full in enumerate(layers):
-        h, st = OD.layer_fwd(sh, h, full, p, seed, sites[l])
+        h, st = OD.layer_fwd(sh, h, full, p, seed, sites[l], None if drops is None else drops[l])
         states.append(st)
     y = h
     grads = [None] * nl
@@ -99,15 +111,17 @@ def _stage_dropout(sh: OL.LayerShape, layers: list, x, g, k: int, p: float, seed
     return y, g, grads
 
 
-def stage_micro_batches(sh: OL.LayerShape, layers: list, xs, gs, dropout=None):
+def stage_micro_batches(sh: OL.LayerShape, layers: list, xs, gs, dropout=None, attn_dropout=None):
     """Forward and backward of every micro-batch. Returns (ys, dxs, per-micro-batch
-    flat gradients). dropout = (p, seed) puts dropout on every half's output."""
+    flat gradients). dropout = (p, seed) puts dropout on every half's output;
+    attn_dropout = (rate, seed, site0) on the attention probabilities."""
     ys, dxs, flats = [], [], []
     for k, (x, g) in enumerate(zip(xs, gs)):
+        drops = attn_drops(len(layers), k, attn_dropout)
         if dropout is not None and dropout[0] > 0.0:
-            y, dx, grads = _stage_dropout(sh, layers, x, g, k, dropout[0], dropout[1])
+            y, dx, grads = _stage_dropout(sh, layers, x, g, k, dropout[0], dropout[1], drops)
         else:
-            y, states = stage_fwd(sh, layers, x)
+            y, states = stage_fwd(sh, layers, x, drops)
             dx, grads = stage_bwd(sh, layers, states, g)
         ys.append(y)
         dxs.append(dx)

@@ -61,8 +61,11 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def make_desc(batch, seq, hidden, heads, ffn, tp_size=1, tp_rank=0, dtype=BF16, ln_eps=1e-5) -> LayerDesc:
-    return LayerDesc(batch, seq, hidden, heads, ffn, tp_size, tp_rank, dtype, ln_eps)
+def make_desc(batch, seq, hidden, heads, ffn, tp_size=1, tp_rank=0, dtype=BF16, ln_eps=1e-5,
+              attn_dropout=0.0, attn_dropout_seed=0, attn_dropout_site=0) -> LayerDesc:
+    """mtnlg_layer_desc; attn_dropout > 0 drops attention probabilities (BF16)."""
+    return LayerDesc(batch, seq, hidden, heads, ffn, tp_size, tp_rank, dtype, ln_eps, attn_dropout,
+                     attn_dropout_seed, attn_dropout_site)
 
 
 def saved_bytes(desc: LayerDesc, half: int) -> int:

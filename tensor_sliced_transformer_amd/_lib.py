@@ -25,7 +25,8 @@ ATTN, MLP = 0, 1
 class LayerDesc(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("seq", c_int32), ("hidden", c_int32), ("heads", c_int32),
                 ("ffn", c_int32), ("tp_size", c_int32), ("tp_rank", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float)]
+                ("ln_eps", c_float), ("attn_dropout", c_float), ("attn_dropout_seed", ctypes.c_uint64),
+                ("attn_dropout_site", ctypes.c_uint64)]
 
 
 class StageDesc(ctypes.Structure):

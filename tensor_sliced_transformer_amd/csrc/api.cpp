@@ -57,6 +57,12 @@ int validate_desc(const mtnlg_layer_desc* desc, int32_t half, Dims* out) {
   if ((int64_t)D.seq * 3 * D.hidden / D.tp_size * (int64_t)elem_bytes(D.dtype) >= ((int64_t)1 << 31))
     return fail(MTNLG_ERR_SHAPE, "one sequence of the QKV activations must stay below 2 GiB");
   if (!(D.ln_eps > 0.0f) || !isfinite(D.ln_eps)) return fail(MTNLG_ERR_ARG, "ln_eps must be positive and finite");
+  if (!(D.attn_dropout >= 0.0f && D.attn_dropout < 1.0f))
+    return fail(MTNLG_ERR_ARG, "attn_dropout must be in [0, 1)");
+  if (nearbyint((double)D.attn_dropout * 65536.0) >= 65536.0)
+    return fail(MTNLG_ERR_ARG, "attn_dropout rounds to 1");
+  if (D.attn_dropout > 0.0f && D.dtype != MTNLG_BF16)
+    return fail(MTNLG_ERR_UNIMPLEMENTED, "dropout on the attention probabilities needs the BF16 path");
   const int64_t T = (int64_t)D.batch * D.seq;
   {
     // every GEMM operand of the layer (activations T x width, weights) must
@@ -151,6 +157,17 @@ WsLayout ws_layout(const Dims& d, int half) {
   return L;
 }
 
+// The attention-probability dropout of a layer call (thr 0: none).
+AttnDropout attn_dropout(const mtnlg_layer_desc* desc, const Dims& d) {
+  AttnDropout a{};
+  a.thr = (uint32_t)nearbyint((double)desc->attn_dropout * 65536.0);
+  a.scale = a.thr ? (float)(65536.0 / (65536.0 - (double)a.thr)) : 1.0f;
+  a.seed = desc->attn_dropout_seed;
+  a.site = desc->attn_dropout_site;
+  a.head0 = desc->tp_rank * (int)d.nhl;
+  return a;
+}
+
 char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
 
@@ -175,7 +192,8 @@ int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mt
                    f16qk ? EPI_BIAS_F16LO : EPI_BIAS, params->b_in, nullptr, nullptr,
                    plan_gemm(d.dtype, d.T, n3, d.h, true), gws, st, f16qk ? (int)(2 * d.w) : 0),
               "qkv gemm");
-    MTNLG_HIP(attention_fwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, st),
+    MTNLG_HIP(attention_fwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse,
+                            attn_dropout(desc, d), st),
               "attention_fwd");
     if (y_partial)
       MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.h, d.w, o, d.w, params->w_out, d.h, y_partial, d.h, EPI_STORE,
@@ -247,7 +265,7 @@ int backward_from(const mtnlg_layer_desc* desc, const Dims& d, int half, const m
                    nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, d.T, true), gws, st),
               "attn dWo gemm");
     MTNLG_HIP(attention_bwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, dO, dqkv,
-                            at(ws, W.attn), st),
+                            at(ws, W.attn), attn_dropout(desc, d), st),
               "attention_bwd");
     MTNLG_HIP(colsum(d.dtype, d.T, n3, dqkv, grads->b_in, cs, st), "attn dbqkv colsum");
     // dW_qkv = LN1(x)^T dQKV
@@ -684,7 +702,8 @@ int mtnlg_attention_fwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads
   CHECK_PTR(qkv);
   CHECK_PTR(o);
   CHECK_PTR(lse);
-  MTNLG_HIP(attention_fwd(dtype, batch, seq, heads, head_dim, qkv, o, lse, static_cast<hipStream_t>(stream)),
+  MTNLG_HIP(attention_fwd(dtype, batch, seq, heads, head_dim, qkv, o, lse, AttnDropout{},
+                          static_cast<hipStream_t>(stream)),
             "attention_fwd");
   return MTNLG_OK;
 }
@@ -706,7 +725,7 @@ int mtnlg_attention_bwd(int32_t dtype, int32_t batch, int32_t seq, int32_t heads
   CHECK_PTR(dqkv);
   CHECK_PTR(ws);
   if (ws_bytes < attention_bwd_ws(batch, seq, heads)) return fail(MTNLG_ERR_WORKSPACE, "workspace too small");
-  MTNLG_HIP(attention_bwd(dtype, batch, seq, heads, head_dim, qkv, o, lse, do_, dqkv, ws,
+  MTNLG_HIP(attention_bwd(dtype, batch, seq, heads, head_dim, qkv, o, lse, do_, dqkv, ws, AttnDropout{},
                           static_cast<hipStream_t>(stream)),
             "attention_bwd");
   return MTNLG_OK;

@@ -475,11 +475,12 @@ hipError_t bwd_launch(int batch, int seq, int heads, const void* qkv, const void
 }  // namespace
 
 hipError_t attention_fwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv, void* o,
-                         float* lse, hipStream_t st) {
+                         float* lse, const AttnDropout& drop, hipStream_t st) {
   if (batch == 0) return hipSuccess;
 #define MTNLG_AF(T, D) \
   if (head_dim == D) return fwd_launch<T, D>(batch, seq, heads, qkv, o, lse, st);
-  if (dtype == kBF16) return attention_fwd_bf16(batch, seq, heads, head_dim, qkv, o, lse, st);
+  if (dtype == kBF16) return attention_fwd_bf16(batch, seq, heads, head_dim, qkv, o, lse, drop, st);
+  if (drop.thr) return hipErrorInvalidValue;  // dropout on the probabilities: bf16 kernels only
   MTNLG_AF(float, 64) MTNLG_AF(float, 128)
 #undef MTNLG_AF
   return hipErrorInvalidValue;
@@ -489,12 +490,14 @@ hipError_t attention_fwd(int dtype, int batch, int seq, int heads, int head_dim,
 size_t attention_bwd_ws(int batch, int seq, int heads) { return (size_t)batch * seq * heads * 2 * sizeof(float); }
 
 hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv, const void* o,
-                         const float* lse, const void* dout, void* dqkv, void* ws, hipStream_t st) {
+                         const float* lse, const void* dout, void* dqkv, void* ws, const AttnDropout& drop,
+                         hipStream_t st) {
   if (batch == 0) return hipSuccess;
   float* dd = static_cast<float*>(ws);
 #define MTNLG_AB(T, D) \
   if (head_dim == D) return bwd_launch<T, D>(batch, seq, heads, qkv, o, lse, dout, dqkv, dd, st);
-  if (dtype == kBF16) return attention_bwd_bf16(batch, seq, heads, head_dim, qkv, o, lse, dout, dqkv, ws, st);
+  if (dtype == kBF16) return attention_bwd_bf16(batch, seq, heads, head_dim, qkv, o, lse, dout, dqkv, ws, drop, st);
+  if (drop.thr) return hipErrorInvalidValue;
   MTNLG_AB(float, 64) MTNLG_AB(float, 128)
 #undef MTNLG_AB
   return hipErrorInvalidValue;

@@ -58,11 +58,11 @@ constexpr float kSlack = 8.0f;
 // a three-stage ring at head_dim 160.
 constexpr int kFwdRing = 2;
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv,
                                                                bf16_t* __restrict__ o, float* __restrict__ lse,
                                                                int seq, int nh, int64_t tokens, int nbh,
-                                                               float scale_log2) {
+                                                               float scale_log2, AttnDropout drop) {
   using TL = Tile<D>;
   constexpr int EB = TL::EB, SUB = TL::SUB, STAGE = 2 * TL::BYTES;
   __shared__ __align__(1024) char smem[kFwdRing * STAGE];
@@ -137,8 +137,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float p = fast_exp2(fmaf(s[i], scale_log2, -m));
-      l += p;
+      l += p;  // the normaliser is the softmax's own, before dropout
       s[i] = p;
+    }
+    if (DROP) {
+      const uint32_t keep = attn_keep_bits<false>(drop, (uint64_t)((qw0 >> 2) + (lq >> 2)),
+                                                  (uint64_t)((kw0 >> 2) + 2 * (lq & 3) + g), drop.head0 + n, b, lane);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = ((keep >> i) & 1u) ? s[i] * drop.scale : 0.0f;
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -186,13 +192,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
 // ------------------------------------------------------------- backward: dQ
 // Same walk as the forward. Also computes, per query, D = rowsum(dO * O) and
 // L = lse * log2(e), and stores the pair for the dK/dV kernel.
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restrict__ qkv,
                                                            const bf16_t* __restrict__ o,
                                                            const bf16_t* __restrict__ dout,
                                                            const float* __restrict__ lse, float2* __restrict__ ldw,
                                                            bf16_t* __restrict__ dqkv, int seq, int nh,
-                                                           int64_t tokens, int nbh, float scale, float scale_log2) {
+                                                           int64_t tokens, int nbh, float scale, float scale_log2,
+                                                           AttnDropout drop) {
   using TL = Tile<D>;
   constexpr int EB = TL::EB, SUB = TL::SUB, STAGE = 2 * TL::BYTES;
   __shared__ __align__(1024) char smem[kRing * STAGE];
@@ -260,10 +267,20 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
       s = mma_f16(frag_row(sk, 32 * kh + lq, st, g), qf[st], s);
       dp = mma(frag_row(sv, 32 * kh + lq, st, g), df[st], dp);
     }
+    if (DROP) {  // the gradient reaching P is dO V^T * keep * scale
+      const uint32_t keep = attn_keep_bits<false>(drop, (uint64_t)((qw0 >> 2) + (lq >> 2)),
+                                                  (uint64_t)((kw0 >> 2) + 2 * (lq & 3) + g), drop.head0 + n, b, lane);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(s[i], scale_log2, -lrow));
-      dp[i] = p * (dp[i] - dsum);
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], scale_log2, -lrow));
+        dp[i] = p * ((((keep >> i) & 1u) ? dp[i] * drop.scale : 0.0f) - dsum);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], scale_log2, -lrow));
+        dp[i] = p * (dp[i] - dsum);
+      }
     }
     if (kw0 == qw0) {
 #pragma unroll
@@ -305,52 +322,54 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
 }
 
 template <int D>
-hipError_t fwd_launch(int batch, int seq, int heads, const void* qkv, void* o, float* lse, hipStream_t st) {
+hipError_t fwd_launch(int batch, int seq, int heads, const void* qkv, void* o, float* lse, const AttnDropout& drop,
+                      hipStream_t st) {
   const int nbh = batch * heads;
   const float scale_log2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3((unsigned)((seq / kRows) * nbh)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(qkv), static_cast<bf16_t*>(o), lse, seq, heads,
-                     (int64_t)batch * seq, nbh, scale_log2);
+  hipLaunchKernelGGL((drop.thr ? attn_fwd_bf16_kernel<D, true> : attn_fwd_bf16_kernel<D, false>),
+                     dim3((unsigned)((seq / kRows) * nbh)), dim3(256), 0, st, static_cast<const bf16_t*>(qkv),
+                     static_cast<bf16_t*>(o), lse, seq, heads, (int64_t)batch * seq, nbh, scale_log2, drop);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t bwd_launch(int batch, int seq, int heads, const void* qkv, const void* o, const float* lse,
-                      const void* dout, void* dqkv, float2* ldw, hipStream_t st) {
+                      const void* dout, void* dqkv, float2* ldw, const AttnDropout& drop, hipStream_t st) {
   const int nbh = batch * heads;
   const int64_t tokens = (int64_t)batch * seq;
   const float scale = 1.0f / sqrtf((float)D);
   const float scale_log2 = kLog2e * scale;
   const dim3 grid((unsigned)((seq / kRows) * nbh));
-  hipLaunchKernelGGL((attn_dq_bf16_kernel<D>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(qkv),
+  hipLaunchKernelGGL((drop.thr ? attn_dq_bf16_kernel<D, true> : attn_dq_bf16_kernel<D, false>), grid, dim3(256), 0, st, static_cast<const bf16_t*>(qkv),
                      static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), lse, ldw,
-                     static_cast<bf16_t*>(dqkv), seq, heads, tokens, nbh, scale, scale_log2);
+                     static_cast<bf16_t*>(dqkv), seq, heads, tokens, nbh, scale, scale_log2, drop);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return dkdv_bf16(batch, seq, heads, D, qkv, dout, ldw, dqkv, st);
+  return dkdv_bf16(batch, seq, heads, D, qkv, dout, ldw, dqkv, drop, st);
 }
 
 }  // namespace
 
 hipError_t attention_fwd_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, void* o, float* lse,
-                              hipStream_t st) {
+                              const AttnDropout& drop, hipStream_t st) {
   if (seq % kRows) return hipErrorInvalidValue;
   switch (head_dim) {
-    case 64: return fwd_launch<64>(batch, seq, heads, qkv, o, lse, st);
-    case 128: return fwd_launch<128>(batch, seq, heads, qkv, o, lse, st);
-    case 160: return fwd_launch<160>(batch, seq, heads, qkv, o, lse, st);
+    case 64: return fwd_launch<64>(batch, seq, heads, qkv, o, lse, drop, st);
+    case 128: return fwd_launch<128>(batch, seq, heads, qkv, o, lse, drop, st);
+    case 160: return fwd_launch<160>(batch, seq, heads, qkv, o, lse, drop, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t attention_bwd_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, const void* o,
-                              const float* lse, const void* dout, void* dqkv, void* ws, hipStream_t st) {
+                              const float* lse, const void* dout, void* dqkv, void* ws, const AttnDropout& drop,
+                              hipStream_t st) {
   if (seq % kRows) return hipErrorInvalidValue;
   float2* ldw = static_cast<float2*>(ws);
   switch (head_dim) {
-    case 64: return bwd_launch<64>(batch, seq, heads, qkv, o, lse, dout, dqkv, ldw, st);
-    case 128: return bwd_launch<128>(batch, seq, heads, qkv, o, lse, dout, dqkv, ldw, st);
-    case 160: return bwd_launch<160>(batch, seq, heads, qkv, o, lse, dout, dqkv, ldw, st);
+    case 64: return bwd_launch<64>(batch, seq, heads, qkv, o, lse, dout, dqkv, ldw, drop, st);
+    case 128: return bwd_launch<128>(batch, seq, heads, qkv, o, lse, dout, dqkv, ldw, drop, st);
+    case 160: return bwd_launch<160>(batch, seq, heads, qkv, o, lse, dout, dqkv, ldw, drop, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -155,9 +155,55 @@ __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, flo
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
+// ---- dropout on the attention probabilities ----
+//
+// Element (b, head, q, k) is kept when the 16-bit draw at bits 16 * (k % 4)
+// of word q % 4 of Philox4x64-10 at counter (q / 4, k / 4, head, b), key
+// (seed, site), is >= thr (head: the global head index). One generator call
+// thus serves a 4 x 4 block of (query, key) pairs, and the four lanes of a
+// quad (lanes 4a .. 4a+3) hold, in either accumulator layout, the 16
+// elements of four such blocks between them: each lane makes one call and a
+// transpose of 4-bit rows across the quad (two DPP exchanges) hands every
+// lane its own 16 keep bits.
+//   forward / dQ layout (query per lane column): lane 4a+t of a wave whose
+//     queries start at qw0 and keys at kw0 draws block
+//     (qw0/4 + a, kw0/4 + 2t + g);
+//   dK/dV layout (key per lane column): block (qw0/4 + 2t + g, kw0/4 + a),
+//     its bits transposed within the 4 x 4 block first.
+// Bit i of the result is the keep bit of accumulator slot i.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <bool KEY_LANES>
+__device__ __forceinline__ uint32_t attn_keep_bits(const AttnDropout& d, uint64_t c0, uint64_t c1, int head, int b,
+                                                   int lane) {
+  uint64_t w[4];
+  philox4x64(c0, c1, (uint64_t)head, (uint64_t)b, d.seed, d.site, w);
+  uint32_t m = 0;  // bit 4r + c: draw c of word r (row r = q % 4, column c = k % 4)
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) m |= (uint32_t)(((w[r] >> (16 * c)) & 0xFFFFu) >= d.thr) << (4 * r + c);
+  if (KEY_LANES) {  // bit 4r + c -> bit 4c + r
+    uint32_t t = (m ^ (m >> 3)) & 0x0A0Au;
+    m ^= t ^ (t << 3);
+    t = (m ^ (m >> 6)) & 0x00CCu;
+    m ^= t ^ (t << 6);
+  }
+  // nibble j of lane t' <- nibble t' of lane j (within the quad)
+  const int t = lane & 3;
+  uint32_t p = dpp_u<0xB1>(m);  // lane t ^ 1
+  m = (t & 1) ? ((m & 0xF0F0u) | ((p & 0xF0F0u) >> 4)) : ((m & 0x0F0Fu) | ((p & 0x0F0Fu) << 4));
+  p = dpp_u<0x4E>(m);  // lane t ^ 2
+  m = (t & 2) ? ((m & 0xFF00u) | ((p & 0xFF00u) >> 8)) : ((m & 0x00FFu) | ((p & 0x00FFu) << 8));
+  return m;
+}
+
 // dK and dV given the (L, D) pairs the dQ kernel stores (attention_bf16_dkdv.hip).
 hipError_t dkdv_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, const void* dout,
-                     const float2* ldw, void* dqkv, hipStream_t st);
+                     const float2* ldw, void* dqkv, const AttnDropout& drop, hipStream_t st);
 
 }  // namespace attn
 }  // namespace mtnlg

@@ -17,13 +17,13 @@ using namespace attn;
 // stage also holds the (L, D) pairs of the tile's 64 queries: wave w loads
 // queries 16w .. 16w+15 into its own 1 KiB slot (lanes 8..63 load nothing
 // but still write zeros, hence the slot).
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __restrict__ qkv,
                                                              const bf16_t* __restrict__ dout,
                                                              const float2* __restrict__ ldw,
                                                              bf16_t* __restrict__ dqkv, int seq, int nh,
                                                              int64_t tokens, int nbh, float scale,
-                                                             float scale_log2) {
+                                                             float scale_log2, AttnDropout drop) {
   using TL = Tile<D>;
   constexpr int EB = TL::EB, SUB = TL::SUB;
   constexpr int LD_OFF = 2 * TL::BYTES, STAGE = 2 * TL::BYTES + 4096;
@@ -93,6 +93,12 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
       s = mma_f16(frag_row(sq, 32 * qh + lq, st, g), kf[st], s);
       dp = mma(frag_row(so, 32 * qh + lq, st, g), vf[st], dp);
     }
+    // dropout on the probabilities: dV takes P * keep * scale, and the
+    // gradient reaching P is dO V^T * keep * scale (all ones without dropout)
+    uint32_t keep = 0xFFFFu;
+    if (DROP)
+      keep = attn_keep_bits<true>(drop, (uint64_t)((qw0 >> 2) + 2 * (lq & 3) + g), (uint64_t)((kw0 >> 2) + (lq >> 2)),
+                                  drop.head0 + n, b, lane);
 #pragma unroll
     for (int i2 = 0; i2 < 8; ++i2) {  // queries 32*qh + 8*(i>>2) + 4*g + (i&3), two at a time
       const int ql = 32 * qh + 8 * (i2 >> 1) + 4 * g + 2 * (i2 & 1);
@@ -101,8 +107,14 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
       for (int j = 0; j < 2; ++j) {
         const int i = 2 * i2 + j;
         const float p = fast_exp2(fmaf(s[i], scale_log2, -(j ? pr.z : pr.x)));
-        s[i] = p;
-        dp[i] = p * (dp[i] - (j ? pr.w : pr.y));
+        if (DROP) {
+          const bool kept = (keep >> i) & 1u;
+          s[i] = kept ? p * drop.scale : 0.0f;
+          dp[i] = p * ((kept ? dp[i] * drop.scale : 0.0f) - (j ? pr.w : pr.y));
+        } else {
+          s[i] = p;
+          dp[i] = p * (dp[i] - (j ? pr.w : pr.y));
+        }
       }
     }
     if (kw0 == qw0) {
@@ -159,12 +171,14 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
 
 template <int D>
 hipError_t dkdv_launch(int batch, int seq, int heads, const void* qkv, const void* dout, const float2* ldw,
-                       void* dqkv, hipStream_t st) {
+                       void* dqkv, const AttnDropout& drop, hipStream_t st) {
   const int nbh = batch * heads;
   const float scale = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D>), dim3((unsigned)((seq / kRows) * nbh)), dim3(256), 0, st,
+  hipLaunchKernelGGL((drop.thr ? attn_dkdv_bf16_kernel<D, true> : attn_dkdv_bf16_kernel<D, false>),
+                     dim3((unsigned)((seq / kRows) * nbh)), dim3(256), 0, st,
                      static_cast<const bf16_t*>(qkv), static_cast<const bf16_t*>(dout), ldw,
-                     static_cast<bf16_t*>(dqkv), seq, heads, (int64_t)batch * seq, nbh, scale, kLog2e * scale);
+                     static_cast<bf16_t*>(dqkv), seq, heads, (int64_t)batch * seq, nbh, scale, kLog2e * scale,
+                     drop);
   return hipGetLastError();
 }
 
@@ -173,11 +187,11 @@ hipError_t dkdv_launch(int batch, int seq, int heads, const void* qkv, const voi
 namespace attn {
 
 hipError_t dkdv_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, const void* dout,
-                     const float2* ldw, void* dqkv, hipStream_t st) {
+                     const float2* ldw, void* dqkv, const AttnDropout& drop, hipStream_t st) {
   switch (head_dim) {
-    case 64: return dkdv_launch<64>(batch, seq, heads, qkv, dout, ldw, dqkv, st);
-    case 128: return dkdv_launch<128>(batch, seq, heads, qkv, dout, ldw, dqkv, st);
-    case 160: return dkdv_launch<160>(batch, seq, heads, qkv, dout, ldw, dqkv, st);
+    case 64: return dkdv_launch<64>(batch, seq, heads, qkv, dout, ldw, dqkv, drop, st);
+    case 128: return dkdv_launch<128>(batch, seq, heads, qkv, dout, ldw, dqkv, drop, st);
+    case 160: return dkdv_launch<160>(batch, seq, heads, qkv, dout, ldw, dqkv, drop, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -120,6 +120,35 @@ __device__ __forceinline__ F block_sum(F v, F* red) {
   return s;
 }
 
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC 2011) of the counter (c0, c1, c2, c3) under the key
+// (k0, k1): ten rounds, each multiplying two of the four 64-bit words by a
+// round constant into 128-bit products and mixing the halves with the other
+// words and the key; the key advances by two Weyl increments between rounds.
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64(uint64_t x0, uint64_t x1, uint64_t x2, uint64_t x3, uint64_t k0,
+                                           uint64_t k1, uint64_t w[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, x0), lo0 = kPhiloxM0 * x0;
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, x2), lo1 = kPhiloxM1 * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  w[0] = x0;
+  w[1] = x1;
+  w[2] = x2;
+  w[3] = x3;
+}
+
 // ---- direct-to-LDS loads and transposing LDS reads (gfx950) ----
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));

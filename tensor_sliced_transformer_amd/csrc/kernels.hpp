@@ -75,16 +75,25 @@ hipError_t layernorm_bwd(int dtype, int gy_dtype, int64_t rows, int64_t cols, co
                          void* dx, void* dgamma, void* dbeta, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
+// Dropout on the attention probabilities (bf16 kernels; see attention_bf16.hpp
+// for the mask): thr == 0 is no dropout.
+struct AttnDropout {
+  uint64_t seed, site;
+  uint32_t thr;  // drop when the 16-bit draw is below thr
+  float scale;   // 65536 / (65536 - thr)
+  int head0;     // global index of the launch's head 0
+};
 hipError_t attention_fwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv,
-                         void* o, float* lse, hipStream_t st);
+                         void* o, float* lse, const AttnDropout& drop, hipStream_t st);
 size_t attention_bwd_ws(int batch, int seq, int heads);
 hipError_t attention_fwd_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, void* o, float* lse,
-                              hipStream_t st);
+                              const AttnDropout& drop, hipStream_t st);
 hipError_t attention_bwd_bf16(int batch, int seq, int heads, int head_dim, const void* qkv, const void* o,
-                              const float* lse, const void* dout, void* dqkv, void* ws, hipStream_t st);
+                              const float* lse, const void* dout, void* dqkv, void* ws, const AttnDropout& drop,
+                              hipStream_t st);
 hipError_t attention_bwd(int dtype, int batch, int seq, int heads, int head_dim, const void* qkv,
                          const void* o, const float* lse, const void* dout, void* dqkv, void* ws,
-                         hipStream_t st);
+                         const AttnDropout& drop, hipStream_t st);
 
 // ---------------------------------------------------------------- streaming
 constexpr int kMaxPartials = 16;

@@ -220,6 +220,12 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
   auto site = [&](int k, int l, int half) -> uint64_t {
     return ((uint64_t)k * (uint64_t)desc->layers + (uint64_t)l) * 2u + (uint64_t)half;
   };
+  // layer l of micro-batch k: its own attention-probability mask
+  auto layer_of = [&](int k, int l) -> mtnlg_layer_desc {
+    mtnlg_layer_desc Lk = *L;
+    Lk.attn_dropout_site += (uint64_t)k * (uint64_t)desc->layers + (uint64_t)l;
+    return Lk;
+  };
   auto saved = [&](int l, int half) -> void* {
     if (desc->recompute) return base + W.saved;
     return base + W.saved + (size_t)l * (W.saved_a + W.saved_m) + (half == MTNLG_MLP ? W.saved_a : 0);
@@ -231,10 +237,11 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
       layer_offsets(d, l, o);
       const void* in[2] = {xin(l, k), mid(l)};
       void* out[2] = {mid(l), xout(l, k)};
+      const mtnlg_layer_desc Lk = layer_of(k, l);
       for (int half = 0; half < 2; ++half) {
         const int64_t* t = o[half];
         const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
-        STAGE_CALL(mtnlg_layer_fwd(L, half, &p, in[half], part, saved(l, half), lws, lws_bytes, stream));
+        STAGE_CALL(mtnlg_layer_fwd(&Lk, half, &p, in[half], part, saved(l, half), lws, lws_bytes, stream));
         const void* parts[1] = {part};
         if (drop) {
           const mtnlg_dropout dr = {desc->dropout_seed, site(k, l, half), desc->dropout_p};
@@ -254,6 +261,7 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
       // accumulation of it must be done
       if (overlap && k > 0) MTNLG_HIP(hipStreamWaitEvent(S, acc_done[l], 0), "hipStreamWaitEvent");
       const void* in[2] = {xin(l, k), mid(l)};
+      const mtnlg_layer_desc Lk = layer_of(k, l);
       for (int half = 1; half >= 0; --half) {
         const int64_t* t = o[half];
         const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
@@ -267,9 +275,9 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
           dyh = base + W.dz;
         }
         if (desc->recompute)
-          STAGE_CALL(mtnlg_layer_bwd_recompute(L, half, &p, in[half], dyh, part, &g, lws, lws_bytes, stream));
+          STAGE_CALL(mtnlg_layer_bwd_recompute(&Lk, half, &p, in[half], dyh, part, &g, lws, lws_bytes, stream));
         else
-          STAGE_CALL(mtnlg_layer_bwd(L, half, &p, in[half], saved(l, half), dyh, part, &g, lws, lws_bytes,
+          STAGE_CALL(mtnlg_layer_bwd(&Lk, half, &p, in[half], saved(l, half), dyh, part, &g, lws, lws_bytes,
                                      stream));
         // dx of the half = dy (residual path) + the slice's partial
         void* dst = half == MTNLG_MLP ? g1 : (l == 0 ? static_cast<char*>(dx) + (size_t)k * act : g2);

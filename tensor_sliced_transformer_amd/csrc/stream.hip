@@ -93,36 +93,12 @@ __global__ __launch_bounds__(kStreamThreads) void reduce_partials_kernel(Partial
 
 // ---- dropout on the sum of the partials (counter-based mask) ----
 //
-// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
-// Easy as 1, 2, 3", SC 2011): ten rounds, each multiplying two of the four
-// 64-bit words by a round constant into 128-bit products and mixing the
-// halves with the other words and the key; the key advances by two Weyl
-// increments between rounds. One call yields 256 bits, sixteen 16-bit draws:
-// element e of a row-major tensor uses block e / 16 (counter (e/16, 0, 0, 0),
+// One Philox4x64-10 block (philox4x64 in common.hpp) yields 256 bits, sixteen
+// 16-bit draws: element e of a row-major tensor uses block e / 16 (counter (e/16, 0, 0, 0),
 // key (seed, site)) and the draw at bits 16 * (e % 4) of word (e % 16) / 4.
 // It is kept when draw >= thr; kept values are multiplied by scale.
-constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
-constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
-constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
-constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
-
-__device__ __forceinline__ void philox4x64(uint64_t c0, uint64_t k0, uint64_t k1, uint64_t w[4]) {
-  uint64_t x0 = c0, x1 = 0, x2 = 0, x3 = 0;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(kPhiloxM0, x0), lo0 = kPhiloxM0 * x0;
-    const uint64_t hi1 = __umul64hi(kPhiloxM1, x2), lo1 = kPhiloxM1 * x2;
-    x0 = hi1 ^ x1 ^ k0;
-    x1 = lo1;
-    x2 = hi0 ^ x3 ^ k1;
-    x3 = lo0;
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
-  }
-  w[0] = x0;
-  w[1] = x1;
-  w[2] = x2;
-  w[3] = x3;
+__device__ __forceinline__ void philox_block(uint64_t c0, uint64_t k0, uint64_t k1, uint64_t w[4]) {
+  philox4x64(c0, 0, 0, 0, k0, k1, w);
 }
 
 struct DropoutArgs {
@@ -134,7 +110,7 @@ struct DropoutArgs {
 // keep bit j (0..15) of a 16-element group as a 16-bit mask
 __device__ __forceinline__ uint32_t keep_bits(uint64_t group, const DropoutArgs& d) {
   uint64_t w[4];
-  philox4x64(group, d.seed, d.site, w);
+  philox_block(group, d.seed, d.site, w);
   uint32_t bits = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) bits |= (uint32_t)(((w[j >> 2] >> (16 * (j & 3))) & 0xFFFFu) >= d.thr) << j;

@@ -8,9 +8,15 @@
   in full (the oracle runs the same slice in float64);
 * run-to-run determinism of a backward;
 * the backward that recomputes the forward is bit-identical to the stored one;
-* the tiny layer with dropout on both halves (Philox masks) against the oracle.
+* the tiny layer with dropout on both halves (Philox masks) against the oracle;
+* dropout on the attention probabilities (head_dim 64, 128 and 160, slices
+  of rank > 0 so the global head index enters the mask, and the MT-NLG shard
+  at full size): forward and backward against the oracle drawing the same
+  mask, and the recomputing backward bit-identical to the stored one.
 Tolerance: ||gpu - oracle||_inf / ||oracle||_inf per tensor (1e-4 fp32, 2e-2 bf16).
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
@@ -44,9 +50,9 @@ def shape_of(w):
 class GpuHalf:
     """Device buffers and calls of one slice of one half."""
 
-    def __init__(self, w, half, params_np, rank=0):
+    def __init__(self, w, half, params_np, rank=0, desc=None):
         self.w, self.half, self.dt = w, half, w.dtype
-        self.desc = desc_of(w, rank)
+        self.desc = desc_of(w, rank) if desc is None else desc
         self.p = {k: to_gpu(v, self.dt) for k, v in params_np.items() if k != "b_out"}
         self.saved = empty_bytes(tst.saved_bytes(self.desc, HALF[half]))
         self.ws = empty_bytes(tst.workspace_bytes(self.desc, HALF[half]))
@@ -67,13 +73,18 @@ def oracle_params(p):
     return {k: v.astype(np.float64) for k, v in p.items()}
 
 
-def check_half(w, half, tag_x, tag_g):
-    """Forward and backward of slice 0 of one half vs the oracle, every output in full."""
-    print(f"{w.name} {half}", flush=True)
-    pn = make_half_params(w, half, 0)
+def check_half(w, half, tag_x, tag_g, rank=0, attn_drop=None):
+    """Forward and backward of slice `rank` of one half vs the oracle, every
+    output in full. attn_drop: None, or (rate, seed, site) for dropout on the
+    attention probabilities. Returns the GpuHalf and the inputs on the GPU."""
+    print(f"{w.name} {half} slice {rank} attention dropout {attn_drop}", flush=True)
+    pn = make_half_params(w, half, rank)
     x = make_activation(w, tag_x)
     g = make_activation(w, tag_g)
-    gh = GpuHalf(w, half, pn)
+    desc = None
+    if attn_drop is not None:
+        desc = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, rank, tst.BF16, 1e-5, *attn_drop)
+    gh = GpuHalf(w, half, pn, rank, desc)
     xg, gg = to_gpu(x, w.dtype), to_gpu(g, w.dtype)
     y = gh.fwd(xg)
     dx = gh.bwd(xg, gg)
@@ -86,6 +97,8 @@ def check_half(w, half, tag_x, tag_g):
         kw = {"store": store}
         if half == "attn" and store is not None:
             kw["store_qk"] = round_to_f16
+        if half == "attn" and attn_drop is not None:
+            kw["attn_drop"] = (*attn_drop, rank * sh.local_heads)
         part, saved = fwd(sh, x.astype(np.float64), po, **kw)
         rdx, rg, _ = bwd(sh, g.astype(np.float64), po, saved)
         return part, rdx, rg
@@ -107,6 +120,7 @@ def check_half(w, half, tag_x, tag_g):
         print("vs oracle with bf16 saved tensors:", {k: f"{v:.2e}" for k, v in diag.items()}, flush=True)
         for k, e in diag.items():
             assert e <= TOL["bf16"], f"{k}: {e:.3e} against the diagnostic oracle"
+    return gh, xg, gg
 
 
 @pytest.mark.parametrize("half", ["attn", "mlp"])
@@ -301,3 +315,44 @@ def test_tiny_layer_two_slices_with_dropout():
         for k in ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out"):
             assert_close(f"attn{i}.{k}", to_np(A[i].g[k]), ga[i][k], dt)
             assert_close(f"mlp{i}.{k}", to_np(M[i].g[k]), gm[i][k], dt)
+
+
+# Shapes for dropout on the attention probabilities: head_dim 64, 128 and 160;
+# slices of rank > 0 (the mask takes the global head index); seq 384 is three
+# 128-query tiles.
+ATTN_DROP = [
+    replace(WORKLOADS[6], index=61, name="attn-drop-d64-t2", batch=2, seq=256, hidden=256, heads=4, ffn=1024,
+            tp=2, slices=(1,), extra={}),
+    replace(WORKLOADS[6], index=62, name="attn-drop-d128", batch=2, seq=256, hidden=512, heads=4, ffn=1024,
+            tp=1, slices=(0,), extra={}),
+    replace(WORKLOADS[6], index=63, name="attn-drop-d160-t2", batch=2, seq=384, hidden=640, heads=4, ffn=1280,
+            tp=2, slices=(1,), extra={}),
+]
+
+
+@pytest.mark.parametrize("wi", range(len(ATTN_DROP)))
+def test_attention_probability_dropout(wi):
+    """Forward and backward of the attention half with dropout (rate 0.1) on
+    its probabilities against the oracle with the same mask; the recomputing
+    backward regenerates the mask and is bit-identical to the stored one."""
+    w = ATTN_DROP[wi]
+    rank = w.slices[0]
+    drop = (float(np.float32(0.1)), 0x5EED00 + wi, 3 + wi)
+    gh, xg, gg = check_half(w, "attn", 1, 2, rank, drop)
+    dx_ref = gh.bwd(xg, gg).clone()
+    g_ref = {k: v.clone() for k, v in gh.g.items()}
+    ws = empty_bytes(tst.recompute_workspace_bytes(gh.desc, tst.ATTN))
+    dx = empty((w.tokens, w.hidden), w.dtype)
+    for k in gh.g:
+        gh.g[k].fill_(float("nan"))
+    tst.layer_bwd_recompute(gh.desc, tst.ATTN, gh.p, xg, gg, dx, gh.g, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_ref)
+    for k in g_ref:
+        assert torch.equal(gh.g[k], g_ref[k]), k
+
+
+def test_mtnlg_shard_attention_dropout():
+    """The MT-NLG attention slice of rank 3 (global heads 48..63) at full size
+    with dropout 0.1 on its probabilities, every output against the oracle."""
+    check_half(WORKLOADS[3], "attn", 1, 2, 3, (float(np.float32(0.1)), 20220128, 5))

@@ -11,8 +11,10 @@ Checked:
   master rounded to nearest even, bit for bit;
 * the recompute schedule, and the accumulation overlapped on a second
   stream, give bit-identical results to the plain schedule;
-* all of it without dropout and with dropout (p = 0.15) on every half's
-  output, the masks drawn by the GPU and, independently, by the oracle.
+* all of it without dropout, with dropout (p = 0.15) on every half's
+  output, and with dropout on the attention probabilities as well (rate 0.1,
+  each layer and micro-batch with its own site), the masks drawn by the GPU
+  and, independently, by the oracle.
 Tolerance metric: ||gpu - oracle||_inf / ||oracle||_inf per tensor.
 """
 import numpy as np
@@ -86,12 +88,16 @@ def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0, aux=False)
     return out, flat, m0, v0, offs
 
 
-@pytest.mark.parametrize("p", [0.0, 0.15])
-def test_stage_step_against_oracle_and_recompute(p):
+@pytest.mark.parametrize("p,pa", [(0.0, 0.0), (0.15, 0.0), (0.15, 0.1)])
+def test_stage_step_against_oracle_and_recompute(p, pa):
     w, L, MB, ld, halves, full, xs, gs = _setup()
     p = float(np.float32(p))           # the rate as the library receives it
+    pa = float(np.float32(pa))
     seed = 0xC0FFEE
-    print(f"stage {w.name}: {L} layers, {MB} micro-batches, dropout {p}", flush=True)
+    attn = (pa, 0xA77E, 7) if pa > 0.0 else None
+    if attn is not None:
+        ld = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, 1, 0, tst.BF16, 1e-5, *attn)
+    print(f"stage {w.name}: {L} layers, {MB} micro-batches, dropout {p}, attention dropout {pa}", flush=True)
     cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, max_grad_norm=0.5, inv_loss_scale=1.0,
                         step=w.extra["step"])
     got, flat, m0, v0, offs = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed)
@@ -106,7 +112,7 @@ def test_stage_step_against_oracle_and_recompute(p):
     sh = OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=1)
     ys, dxs, flats = OS.stage_micro_batches(sh, [{k: v.astype(np.float64) for k, v in q.items()} for q in full],
                                             [x.astype(np.float64) for x in xs], [g.astype(np.float64) for g in gs],
-                                            dropout=(p, seed))
+                                            dropout=(p, seed), attn_dropout=attn)
     errs = {}
     for k in range(MB):
         errs[f"y{k}"] = rel_inf(got["y"][k], ys[k])

@@ -136,3 +136,53 @@ def test_stage_with_dropout_finite_differences():
     np.testing.assert_allclose(y1, ys0[0], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dx1, dxs0[0], rtol=0, atol=1e-12)
     np.testing.assert_allclose(OS.flatten(g1), fl0[0], rtol=0, atol=1e-12)
+
+
+def test_stage_with_attention_dropout_finite_differences():
+    """Dropout on the attention probabilities of every layer (each layer and
+    micro-batch keyed by its own site) together with dropout on every half's
+    output: the summed loss's gradient matches central differences; each
+    layer's attention mask differs from the others'; at rate 0 the stage is
+    the plain one."""
+    from oracle import dropout as OD
+    sh = OL.LayerShape(batch=1, seq=8, hidden=12, heads=3, ffn=24, tp=1)
+    layers = []
+    for i in range(2):
+        r = rng(180 + i)
+        layers.append({k: (1.0 + 0.2 * r.standard_normal(s)) if k in ("ln1_g", "ln2_g") else 0.3 * r.standard_normal(s)
+                       for k, s in OL.full_param_shapes(sh).items()})
+    xs = [rng(190 + k).standard_normal((sh.tokens, sh.hidden)) for k in range(2)]
+    gs = [rng(200 + k).standard_normal((sh.tokens, sh.hidden)) for k in range(2)]
+    p, seed, ad = 0.2, 31, (0.25, 901, 40)
+    _, dxs, flats = OS.stage_micro_batches(sh, layers, xs, gs, dropout=(p, seed), attn_dropout=ad)
+    acc = OA.accumulate(flats)
+    r = rng(210)
+    up = [{k: r.standard_normal(v.shape) for k, v in q.items()} for q in layers]
+    ux = [r.standard_normal(x.shape) for x in xs]
+    delta = 1e-5
+
+    def loss_at(s):
+        tot = 0.0
+        for k, (x, g) in enumerate(zip(xs, gs)):
+            lay = [{key: q[key] + s * u[key] for key in q} for q, u in zip(layers, up)]
+            h = x + s * ux[k]
+            for l, full in enumerate(lay):
+                h, _ = OD.layer_fwd(sh, h, full, p, seed, ((k * 2 + l) * 2, (k * 2 + l) * 2 + 1),
+                                    (ad[0], ad[1], ad[2] + k * 2 + l))
+            tot += float((h * g).sum())
+        return tot
+
+    fd = (loss_at(delta) - loss_at(-delta)) / (2 * delta)
+    an = float(acc @ OS.flatten(up)) + sum(float((dx * u).sum()) for dx, u in zip(dxs, ux))
+    assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0), (fd, an)
+    # four layer calls, four distinct attention masks
+    masks = [OD.attention_keep(1, range(3), sh.seq, ad[0], ad[1], site)
+             for (_, _, site) in OS.attn_drops(2, 0, ad) + OS.attn_drops(2, 1, ad)]
+    for i in range(4):
+        for j in range(i):
+            assert (masks[i] != masks[j]).any()
+    # rate 0: the plain stage
+    ys0, dxs0, fl0 = OS.stage_micro_batches(sh, layers, xs, gs)
+    ys1, dxs1, fl1 = OS.stage_micro_batches(sh, layers, xs, gs, attn_dropout=(0.0, 901, 40))
+    for a, b in zip(ys0 + dxs0 + fl0, ys1 + dxs1 + fl1):
+        np.testing.assert_array_equal(a, b)
