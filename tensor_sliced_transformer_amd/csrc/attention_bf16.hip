@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
     mx = fmaxf(mx, s[15]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * scale_log2;  // finite: key kw0 is visible here
+    mx = xor32_max(mx) * scale_log2;  // finite: key kw0 is visible here
     if (__builtin_amdgcn_ballot_w64(mx > m + kSlack)) {
       const float mn = fmaxf(m, mx);
       const float corr = fast_exp2(m - mn);
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
   });
 
   // merge the two key halves: (m, l, O) of wave kh=1 into wave kh=0
-  l += __shfl_xor(l, 32, kWave);
+  l = xor32_sum(l);
   __syncthreads();  // every load has been waited for and every wave is done with the ring
   static_assert(2 * (EB * 16 + 2) * 64 * 4 <= kFwdRing * STAGE, "merge staging exceeds the ring");
   float* xs = reinterpret_cast<float*>(smem) + qg * (EB * 16 + 2) * 64;
@@ -231,8 +231,10 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
 #pragma unroll
     for (int j = 0; j < 8; ++j) dsum += a[j] * (float)df[s][j];
   }
-  dsum += __shfl_xor(dsum, 32, kWave);
-  const float lrow = lse[(int64_t)n * tokens + tq] * kLog2e;
+  dsum = xor32_sum(dsum);
+  // log2 of the softmax normaliser, plus the dS down-shift (kDsShift): P and
+  // dS below are 2^-kDsShift times their values
+  const float lrow = fmaf(lse[(int64_t)n * tokens + tq], kLog2e, kDsShift);
 #pragma unroll
   for (int s = 0; s < SUB; ++s) {
     settle(qf[s]);
@@ -289,9 +291,9 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bf16x8_t db = pack_slots(dp, t);
+      const bf16x8_t db = pack_slots_f16(dp, t);
 #pragma unroll
-      for (int e = 0; e < EB; ++e) dq[e] = mma(f16_to_bf16(frag_tr(sk, e, 32 * kh, t, lane)), db, dq[e]);
+      for (int e = 0; e < EB; ++e) dq[e] = mma_f16(frag_tr(sk, e, 32 * kh, t, lane), db, dq[e]);
     }
   });
 
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          v[r] = (dq[e][4 * blk + r] + xs[(e * 16 + 4 * blk + r) * 64 + lane]) * scale;
+          v[r] = (dq[e][4 * blk + r] + xs[(e * 16 + 4 * blk + r) * 64 + lane]) * (scale * kDsUp);
         store4(row + e * 32 + 8 * blk + 4 * g, v[0], v[1], v[2], v[3]);
       }
   }

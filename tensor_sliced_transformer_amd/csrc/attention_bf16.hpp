@@ -86,15 +86,19 @@ __device__ __forceinline__ f32x16_t mma_f16(const bf16x8_t& a, const bf16x8_t& b
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
                                                 0, 0, 0);
 }
-// An fp16 fragment (of Q or K) as bf16, round to nearest even, for the products
-// that pair it with bf16 data (dQ = dS K, dK = dS^T Q).
-__device__ __forceinline__ bf16x8_t f16_to_bf16(const bf16x8_t& x) {
-  const f16x8_t h = __builtin_bit_cast(f16x8_t, x);
+// dQ = dS K and dK = dS^T Q pair dS with the fp16 Q and K fragments on the
+// fp16 MFMA, dS packed as fp16 (pack_slots_f16). The backward kernels compute
+// P, and so dS, scaled by 2^-kDsShift (the shift is folded into the
+// exponent's offset): fp16 then holds |dS| up to 65504 * 2^kDsShift, and the
+// accumulated dQ, dK and dV are multiplied by 2^kDsShift at the end (exact).
+constexpr float kDsShift = 8.0f;
+constexpr float kDsUp = 256.0f;
+__device__ __forceinline__ bf16x8_t pack_slots_f16(const f32x16_t& a, int t) {
   uint4 u;
-  u.x = pack_bf16x2((float)h[0], (float)h[1]);
-  u.y = pack_bf16x2((float)h[2], (float)h[3]);
-  u.z = pack_bf16x2((float)h[4], (float)h[5]);
-  u.w = pack_bf16x2((float)h[6], (float)h[7]);
+  u.x = pack_f16x2(a[8 * t + 0], a[8 * t + 1]);
+  u.y = pack_f16x2(a[8 * t + 2], a[8 * t + 3]);
+  u.z = pack_f16x2(a[8 * t + 4], a[8 * t + 5]);
+  u.w = pack_f16x2(a[8 * t + 6], a[8 * t + 7]);
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
@@ -125,6 +129,18 @@ __device__ __forceinline__ void settle(const bf16x8_t& x) { asm volatile("" : : 
 // 2^x by the hardware instruction (results below 2^-126 flush to zero, which
 // is immaterial next to the softmax row sum of at least 1).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max and sum of x over lanes l and l ^ 32 (the two halves of a 32x32
+// accumulator column), with v_permlane32_swap: the swap puts the other half's
+// values beside this half's, in registers (no LDS round trip).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // The walk over `count` streamed tiles through the LDS ring. issue(t, stage)
 // starts the loads of tile t into a ring stage; body(it, stage) computes on

@@ -128,11 +128,11 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bf16x8_t pb = pack_slots(s, t);
-      const bf16x8_t db = pack_slots(dp, t);
+      const bf16x8_t db = pack_slots_f16(dp, t);
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
         dv[e] = mma(frag_tr(so, e, 32 * qh, t, lane), pb, dv[e]);
-        dk[e] = mma(f16_to_bf16(frag_tr(sq, e, 32 * qh, t, lane)), db, dk[e]);
+        dk[e] = mma_f16(frag_tr(sq, e, 32 * qh, t, lane), db, dk[e]);
       }
     }
   });
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * blk + r;
-          a[r] = (dk[e][i] + xs[(e * 16 + i) * 64 + lane]) * scale;
-          c[r] = dv[e][i] + xs[((EB + e) * 16 + i) * 64 + lane];
+          a[r] = (dk[e][i] + xs[(e * 16 + i) * 64 + lane]) * (scale * kDsUp);
+          c[r] = (dv[e][i] + xs[((EB + e) * 16 + i) * 64 + lane]) * kDsUp;
         }
         store4(krow + e * 32 + 8 * blk + 4 * g, a[0], a[1], a[2], a[3]);
         store4(vrow + e * 32 + 8 * blk + 4 * g, c[0], c[1], c[2], c[3]);
