@@ -58,6 +58,10 @@ constexpr float kSlack = 8.0f;
 // a three-stage ring at head_dim 160.
 constexpr int kFwdRing = 2;
 
+// The dQ kernel's ring: its pipelined walk reads tiles it+1 and it+2 during
+// iteration it, and loads keep two iterations of lead.
+constexpr int kDqRing = 4;
+
 template <int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ qkv,
                                                                bf16_t* __restrict__ o, float* __restrict__ lse,
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
 // Same walk as the forward. Also computes, per query, D = rowsum(dO * O) and
 // L = lse * log2(e), and stores the pair for the dK/dV kernel.
 template <int D, bool DROP>
-__global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_dq_bf16_kernel(const bf16_t* __restrict__ qkv,
                                                            const bf16_t* __restrict__ o,
                                                            const bf16_t* __restrict__ dout,
                                                            const float* __restrict__ lse, float2* __restrict__ ldw,
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
                                                            AttnDropout drop) {
   using TL = Tile<D>;
   constexpr int EB = TL::EB, SUB = TL::SUB, STAGE = 2 * TL::BYTES;
-  __shared__ __align__(1024) char smem[kRing * STAGE];
+  __shared__ __align__(1024) char smem[kDqRing * STAGE];
 
   const int nqb = seq / kRows;
   const int qb = nqb - 1 - (int)blockIdx.x / nbh;
@@ -256,46 +260,115 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(const bf16_t* __restr
 #pragma unroll
   for (int e = 0; e < EB; ++e) zero(dq[e]);
 
-  ring_walk<2 * TL::IPW>(qb + 1, issue, [&](int it, int stage) {
-    const char* sk = smem + stage * STAGE;
+  // Software-pipelined walk over the key tiles: iteration it computes S and
+  // dP of tile it+1 on the matrix cores while the vector units turn tile
+  // it's S and dP into dS, then accumulates dQ += dS K of tile it. Tiles
+  // it+1 and it+2 are resident during iteration it; the ring's kDqRing
+  // stages give every tile two iterations from the issue of its loads to
+  // its first use.
+  constexpr int NLD = 2 * TL::IPW;  // loads per wave per tile
+  const int T = qb + 1;             // key tiles of this query block
+  auto active = [&](int it) { return it * kRows + 32 * kh <= qw0; };  // some key of the half is visible
+  f32x16_t sb[2], dpb[2];
+  auto chains = [&](int it, int buf) {  // S and dP of tile it, alone (the first tile)
+    const char* sk = smem + (it % kDqRing) * STAGE;
     const char* sv = sk + TL::BYTES;
-    const int kw0 = it * kRows + 32 * kh;
-    if (kw0 > qw0) return;
-    f32x16_t s, dp;
-    zero(s);
-    zero(dp);
+    zero(sb[buf]);
+    zero(dpb[buf]);
 #pragma unroll
     for (int st = 0; st < SUB; ++st) {
-      s = mma_f16(frag_row(sk, 32 * kh + lq, st, g), qf[st], s);
-      dp = mma(frag_row(sv, 32 * kh + lq, st, g), df[st], dp);
+      sb[buf] = mma_f16(frag_row(sk, 32 * kh + lq, st, g), qf[st], sb[buf]);
+      dpb[buf] = mma(frag_row(sv, 32 * kh + lq, st, g), df[st], dpb[buf]);
     }
-    if (DROP) {  // the gradient reaching P is dO V^T * keep * scale
-      const uint32_t keep = attn_keep_bits<false>(drop, (uint64_t)((qw0 >> 2) + (lq >> 2)),
-                                                  (uint64_t)((kw0 >> 2) + 2 * (lq & 3) + g), drop.head0 + n, b, lane);
+  };
+  // dS of slot i from S and dP (2^-kDsShift scale)
+  auto ds_slot = [&](f32x16_t& s, f32x16_t& dp, uint32_t keep, int i) {
+    const float p = fast_exp2(fmaf(s[i], scale_log2, -lrow));
+    if (DROP)  // the gradient reaching P is dO V^T * keep * scale
+      dp[i] = p * ((((keep >> i) & 1u) ? dp[i] * drop.scale : 0.0f) - dsum);
+    else
+      dp[i] = p * (dp[i] - dsum);
+  };
+
+  // Fragment registers of two consecutive iterations: tile it+1's K and V
+  // rows (S and dP) and tile it's transposed K (dQ), for iteration it.
+  bf16x8_t kfr[2][SUB], vfr[2][SUB], ktr[2][2][EB];
+  auto read_frags = [&](int it, int fb) {  // fragments of iteration it into set fb
+    const char* sk = smem + (it % kDqRing) * STAGE;         // tile it
+    const char* skn = smem + ((it + 1) % kDqRing) * STAGE;  // tile it+1 (past the last: stale, unused)
+    const char* svn = skn + TL::BYTES;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[i], scale_log2, -lrow));
-        dp[i] = p * ((((keep >> i) & 1u) ? dp[i] * drop.scale : 0.0f) - dsum);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[i], scale_log2, -lrow));
-        dp[i] = p * (dp[i] - dsum);
-      }
+    for (int st = 0; st < SUB; ++st) {
+      kfr[fb][st] = frag_row(skn, 32 * kh + lq, st, g);
+      vfr[fb][st] = frag_row(svn, 32 * kh + lq, st, g);
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < EB; ++e) ktr[fb][t][e] = frag_tr(sk, e, 32 * kh, t, lane);
+  };
+
+  // One iteration; BUF = it & 1 is a template constant so that register sets
+  // are never indexed at run time. The S and dP chains of tile it+1 run with
+  // tile it's dS computed between their matrix instructions (source order,
+  // kept by scheduling barriers); then a barrier publishes tile it+2, the
+  // next iteration's fragments are read, and dQ += dS K of tile it covers
+  // their latency.
+  auto step = [&](int it, auto BUF_) {
+    constexpr int buf = decltype(BUF_)::value;
+    const int kw0 = it * kRows + 32 * kh;
+    uint32_t keep = 0;
+    if (DROP)
+      keep = attn_keep_bits<false>(drop, (uint64_t)((qw0 >> 2) + (lq >> 2)), (uint64_t)((kw0 >> 2) + 2 * (lq & 3) + g),
+                                   drop.head0 + n, b, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t& sn = sb[buf ^ 1];
+    f32x16_t& dpn = dpb[buf ^ 1];
+    zero(sn);
+    zero(dpn);
+#pragma unroll
+    for (int st = 0; st < SUB; ++st) {
+      sn = mma_f16(kfr[buf][st], qf[st], sn);
+      dpn = mma(vfr[buf][st], df[st], dpn);
+#pragma unroll
+      for (int i = 16 * st / SUB; i < 16 * (st + 1) / SUB; ++i) ds_slot(sb[buf], dpb[buf], keep, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Tile it+2 landed (tile it+3 may still be in flight), and every wave's
+    // reads of tile it are done (its transposed K was read at the previous
+    // barrier): tile it's stage takes tile it+kDqRing.
+    wait_tiles<NLD>(min(T - 3 - it, kDqRing - 3));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __syncthreads();
+    if (it + kDqRing < T) issue(it + kDqRing, it % kDqRing);
+    read_frags(it + 1, buf ^ 1);
+    f32x16_t& dp = dpb[buf];
     if (kw0 == qw0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + 4 * g + (i & 3) > lq) dp[i] = 0.0f;
     }
+    if (active(it)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8_t db = pack_slots_f16(dp, t);
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8_t db = pack_slots_f16(dp, t);
 #pragma unroll
-      for (int e = 0; e < EB; ++e) dq[e] = mma_f16(frag_tr(sk, e, 32 * kh, t, lane), db, dq[e]);
+        for (int e = 0; e < EB; ++e) dq[e] = mma_f16(ktr[buf][t][e], db, dq[e]);
+      }
     }
-  });
+  };
+
+  for (int t = 0; t < kDqRing; ++t)
+    if (t < T) issue(t, t);
+  wait_tiles<NLD>(min(T - 2, kDqRing - 2));  // tiles 0 and 1
+  __syncthreads();
+  chains(0, 0);
+  read_frags(0, 0);
+  for (int it = 0; it < T; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < T) step(it + 1, std::integral_constant<int, 1>{});
+  }
+  MTNLG_VMCNT(0);
 
   __syncthreads();
   float* xs = reinterpret_cast<float*>(smem) + qg * (EB * 16) * 64;
