@@ -84,12 +84,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
   const int qw0 = q0 + 32 * qg;
   const int qw = qw0 + lq;
 
-  bf16x8_t qf[SUB];
-#pragma unroll
-  for (int s = 0; s < SUB; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)qw * ld + (int64_t)n * D + 16 * s + 8 * g);
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) settle(qf[s]);
   uint32_t voff[TL::IPW];
 #pragma unroll
   for (int u = 0; u < TL::IPW; ++u) voff[u] = tile_voff<D>(wave, u, lane, ld);
@@ -102,12 +96,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const bf16_t* __r
     issue_tile<D>(rs, voff, r0 + col_v, st + TL::BYTES, wave);
   };
 
+  // the first key tile is in flight while the query rows are read
+  issue(0, 0);
+  bf16x8_t qf[SUB];
+#pragma unroll
+  for (int s = 0; s < SUB; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)qw * ld + (int64_t)n * D + 16 * s + 8 * g);
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) settle(qf[s]);
+
   f32x16_t oacc[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) zero(oacc[e]);
   float m = -INFINITY, l = 0.0f;
 
-  ring_walk<2 * TL::IPW, kFwdRing>(qb + 1, issue, [&](int it, int stage) {
+  ring_walk<2 * TL::IPW, kFwdRing, 1>(qb + 1, issue, [&](int it, int stage) {
     const char* sk = smem + stage * STAGE;
     const char* sv = sk + TL::BYTES;
     const int kw0 = it * kRows + 32 * kh;
@@ -223,27 +226,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int qw = qw0 + lq;
   const int64_t tq = (int64_t)b * seq + qw;  // token of this lane's query
 
-  bf16x8_t qf[SUB], df[SUB];
-  float dsum = 0.0f;
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-    qf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)qw * ld + (int64_t)n * D + 16 * s + 8 * g);
-    const int64_t oo = tq * ldo + (int64_t)n * D + 16 * s + 8 * g;
-    df[s] = *reinterpret_cast<const bf16x8_t*>(dout + oo);
-    float a[8];
-    load8(o + oo, a);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dsum += a[j] * (float)df[s][j];
-  }
-  dsum = xor32_sum(dsum);
-  // log2 of the softmax normaliser, plus the dS down-shift (kDsShift): P and
-  // dS below are 2^-kDsShift times their values
-  const float lrow = fmaf(lse[(int64_t)n * tokens + tq], kLog2e, kDsShift);
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-    settle(qf[s]);
-    settle(df[s]);
-  }
   uint32_t voff[TL::IPW];
 #pragma unroll
   for (int u = 0; u < TL::IPW; ++u) voff[u] = tile_voff<D>(wave, u, lane, ld);
@@ -256,6 +238,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     issue_tile<D>(rs, voff, r0 + col_v, st + TL::BYTES, wave);
   };
 
+  // The first two key tiles are in flight while this lane's query, output
+  // gradient and output rows are read (the register loads' waits cover the
+  // older tile loads too); tiles 2 and 3 follow once the register operands
+  // have landed, so that no compiler-tracked load is pending in the loop.
+  const int T = qb + 1;  // key tiles of this query block
+  for (int t = 0; t < 2; ++t)
+    if (t < T) issue(t, t);
+  // All register operands are requested before the first wait, so that their
+  // latencies overlap one another and the two tiles' loads.
+  bf16x8_t qf[SUB], df[SUB], of[SUB];
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    qf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)qw * ld + (int64_t)n * D + 16 * s + 8 * g);
+    const int64_t oo = tq * ldo + (int64_t)n * D + 16 * s + 8 * g;
+    df[s] = *reinterpret_cast<const bf16x8_t*>(dout + oo);
+    of[s] = *reinterpret_cast<const bf16x8_t*>(o + oo);
+  }
+  const float lse_q = lse[(int64_t)n * tokens + tq];
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    settle(qf[s]);
+    settle(df[s]);
+    settle(of[s]);
+  }
+  asm volatile("" : : "v"(lse_q));
+  float dsum = 0.0f;
+#pragma unroll
+  for (int s = 0; s < SUB; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dsum += (float)of[s][j] * (float)df[s][j];
+  dsum = xor32_sum(dsum);
+  // log2 of the softmax normaliser, plus the dS down-shift (kDsShift): P and
+  // dS below are 2^-kDsShift times their values
+  const float lrow = fmaf(lse_q, kLog2e, kDsShift);
   f32x16_t dq[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) zero(dq[e]);
@@ -267,7 +283,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // stages give every tile two iterations from the issue of its loads to
   // its first use.
   constexpr int NLD = 2 * TL::IPW;  // loads per wave per tile
-  const int T = qb + 1;             // key tiles of this query block
   auto active = [&](int it) { return it * kRows + 32 * kh <= qw0; };  // some key of the half is visible
   f32x16_t sb[2], dpb[2];
   auto chains = [&](int it, int buf) {  // S and dP of tile it, alone (the first tile)
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  for (int t = 0; t < kDqRing; ++t)
+  for (int t = 2; t < kDqRing; ++t)
     if (t < T) issue(t, t);
   wait_tiles<NLD>(min(T - 2, kDqRing - 2));  // tiles 0 and 1
   __syncthreads();

@@ -147,11 +147,13 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // tile it. The loop is unrolled by the ring depth so that each stage index,
 // and with it every LDS address of the body, is a compile-time offset.
 // RING is the number of ring stages (kRing unless a kernel trades depth for a
-// second resident workgroup).
-template <int NLD, int RING = kRing, typename Issue, typename Body>
+// second resident workgroup). The caller may have issued tiles 0 .. PRE-1
+// itself (ahead of its own register loads, so that both latencies overlap).
+template <int NLD, int RING = kRing, int PRE = 0, typename Issue, typename Body>
 __device__ __forceinline__ void ring_walk(int count, Issue&& issue, Body&& body) {
+  static_assert(PRE <= RING - 1, "at most RING - 1 tiles ahead");
 #pragma unroll
-  for (int t = 0; t < RING - 1; ++t)
+  for (int t = PRE; t < RING - 1; ++t)
     if (t < count) issue(t, t);
   for (int it0 = 0; it0 < count; it0 += RING) {
 #pragma unroll

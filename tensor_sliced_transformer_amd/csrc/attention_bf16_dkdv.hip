@@ -45,17 +45,6 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
   const int kw0 = kb * kRows + 32 * kg;
   const int kw = kw0 + lq;
 
-  bf16x8_t kf[SUB], vf[SUB];
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-    kf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)kw * ld + (int64_t)(nh + n) * D + 16 * s + 8 * g);
-    vf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)kw * ld + (int64_t)(2 * nh + n) * D + 16 * s + 8 * g);
-  }
-#pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-    settle(kf[s]);
-    settle(vf[s]);
-  }
   uint32_t voff_q[TL::IPW], voff_o[TL::IPW];
 #pragma unroll
   for (int u = 0; u < TL::IPW; ++u) {
@@ -72,6 +61,22 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
     dtl16_so(rs_l, st + LD_OFF + wave * 1024, voff_l, (uint32_t)q0 * 8u);
   };
 
+  // the first two query tiles are in flight while the key and value rows are read
+  const int count = seq / kRows - kb;
+  for (int t = 0; t < 2; ++t)
+    if (t < count) issue(t, t);
+  bf16x8_t kf[SUB], vf[SUB];
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    kf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)kw * ld + (int64_t)(nh + n) * D + 16 * s + 8 * g);
+    vf[s] = *reinterpret_cast<const bf16x8_t*>(base + (int64_t)kw * ld + (int64_t)(2 * nh + n) * D + 16 * s + 8 * g);
+  }
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    settle(kf[s]);
+    settle(vf[s]);
+  }
+
   f32x16_t dk[EB], dv[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) {
@@ -79,7 +84,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
     zero(dv[e]);
   }
 
-  ring_walk<2 * TL::IPW + 1>(seq / kRows - kb, issue, [&](int it, int stage) {
+  ring_walk<2 * TL::IPW + 1, kRing, 2>(count, issue, [&](int it, int stage) {
     const char* sq = smem + stage * STAGE;
     const char* so = sq + TL::BYTES;
     const char* sl = sq + LD_OFF;
