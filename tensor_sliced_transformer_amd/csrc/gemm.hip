@@ -1426,29 +1426,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_rs_kernel(GemmArgs p) 
     const uint4 bias_raw = has_bias ? epi_bias_load(p, n0c, wn, lane) : make_uint4(0u, 0u, 0u, 0u);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __syncthreads();
-    if (has_next) {
-      lane_setup();
-      tw = tile_work(p, wnext);
-      m0 = tw.tm * BM;
-      n0 = tw.tn * BN;
-      kbeg = tw.kbeg;
-      kend = tw.kend;
-      nk = (kend - kbeg + kBK64 - 1) / kBK64;
-      item_offsets();
-#pragma unroll
-      for (int u = 0; u < NL; ++u) gload(u, 0);
+    if (!has_next) {
+      epi_dispatch<EPI>(pt != nullptr, [&](auto kind) {
+        epilogue256<decltype(kind)::value, FM, FN, TN, BN>(p, acc, slab, m0c, n0c, wm, wn, lane, pt, bias_raw,
+                                                           [] {});
+      });
+      break;
     }
+    // The next item's loads and the LDS writes that consume them share one
+    // branch, so that no path leaves those loads pending into the K loop
+    // (where the compiler would then wait for them at every iteration).
+    lane_setup();
+    tw = tile_work(p, wnext);
+    m0 = tw.tm * BM;
+    n0 = tw.tn * BN;
+    kbeg = tw.kbeg;
+    kend = tw.kend;
+    nk = (kend - kbeg + kBK64 - 1) / kBK64;
+    item_offsets();
+#pragma unroll
+    for (int u = 0; u < NL; ++u) gload(u, 0);
     epi_dispatch<EPI>(pt != nullptr, [&](auto kind) {
       epilogue256<decltype(kind)::value, FM, FN, TN, BN>(p, acc, slab, m0c, n0c, wm, wn, lane, pt, bias_raw, [&]() {
-        if (has_next) {
 #pragma unroll
-          for (int u = 0; u < NL; ++u) swrite(u, 0);
+        for (int u = 0; u < NL; ++u) swrite(u, 0);
 #pragma unroll
-          for (int u = 0; u < NL; ++u) gload(u, 1);
-        }
+        for (int u = 0; u < NL; ++u) gload(u, 1);
       });
     });
-    if (!has_next) break;
     w = wnext;
   }
 }
