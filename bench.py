@@ -282,6 +282,9 @@ def main():
                                  for r in gemm_rows) / len(gemm_rows),
         "launches": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in gemm_rows]}
 
+    if not args.no_clock:
+        result["roofline"]["power_probe"] = gemm_power_probe(torch, tst, dev, T, h, fl)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pa_np, pm_np, x_np, g_np)
 
@@ -509,6 +512,51 @@ def gemm_breakdown(torch, tst, dev, T, h, wl, fl, reps=10):
                      "ms": ms, "tflops": fl_ / (ms * 1e-3) / 1e12, "flop": fl_})
         del a, b, c, ws
     return rows
+
+
+def gemm_power_probe(torch, tst, dev, T, h, fl, reps=20):
+    """One GEMM of the step (the MLP input-gradient product, NT) run back to back
+    with the step's operand distributions and again with all-zero operands: the
+    same instructions, schedule and memory traffic, but the zero operands draw
+    less MFMA power, so the GPU holds a higher clock under its power cap. The
+    TFLOP/s and the sampled clock of the two runs show how much of the distance
+    to the nominal peak is the clock (power) and how much the kernel."""
+    M, N, K = T, fl, h
+    out = {"gemm": f"mlp_dY {M}x{N}x{K} NT"}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    a = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+    b = (torch.randn((N, K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(tst.gemm_workspace_bytes(tst.BF16, M, N, K), 16), dtype=torch.uint8, device=dev)
+    for kind in ("step_data", "zero_operands"):
+        if kind == "zero_operands":
+            a.zero_()
+            b.zero_()
+
+        def run():
+            tst.gemm(a, b, c, False, True, ws=ws)
+
+        for _ in range(5):
+            run()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            run()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        ck = clock_sample(torch, run, ms, seconds=1.0) or {}
+        row = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+               "gfx_clock_mhz": ck.get("gfx_clock_mhz"), "socket_power_w": ck.get("socket_power_w")}
+        if ck.get("gfx_clock_mhz"):
+            row["frac_at_clock"] = round(tf / (PEAK_BF16_TFLOPS * ck["gfx_clock_mhz"] / 2400.0), 4)
+        out[kind] = row
+        log(f"power probe ({kind}): {tf:.1f} TFLOP/s at {row['gfx_clock_mhz']} MHz, {row['socket_power_w']} W")
+    del a, b, c, ws
+    return out
 
 
 def adam_bench(torch, tst, dev, reps):
