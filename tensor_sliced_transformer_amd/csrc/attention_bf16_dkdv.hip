@@ -18,7 +18,7 @@ using namespace attn;
 // queries 16w .. 16w+15 into its own 1 KiB slot (lanes 8..63 load nothing
 // but still write zeros, hence the slot).
 template <int D, bool DROP>
-__global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_dkdv_bf16_kernel(const bf16_t* __restrict__ qkv,
                                                              const bf16_t* __restrict__ dout,
                                                              const float2* __restrict__ ldw,
                                                              bf16_t* __restrict__ dqkv, int seq, int nh,
@@ -90,14 +90,46 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
     const char* sl = sq + LD_OFF;
     const int qw0 = (kb + it) * kRows + 32 * qh;
     if (kw0 > qw0) return;  // 32-aligned blocks: all of this half is masked
+    // Every row fragment of the two chains is requested before the first
+    // matrix instruction, the (L, D) pairs and the transposed fragments of
+    // the first update half before the softmax arithmetic, and those of the
+    // second half between the first half's matrix instructions, so that one
+    // wave per SIMD does not wait out an LDS round trip per instruction;
+    // scheduling barriers keep this source order.
+    bf16x8_t fq[SUB], fo[SUB];
+#pragma unroll
+    for (int st = 0; st < SUB; ++st) fq[st] = frag_row(sq, 32 * qh + lq, st, g);
+#pragma unroll
+    for (int st = 0; st < SUB; ++st) fo[st] = frag_row(so, 32 * qh + lq, st, g);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16_t s, dp;
     zero(s);
     zero(dp);
 #pragma unroll
-    for (int st = 0; st < SUB; ++st) {
-      s = mma_f16(frag_row(sq, 32 * qh + lq, st, g), kf[st], s);
-      dp = mma(frag_row(so, 32 * qh + lq, st, g), vf[st], dp);
+    for (int st = 0; st < SUB; ++st) s = mma_f16(fq[st], kf[st], s);
+#pragma unroll
+    for (int st = 0; st < SUB; ++st) dp = mma(fo[st], vf[st], dp);
+    // (L, D) of queries 32*qh + 8*(i2>>1) + 4*g + 2*(i2&1) + {0, 1}; these and
+    // the first transposed fragments are read ahead except with dropout, whose
+    // mask arithmetic needs the registers
+    auto ld_pair = [&](int i2) {
+      const int ql = 32 * qh + 8 * (i2 >> 1) + 4 * g + 2 * (i2 & 1);
+      return *reinterpret_cast<const float4*>(sl + (ql >> 4) * 1024 + (ql & 15) * 8);
+    };
+    float4 pr[8];
+    if constexpr (!DROP) {
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) pr[i2] = ld_pair(i2);
     }
+    bf16x8_t tv[2][EB], tk[2][EB];
+    if constexpr (!DROP) {
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        tv[0][e] = frag_tr(so, e, 32 * qh, 0, lane);
+        tk[0][e] = frag_tr(sq, e, 32 * qh, 0, lane);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // dropout on the probabilities: dV takes P * keep * scale, and the
     // gradient reaching P is dO V^T * keep * scale (all ones without dropout)
     uint32_t keep = 0xFFFFu;
@@ -106,19 +138,18 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
                                   drop.head0 + n, b, lane);
 #pragma unroll
     for (int i2 = 0; i2 < 8; ++i2) {  // queries 32*qh + 8*(i>>2) + 4*g + (i&3), two at a time
-      const int ql = 32 * qh + 8 * (i2 >> 1) + 4 * g + 2 * (i2 & 1);
-      const float4 pr = *reinterpret_cast<const float4*>(sl + (ql >> 4) * 1024 + (ql & 15) * 8);
+      if constexpr (DROP) pr[i2] = ld_pair(i2);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int i = 2 * i2 + j;
-        const float p = fast_exp2(fmaf(s[i], scale_log2, -(j ? pr.z : pr.x)));
+        const float p = fast_exp2(fmaf(s[i], scale_log2, -(j ? pr[i2].z : pr[i2].x)));
         if (DROP) {
           const bool kept = (keep >> i) & 1u;
           s[i] = kept ? p * drop.scale : 0.0f;
-          dp[i] = p * ((kept ? dp[i] * drop.scale : 0.0f) - (j ? pr.w : pr.y));
+          dp[i] = p * ((kept ? dp[i] * drop.scale : 0.0f) - (j ? pr[i2].w : pr[i2].y));
         } else {
           s[i] = p;
-          dp[i] = p * (dp[i] - (j ? pr.w : pr.y));
+          dp[i] = p * (dp[i] - (j ? pr[i2].w : pr[i2].y));
         }
       }
     }
@@ -130,14 +161,33 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(const bf16_t* __res
           dp[i] = 0.0f;
         }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8_t pb = pack_slots(s, t);
-      const bf16x8_t db = pack_slots_f16(dp, t);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DROP) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        dv[e] = mma(frag_tr(so, e, 32 * qh, t, lane), pb, dv[e]);
-        dk[e] = mma_f16(frag_tr(sq, e, 32 * qh, t, lane), db, dk[e]);
+        tv[0][e] = frag_tr(so, e, 32 * qh, 0, lane);
+        tk[0][e] = frag_tr(sq, e, 32 * qh, 0, lane);
+      }
+    }
+    {
+      const bf16x8_t pb = pack_slots(s, 0);
+      const bf16x8_t db = pack_slots_f16(dp, 0);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        dv[e] = mma(tv[0][e], pb, dv[e]);
+        dk[e] = mma_f16(tk[0][e], db, dk[e]);
+        tv[1][e] = frag_tr(so, e, 32 * qh, 1, lane);
+        tk[1][e] = frag_tr(sq, e, 32 * qh, 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {
+      const bf16x8_t pb = pack_slots(s, 1);
+      const bf16x8_t db = pack_slots_f16(dp, 1);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        dv[e] = mma(tv[1][e], pb, dv[e]);
+        dk[e] = mma_f16(tk[1][e], db, dk[e]);
       }
     }
   });
