@@ -367,6 +367,14 @@ typedef struct {
                               mtnlg_reduce_partials_dropout */
   uint64_t dropout_seed;   /* the generator key's first word; the site of micro-batch k,
                               layer l, half h is (k * layers + l) * 2 + h */
+  int32_t per_micro_batch_grads; /* with recompute = 0: 0 computes every layer's weight and
+                              bias gradients once, over all micro-batches' tokens, after the
+                              last micro-batch's backward of that layer (the saved tensors
+                              and output gradients of every micro-batch are kept); 1
+                              computes them per micro-batch and accumulates as with
+                              recompute = 1. Ignored (per micro-batch) when recompute = 1,
+                              and when a batched operand (micro_batches * T rows of the
+                              widest activation) would reach 2 GiB. */
 } mtnlg_stage_desc;
 /* layer.attn_dropout > 0 also drops attention probabilities: micro-batch k,
  * layer l keys its mask with (layer.attn_dropout_seed,
@@ -391,14 +399,24 @@ size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
 /* One training step of the stage: for each micro-batch k in order, the
  * forward through every layer, then the backward in reverse order (with
  * dropout_p > 0 each half's output goes through mtnlg_reduce_partials_dropout
- * and its backward starts from mtnlg_dropout_bwd of the same site); then the
- * flat gradient is accumulated into acc (overwritten by k = 0, added for
- * k > 0; the last accumulation carries the norm pass, see
- * mtnlg_grad_accumulate_norm); then mtnlg_adam_update with cfg.
+ * and its backward starts from mtnlg_dropout_bwd of the same site).
+ * Per-micro-batch gradients (recompute = 1 or per_micro_batch_grads = 1):
+ * each micro-batch's flat gradient is accumulated into acc (overwritten by
+ * k = 0, added for k > 0; the last accumulation carries the norm pass, see
+ * mtnlg_grad_accumulate_norm). Batched gradients (the default with
+ * recompute = 0): the backward of every micro-batch computes only the input
+ * gradients, keeping each half's output gradient, its dU or dQKV and its
+ * LayerNorm partial sums; after the last micro-batch's backward of a layer,
+ * that layer's weight gradients are single products over micro_batches * T
+ * rows (fp32 accumulation inside the product, one bf16 rounding into grad)
+ * and its bias and LayerNorm gradients single column sums; acc is then
+ * overwritten by grad with the norm pass. Either way mtnlg_adam_update with
+ * cfg follows.
  *   w       [n] bf16 flat weights; read by every layer and rewritten by the
  *           step as bf16(master)
  *   master, m, v  [n] f32 optimizer state (updated in place)
- *   grad    [n] bf16 scratch: one micro-batch's gradient
+ *   grad    [n] bf16 scratch: one micro-batch's gradient (batched: the sum over
+ *           all micro-batches)
  *   acc     [n] f32: the accumulated gradient (left holding it)
  *   x       [micro_batches, T, h] bf16: stage input (T = batch * seq)
  *   dy      [micro_batches, T, h] bf16: gradient of the stage output
@@ -407,13 +425,14 @@ size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
  *   stats   DEVICE f32[3]: {norm, coef, found_inf} of the step
  *   ws      >= mtnlg_stage_workspace_bytes(desc)
  *   aux_stream  nullable second hipStream_t. When given (and different from
- *           stream), the gradient of each layer of every micro-batch but the
- *           last is accumulated on it as soon as that layer's backward is
- *           done, overlapping the accumulation with the rest of the work;
- *           ordering between the two streams uses 2 * layers events that
- *           the library creates on first use and keeps, per calling thread
- *           and device, until the process ends (a later call on the same
- *           thread records them again; a stream wait refers to the record
+ *           stream), the per-micro-batch gradient of each layer of every
+ *           micro-batch but the last is accumulated on it as soon as that
+ *           layer's backward is done, overlapping the accumulation with the
+ *           rest of the work (batched gradients leave it unused); ordering
+ *           between the two streams uses 2 * layers events that the library
+ *           creates on first use and keeps, per calling thread and device,
+ *           until the process ends (a later call on the same thread records
+ *           them again; a stream wait refers to the record
  *           made before it, so reuse does not change the ordering). Results are
  *           identical with and without it. All of the step's work is
  *           complete once `stream` has passed it.

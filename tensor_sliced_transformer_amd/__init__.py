@@ -275,8 +275,9 @@ STAGE_TENSORS = ("ln_g", "ln_b", "w_in", "b_in", "w_out", "b_out")
 
 
 def make_stage_desc(layer: LayerDesc, layers: int, micro_batches: int, recompute: bool = False,
-                    dropout_p: float = 0.0, dropout_seed: int = 0) -> StageDesc:
-    return StageDesc(layer, layers, micro_batches, int(recompute), dropout_p, dropout_seed)
+                    dropout_p: float = 0.0, dropout_seed: int = 0, per_micro_batch_grads: bool = False) -> StageDesc:
+    return StageDesc(layer, layers, micro_batches, int(recompute), dropout_p, dropout_seed,
+                     int(per_micro_batch_grads))
 
 
 def stage_param_count(sd: StageDesc) -> int:

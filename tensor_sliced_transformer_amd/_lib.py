@@ -31,7 +31,7 @@ class LayerDesc(ctypes.Structure):
 
 class StageDesc(ctypes.Structure):
     _fields_ = [("layer", LayerDesc), ("layers", c_int32), ("micro_batches", c_int32), ("recompute", c_int32),
-                ("dropout_p", c_float), ("dropout_seed", ctypes.c_uint64)]
+                ("dropout_p", c_float), ("dropout_seed", ctypes.c_uint64), ("per_micro_batch_grads", c_int32)]
 
 
 class Dropout(ctypes.Structure):

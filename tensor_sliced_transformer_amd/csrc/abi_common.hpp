@@ -58,5 +58,48 @@ inline const void* const kNoWorkspace = reinterpret_cast<const void*>(~uintptr_t
 int adam_args(const mtnlg_adam_cfg* cfg, int64_t n, float* master, float* m, float* v, const float* grad,
               void* w_bf16, float* stats, const void* ws, size_t ws_bytes, AdamScalars* c);
 
+// ---- layer halves for the pipeline stage (api.cpp) ----
+// Where one half's saved tensors are (ATTN: a = QKV, b = O, c = log-sum-exp;
+// MLP: a = U, b = Y, c unused).
+struct SavedPtrs {
+  void* ln_out;
+  float* mean;
+  float* rstd;
+  void* a;
+  void* b;
+  float* c;
+};
+// Outputs of an input-gradient-only backward: dU (MLP) or dQKV (ATTN), and
+// the LayerNorm's (dgamma, dbeta) partial rows.
+struct DataOnly {
+  void* g;
+  float* lnp;
+};
+// Bytes of one micro-batch's copy of each saved field, of g, of the
+// LayerNorm partial rows, and of one row of the widest activation.
+struct SavedSizes {
+  size_t ln_out, stats, a, b, c, g, lnp, widest;
+};
+int half_saved_sizes(const mtnlg_layer_desc* desc, int half, SavedSizes* out);
+// Workspace of half_fwd and half_bwd_data (the layer backward's), and of
+// half_weight_grads over mb micro-batches.
+size_t half_bwd_ws_bytes(const mtnlg_layer_desc* desc, int half);
+size_t half_weight_grads_ws_bytes(const mtnlg_layer_desc* desc, int half, int mb);
+// The forward of a half into the saved fields S (mtnlg_layer_fwd's work).
+int half_fwd(const mtnlg_layer_desc* desc, int half, const mtnlg_half_params* params, const void* x,
+             void* y_partial, const SavedPtrs& S, void* ws, hipStream_t st);
+// The backward of a half without its weight products and bias column sums:
+// dx_partial, g_out (dU or dQKV) and the LayerNorm partial rows lnp_out.
+int half_bwd_data(const mtnlg_layer_desc* desc, int half, const mtnlg_half_params* params, const void* x,
+                  const SavedPtrs& S, const void* dy, void* dx_partial, void* g_out, float* lnp_out, void* ws,
+                  hipStream_t st);
+// The weight, bias and LayerNorm gradients of a half over mb micro-batches
+// whose saved fields (S: micro-batch 0's, the rest following each field
+// back to back), output gradients dy_all, g_all and partial rows lnp_all lie
+// back to back: each weight gradient is one product over mb * T rows.
+int half_weight_grads(const mtnlg_layer_desc* desc, int half, int mb, const SavedPtrs& S, const void* dy_all,
+                      const void* g_all, const float* lnp_all, const mtnlg_half_grads* grads, void* ws,
+                      hipStream_t st);
+
 }  // namespace abi
 }  // namespace mtnlg

@@ -86,6 +86,9 @@ int validate_desc(const mtnlg_layer_desc* desc, int32_t half, Dims* out) {
   return MTNLG_OK;
 }
 
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
+
 // ---- saved layout ----
 struct SavedLayout {
   size_t ln_out, mean, rstd, a, b, c, total;  // ATTN: a=qkv b=o c=lse; MLP: a=u b=y
@@ -108,6 +111,22 @@ SavedLayout saved_layout(const Dims& d, int half) {
   }
   L.total = off;
   return L;
+}
+
+// Where the saved tensors of one half are: the fields of a `saved` region
+// (the layer entry points), or fields placed elsewhere (a stage keeping
+// every micro-batch's copy of a field back to back).
+SavedPtrs saved_ptrs(const void* saved, const Dims& d, int half) {
+  const SavedLayout L = saved_layout(d, half);
+  char* b = const_cast<char*>(static_cast<const char*>(saved));
+  SavedPtrs S;
+  S.ln_out = b + L.ln_out;
+  S.mean = reinterpret_cast<float*>(b + L.mean);
+  S.rstd = reinterpret_cast<float*>(b + L.rstd);
+  S.a = b + L.a;
+  S.b = b + L.b;
+  S.c = half == MTNLG_ATTN ? reinterpret_cast<float*>(b + L.c) : nullptr;
+  return S;
 }
 
 // ---- GEMMs of each half: (M, N, K) of the forward and backward products ----
@@ -168,23 +187,19 @@ AttnDropout attn_dropout(const mtnlg_layer_desc* desc, const Dims& d) {
   return a;
 }
 
-char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
-const char* at(const void* base, size_t off) { return static_cast<const char*>(base) + off; }
-
 // The forward of one half into `saved`; the row-sliced output GEMM is
 // skipped when y_partial is NULL (a recompute needs only what is saved).
 int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mtnlg_half_params* params,
-                 const void* x, void* y_partial, void* saved, void* gws, hipStream_t st) {
-  const SavedLayout L = saved_layout(d, half);
-  void* ln_out = at(saved, L.ln_out);
-  float* mean = reinterpret_cast<float*>(at(saved, L.mean));
-  float* rstd = reinterpret_cast<float*>(at(saved, L.rstd));
+                 const void* x, void* y_partial, const SavedPtrs& S, void* gws, hipStream_t st) {
+  void* ln_out = S.ln_out;
+  float* mean = S.mean;
+  float* rstd = S.rstd;
   MTNLG_HIP(layernorm_fwd(d.dtype, d.T, d.h, x, params->ln_g, params->ln_b, desc->ln_eps, ln_out, mean, rstd, st),
             "layernorm_fwd");
   if (half == MTNLG_ATTN) {
-    void* qkv = at(saved, L.a);
-    void* o = at(saved, L.b);
-    float* lse = reinterpret_cast<float*>(at(saved, L.c));
+    void* qkv = S.a;
+    void* o = S.b;
+    float* lse = S.c;
     const int64_t n3 = 3 * d.w;
     // bf16: Q and K leave the product in fp16 (see the attention kernels)
     const bool f16qk = d.dtype == MTNLG_BF16;
@@ -200,8 +215,8 @@ int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mt
                      nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.w, true), gws, st),
                 "out-proj gemm");
   } else {
-    void* u = at(saved, L.a);
-    void* y = at(saved, L.b);
+    void* u = S.a;
+    void* y = S.b;
     MTNLG_HIP(gemm(d.dtype, true, false, d.T, d.fl, d.h, ln_out, d.h, params->w_in, d.fl, u, d.fl, EPI_BIAS_GELU,
                    params->b_in, y, nullptr, plan_gemm(d.dtype, d.T, d.fl, d.h, true), gws, st),
               "mlp-up gemm");
@@ -214,76 +229,207 @@ int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mt
 }
 
 
-// The backward of one half from `saved` (workspace laid out by ws_layout).
+// The backward of one half from its saved tensors (workspace laid out by
+// ws_layout). With `dd`, only the input gradient: the weight products and
+// the bias column sums are skipped, dU (MLP) or dQKV (ATTN) is written to
+// dd->g, and the LayerNorm's (dgamma, dbeta) partial rows to dd->lnp
+// (weight_grads reduces them later); grads is unused then.
 int backward_from(const mtnlg_layer_desc* desc, const Dims& d, int half, const mtnlg_half_params* params,
-                  const void* x, const void* saved, const void* dy, void* dx_partial, const mtnlg_half_grads* grads,
-                  void* ws, hipStream_t st) {
+                  const void* x, const SavedPtrs& S, const void* dy, void* dx_partial, const mtnlg_half_grads* grads,
+                  void* ws, hipStream_t st, const DataOnly* dd = nullptr) {
   const WsLayout W = ws_layout(d, half);
-  const SavedLayout L = saved_layout(d, half);
-  const void* ln_out = at(saved, L.ln_out);
-  const float* mean = reinterpret_cast<const float*>(at(saved, L.mean));
-  const float* rstd = reinterpret_cast<const float*>(at(saved, L.rstd));
+  const bool full = dd == nullptr;
+  const void* ln_out = S.ln_out;
+  const float* mean = S.mean;
+  const float* rstd = S.rstd;
   void* dln = at(ws, W.dln);
   void* cs = at(ws, W.cs);
   void* gws = at(ws, W.gemm);
 
-  MTNLG_HIP(colsum(d.dtype, d.T, d.h, dy, grads->b_out, cs, st), "b_out colsum");
+  if (full) MTNLG_HIP(colsum(d.dtype, d.T, d.h, dy, grads->b_out, cs, st), "b_out colsum");
   if (half == MTNLG_MLP) {
-    const void* u = at(saved, L.a);
-    const void* y = at(saved, L.b);
-    void* du = at(ws, W.t1);
+    const void* u = S.a;
+    const void* y = S.b;
+    void* du = full ? at(ws, W.t1) : dd->g;
     // dU = (dy B^T) * GeLU'(u)
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.fl, d.h, dy, d.h, params->w_out, d.h, du, d.fl, EPI_GELU_GRAD,
                    nullptr, nullptr, u, plan_gemm(d.dtype, d.T, d.fl, d.h, true), gws, st),
               "mlp dY gemm");
-    // dB = Y^T dy
-    MTNLG_HIP(gemm(d.dtype, false, false, d.fl, d.h, d.T, y, d.fl, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.fl, d.h, d.T, true), gws, st),
-              "mlp dB gemm");
-    MTNLG_HIP(colsum(d.dtype, d.T, d.fl, du, grads->b_in, cs, st), "mlp da colsum");
-    // dA = LN2(x)^T dU
-    MTNLG_HIP(gemm(d.dtype, false, false, d.h, d.fl, d.T, ln_out, d.h, du, d.fl, grads->w_in, d.fl, EPI_STORE,
-                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, d.fl, d.T, true), gws, st),
-              "mlp dA gemm");
+    if (full) {
+      // dB = Y^T dy
+      MTNLG_HIP(gemm(d.dtype, false, false, d.fl, d.h, d.T, y, d.fl, dy, d.h, grads->w_out, d.h, EPI_STORE,
+                     nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.fl, d.h, d.T, true), gws, st),
+                "mlp dB gemm");
+      MTNLG_HIP(colsum(d.dtype, d.T, d.fl, du, grads->b_in, cs, st), "mlp da colsum");
+      // dA = LN2(x)^T dU
+      MTNLG_HIP(gemm(d.dtype, false, false, d.h, d.fl, d.T, ln_out, d.h, du, d.fl, grads->w_in, d.fl, EPI_STORE,
+                     nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, d.fl, d.T, true), gws, st),
+                "mlp dA gemm");
+    }
     // dLN = dU A^T
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.h, d.fl, du, d.fl, params->w_in, d.fl, dln, d.h, EPI_STORE, nullptr,
                    nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, d.fl, true), gws, st),
               "mlp dX gemm");
   } else {
-    const void* qkv = at(saved, L.a);
-    const void* o = at(saved, L.b);
-    const float* lse = reinterpret_cast<const float*>(at(saved, L.c));
+    const void* qkv = S.a;
+    const void* o = S.b;
+    const float* lse = S.c;
     void* dO = at(ws, W.t1);
-    void* dqkv = at(ws, W.t2);
+    void* dqkv = full ? at(ws, W.t2) : dd->g;
     const int64_t n3 = 3 * d.w;
     // dO = dy W_o^T (short N: split K)
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.w, d.h, dy, d.h, params->w_out, d.h, dO, d.w, EPI_STORE, nullptr,
                    nullptr, nullptr, plan_gemm(d.dtype, d.T, d.w, d.h, true), gws, st),
               "attn dO gemm");
     // dW_o = O^T dy
-    MTNLG_HIP(gemm(d.dtype, false, false, d.w, d.h, d.T, o, d.w, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, d.T, true), gws, st),
-              "attn dWo gemm");
+    if (full)
+      MTNLG_HIP(gemm(d.dtype, false, false, d.w, d.h, d.T, o, d.w, dy, d.h, grads->w_out, d.h, EPI_STORE, nullptr,
+                     nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, d.T, true), gws, st),
+                "attn dWo gemm");
     MTNLG_HIP(attention_bwd(d.dtype, desc->batch, desc->seq, (int)d.nhl, (int)d.d, qkv, o, lse, dO, dqkv,
                             at(ws, W.attn), attn_dropout(desc, d), st),
               "attention_bwd");
-    MTNLG_HIP(colsum(d.dtype, d.T, n3, dqkv, grads->b_in, cs, st), "attn dbqkv colsum");
-    // dW_qkv = LN1(x)^T dQKV
-    MTNLG_HIP(gemm(d.dtype, false, false, d.h, n3, d.T, ln_out, d.h, dqkv, n3, grads->w_in, n3, EPI_STORE, nullptr,
-                   nullptr, nullptr, plan_gemm(d.dtype, d.h, n3, d.T, true), gws, st),
-              "attn dWqkv gemm");
+    if (full) {
+      MTNLG_HIP(colsum(d.dtype, d.T, n3, dqkv, grads->b_in, cs, st), "attn dbqkv colsum");
+      // dW_qkv = LN1(x)^T dQKV
+      MTNLG_HIP(gemm(d.dtype, false, false, d.h, n3, d.T, ln_out, d.h, dqkv, n3, grads->w_in, n3, EPI_STORE,
+                     nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, n3, d.T, true), gws, st),
+                "attn dWqkv gemm");
+    }
     // dLN = dQKV W_qkv^T
     MTNLG_HIP(gemm(d.dtype, true, true, d.T, d.h, n3, dqkv, n3, params->w_in, n3, dln, d.h, EPI_STORE, nullptr,
                    nullptr, nullptr, plan_gemm(d.dtype, d.T, d.h, n3, true), gws, st),
               "attn dX gemm");
   }
-  MTNLG_HIP(layernorm_bwd(d.dtype, d.dtype, d.T, d.h, dln, x, mean, rstd, params->ln_g, dx_partial, grads->ln_g,
-                          grads->ln_b, at(ws, W.lnp), st),
-            "layernorm_bwd");
+  if (full)
+    MTNLG_HIP(layernorm_bwd(d.dtype, d.dtype, d.T, d.h, dln, x, mean, rstd, params->ln_g, dx_partial, grads->ln_g,
+                            grads->ln_b, at(ws, W.lnp), st),
+              "layernorm_bwd");
+  else
+    MTNLG_HIP(layernorm_bwd_partials(d.dtype, d.dtype, d.T, d.h, dln, x, mean, rstd, params->ln_g, dx_partial,
+                                     dd->lnp, st),
+              "layernorm_bwd");
   return MTNLG_OK;
 }
 
+// ---- weight and bias gradients over several micro-batches at once ----
+// R = mb * T rows: every operand below holds the micro-batches' rows back to
+// back. Workspace: the products' tail partials, then the column sums'.
+struct WgLayout {
+  size_t gemm, cs, total;
+};
 
+WgLayout wg_layout(const Dims& d, int half, int64_t R) {
+  const int64_t n_in = half == MTNLG_ATTN ? 3 * d.w : d.fl;  // w_in columns
+  const int64_t n_out = half == MTNLG_ATTN ? d.w : d.fl;     // w_out rows
+  const Shape3 g[2] = {{n_out, d.h, R}, {d.h, n_in, R}};
+  size_t gws = 0;
+  for (const Shape3& s : g)
+    gws = std::max(gws, gemm_workspace_bytes(plan_gemm(d.dtype, s.M, s.N, s.K, true), s.M, s.N));
+  WgLayout L{};
+  L.gemm = 0;
+  L.cs = align256(gws);
+  L.total = L.cs + align256(colsum_ws(R, std::max(d.h, n_in)));
+  return L;
+}
+
+int weight_grads(const Dims& d, int half, int mb, const SavedPtrs& S, const void* dy_all, const void* g_all,
+                 const float* lnp_all, const mtnlg_half_grads* grads, void* ws, hipStream_t st) {
+  const int64_t R = (int64_t)mb * d.T;
+  const WgLayout W = wg_layout(d, half, R);
+  void* gws = at(ws, W.gemm);
+  void* cs = at(ws, W.cs);
+  MTNLG_HIP(colsum(d.dtype, R, d.h, dy_all, grads->b_out, cs, st), "b_out colsum");
+  if (half == MTNLG_MLP) {
+    // dB = Y^T dy, db_A = colsum(dU), dA = LN2(x)^T dU over all R rows
+    MTNLG_HIP(gemm(d.dtype, false, false, d.fl, d.h, R, S.b, d.fl, dy_all, d.h, grads->w_out, d.h, EPI_STORE,
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.fl, d.h, R, true), gws, st),
+              "mlp dB gemm");
+    MTNLG_HIP(colsum(d.dtype, R, d.fl, g_all, grads->b_in, cs, st), "mlp da colsum");
+    MTNLG_HIP(gemm(d.dtype, false, false, d.h, d.fl, R, S.ln_out, d.h, g_all, d.fl, grads->w_in, d.fl, EPI_STORE,
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.h, d.fl, R, true), gws, st),
+              "mlp dA gemm");
+  } else {
+    const int64_t n3 = 3 * d.w;
+    // dW_o = O^T dy, db_qkv = colsum(dQKV), dW_qkv = LN1(x)^T dQKV over all R rows
+    MTNLG_HIP(gemm(d.dtype, false, false, d.w, d.h, R, S.b, d.w, dy_all, d.h, grads->w_out, d.h, EPI_STORE,
+                   nullptr, nullptr, nullptr, plan_gemm(d.dtype, d.w, d.h, R, true), gws, st),
+              "attn dWo gemm");
+    MTNLG_HIP(colsum(d.dtype, R, n3, g_all, grads->b_in, cs, st), "attn dbqkv colsum");
+    MTNLG_HIP(gemm(d.dtype, false, false, d.h, n3, R, S.ln_out, d.h, g_all, n3, grads->w_in, n3, EPI_STORE, nullptr,
+                   nullptr, nullptr, plan_gemm(d.dtype, d.h, n3, R, true), gws, st),
+              "attn dWqkv gemm");
+  }
+  MTNLG_HIP(layernorm_bwd_reduce(d.dtype, mb * layernorm_bwd_blocks(d.T), d.h, lnp_all, grads->ln_g, grads->ln_b,
+                                 st),
+            "layernorm grads");
+  return MTNLG_OK;
+}
+
+}  // namespace
+
+// ---- entry points for the pipeline stage (abi_common.hpp) ----
+namespace mtnlg {
+namespace abi {
+
+int half_saved_sizes(const mtnlg_layer_desc* desc, int half, SavedSizes* out) {
+  Dims d;
+  const int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  out->ln_out = (size_t)(d.T * d.h) * d.eb;
+  out->stats = (size_t)d.T * sizeof(float);
+  out->a = (size_t)(d.T * (half == MTNLG_ATTN ? 3 * d.w : d.fl)) * d.eb;
+  out->b = (size_t)(d.T * (half == MTNLG_ATTN ? d.w : d.fl)) * d.eb;
+  out->c = half == MTNLG_ATTN ? (size_t)(d.nhl * d.T) * sizeof(float) : 0;
+  out->g = out->a;  // dU or dQKV: the shape of a
+  out->lnp = (size_t)layernorm_bwd_blocks(d.T) * 2 * (size_t)d.h * sizeof(float);
+  out->widest = (size_t)std::max<int64_t>(d.h, std::max<int64_t>(3 * d.w, d.fl)) * d.eb;
+  return MTNLG_OK;
+}
+
+size_t half_bwd_ws_bytes(const mtnlg_layer_desc* desc, int half) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return ws_layout(d, half).total;
+}
+
+size_t half_weight_grads_ws_bytes(const mtnlg_layer_desc* desc, int half, int mb) {
+  Dims d;
+  if (validate_desc(desc, half, &d) != MTNLG_OK) return 0;
+  return wg_layout(d, half, (int64_t)mb * d.T).total;
+}
+
+int half_fwd(const mtnlg_layer_desc* desc, int half, const mtnlg_half_params* params, const void* x,
+             void* y_partial, const SavedPtrs& S, void* ws, hipStream_t st) {
+  Dims d;
+  const int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  return forward_into(desc, d, half, params, x, y_partial, S, at(ws, ws_layout(d, half).gemm), st);
+}
+
+int half_bwd_data(const mtnlg_layer_desc* desc, int half, const mtnlg_half_params* params, const void* x,
+                  const SavedPtrs& S, const void* dy, void* dx_partial, void* g_out, float* lnp_out, void* ws,
+                  hipStream_t st) {
+  Dims d;
+  const int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  const DataOnly dd{g_out, lnp_out};
+  return backward_from(desc, d, half, params, x, S, dy, dx_partial, nullptr, ws, st, &dd);
+}
+
+int half_weight_grads(const mtnlg_layer_desc* desc, int half, int mb, const SavedPtrs& S, const void* dy_all,
+                      const void* g_all, const float* lnp_all, const mtnlg_half_grads* grads, void* ws,
+                      hipStream_t st) {
+  Dims d;
+  const int s = validate_desc(desc, half, &d);
+  if (s != MTNLG_OK) return s;
+  return weight_grads(d, half, mb, S, dy_all, g_all, lnp_all, grads, ws, st);
+}
+
+}  // namespace abi
+}  // namespace mtnlg
+
+namespace {
 }  // namespace
 
 extern "C" {
@@ -338,7 +484,8 @@ int mtnlg_layer_fwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
     if (ws_bytes < need) return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   }
   void* gws = need > 0 ? at(ws, W.gemm) : nullptr;
-  return forward_into(desc, d, half, params, x, y_partial, saved, gws, static_cast<hipStream_t>(stream));
+  return forward_into(desc, d, half, params, x, y_partial, saved_ptrs(saved, d, half), gws,
+                      static_cast<hipStream_t>(stream));
 }
 
 int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half_params* params, const void* x,
@@ -369,7 +516,7 @@ int mtnlg_layer_bwd(const mtnlg_layer_desc* desc, int32_t half, const mtnlg_half
   const WsLayout W = ws_layout(d, half);
   if (ws_bytes < W.total)
     return fail(MTNLG_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, W.total);
-  return backward_from(desc, d, half, params, x, saved, dy, dx_partial, grads, ws,
+  return backward_from(desc, d, half, params, x, saved_ptrs(saved, d, half), dy, dx_partial, grads, ws,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -410,9 +557,10 @@ int mtnlg_layer_bwd_recompute(const mtnlg_layer_desc* desc, int32_t half, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* saved = ws;
   void* rest = at(ws, sv);
-  s = forward_into(desc, d, half, params, x, nullptr, saved, at(rest, W.gemm), st);
+  const SavedPtrs S = saved_ptrs(saved, d, half);
+  s = forward_into(desc, d, half, params, x, nullptr, S, at(rest, W.gemm), st);
   if (s != MTNLG_OK) return s;
-  return backward_from(desc, d, half, params, x, saved, dy, dx_partial, grads, rest, st);
+  return backward_from(desc, d, half, params, x, S, dy, dx_partial, grads, rest, st);
 }
 
 int mtnlg_reduce_partials(int64_t rows, int64_t cols, int32_t dtype, const void* const* partials, int32_t n,

@@ -73,6 +73,15 @@ size_t layernorm_bwd_ws(int64_t rows, int64_t cols);
 hipError_t layernorm_bwd(int dtype, int gy_dtype, int64_t rows, int64_t cols, const void* gy,
                          const void* x, const float* mean, const float* rstd, const void* gamma,
                          void* dx, void* dgamma, void* dbeta, void* ws, hipStream_t st);
+// layernorm_bwd in two steps: dx and the per-workgroup [blocks][2][cols] fp32
+// partial sums of (dgamma, dbeta); then their column sums over P partial rows
+// (the partials of several calls can be reduced together, rows back to back).
+int layernorm_bwd_blocks(int64_t rows);
+hipError_t layernorm_bwd_partials(int dtype, int gy_dtype, int64_t rows, int64_t cols, const void* gy,
+                                  const void* x, const float* mean, const float* rstd, const void* gamma, void* dx,
+                                  float* part, hipStream_t st);
+hipError_t layernorm_bwd_reduce(int dtype, int P, int64_t cols, const float* part, void* dgamma, void* dbeta,
+                                hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 // Dropout on the attention probabilities (bf16 kernels; see attention_bf16.hpp

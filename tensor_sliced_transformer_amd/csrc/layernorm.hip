@@ -438,26 +438,38 @@ size_t layernorm_bwd_ws(int64_t rows, int64_t cols) {
   return (size_t)ln_bwd_blocks(rows) * 2 * cols * sizeof(float);
 }
 
-hipError_t layernorm_bwd(int dtype, int gy_dtype, int64_t rows, int64_t cols, const void* gy, const void* x,
-                         const float* mean, const float* rstd, const void* gamma, void* dx, void* dgamma,
-                         void* dbeta, void* ws, hipStream_t st) {
+int layernorm_bwd_blocks(int64_t rows) { return rows > 0 ? ln_bwd_blocks(rows) : 0; }
+
+hipError_t layernorm_bwd_partials(int dtype, int gy_dtype, int64_t rows, int64_t cols, const void* gy,
+                                  const void* x, const float* mean, const float* rstd, const void* gamma, void* dx,
+                                  float* part, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int c = (int)cols;
   const int blocks = ln_bwd_blocks(rows);
   const int rpb = (int)((rows + blocks - 1) / blocks);
-  float* part = static_cast<float*>(ws);
-  hipError_t e;
   if (dtype == kBF16) {
     if (gy_dtype == kBF16)
-      e = ln_bwd_launch<bf16_t, bf16_t>(rows, c, gy, x, mean, rstd, gamma, dx, part, blocks, rpb, st);
-    else
-      e = ln_bwd_launch<bf16_t, float>(rows, c, gy, x, mean, rstd, gamma, dx, part, blocks, rpb, st);
-  } else {
-    e = ln_bwd_launch<float, float>(rows, c, gy, x, mean, rstd, gamma, dx, part, blocks, rpb, st);
+      return ln_bwd_launch<bf16_t, bf16_t>(rows, c, gy, x, mean, rstd, gamma, dx, part, blocks, rpb, st);
+    return ln_bwd_launch<bf16_t, float>(rows, c, gy, x, mean, rstd, gamma, dx, part, blocks, rpb, st);
   }
+  return ln_bwd_launch<float, float>(rows, c, gy, x, mean, rstd, gamma, dx, part, blocks, rpb, st);
+}
+
+hipError_t layernorm_bwd_reduce(int dtype, int P, int64_t cols, const float* part, void* dgamma, void* dbeta,
+                                hipStream_t st) {
+  if (P == 0) return hipSuccess;
+  if (dtype == kBF16) return col_reduce_launch<bf16_t>(part, P, 2, (int)cols, dgamma, dbeta, st);
+  return col_reduce_launch<float>(part, P, 2, (int)cols, dgamma, dbeta, st);
+}
+
+hipError_t layernorm_bwd(int dtype, int gy_dtype, int64_t rows, int64_t cols, const void* gy, const void* x,
+                         const float* mean, const float* rstd, const void* gamma, void* dx, void* dgamma,
+                         void* dbeta, void* ws, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  float* part = static_cast<float*>(ws);
+  const hipError_t e = layernorm_bwd_partials(dtype, gy_dtype, rows, cols, gy, x, mean, rstd, gamma, dx, part, st);
   if (e != hipSuccess) return e;
-  if (dtype == kBF16) return col_reduce_launch<bf16_t>(part, blocks, 2, c, dgamma, dbeta, st);
-  return col_reduce_launch<float>(part, blocks, 2, c, dgamma, dbeta, st);
+  return layernorm_bwd_reduce(dtype, ln_bwd_blocks(rows), cols, part, dgamma, dbeta, st);
 }
 
 size_t colsum_ws(int64_t rows, int64_t cols) {

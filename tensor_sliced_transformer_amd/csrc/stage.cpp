@@ -9,8 +9,21 @@
 // one GPU holds 3 layer slices, and gradients of several micro-batches are
 // accumulated before each step (Elamur summary, Key points). Each micro-batch
 // runs forward then backward before the next starts: with no neighbouring
-// stage this is the order a one-forward-one-backward schedule gives, and it
-// keeps the saved activations of a single micro-batch alive at a time.
+// stage this is the order a one-forward-one-backward schedule gives.
+//
+// Gradients over the micro-batches: the sum over micro-batches of X_k^T dY_k
+// is X^T dY with the micro-batches' rows stacked, so by default (saved
+// tensors kept) the backward of each micro-batch computes only the input
+// gradients and keeps what the weight gradients need (each half's saved
+// tensors, its output gradient, its dU or dQKV and its LayerNorm partial
+// rows, every micro-batch's copy of a field back to back in HBM); after the
+// last micro-batch's backward of a layer, each of its weight gradients is one
+// product over micro_batches * T rows, with fp32 accumulation throughout, and
+// each bias gradient one column sum. The products then run with a K of
+// micro_batches * T instead of T (fewer tile epilogues per FLOP) and no
+// per-micro-batch accumulation pass is left. The recompute schedule (which
+// keeps only each half's input) and per_micro_batch_grads = 1 instead
+// accumulate every micro-batch's gradient into the fp32 accumulator.
 #include <math.h>
 #include <string.h>
 
@@ -36,6 +49,8 @@ int stage_dims(const mtnlg_stage_desc* sd, StageDims* o) {
   if (!sd) return fail(MTNLG_ERR_ARG, "stage desc is NULL");
   if (sd->layers < 1 || sd->micro_batches < 1) return fail(MTNLG_ERR_SHAPE, "layers and micro_batches must be >= 1");
   if (sd->recompute != 0 && sd->recompute != 1) return fail(MTNLG_ERR_ARG, "recompute must be 0 or 1");
+  if (sd->per_micro_batch_grads != 0 && sd->per_micro_batch_grads != 1)
+    return fail(MTNLG_ERR_ARG, "per_micro_batch_grads must be 0 or 1");
   if (!(sd->dropout_p >= 0.0f && sd->dropout_p < 1.0f) || nearbyint((double)sd->dropout_p * 65536.0) >= 65536.0)
     return fail(MTNLG_ERR_ARG, "dropout_p must be in [0, 1)");
   const mtnlg_layer_desc& L = sd->layer;
@@ -65,10 +80,48 @@ void layer_offsets(const StageDims& d, int layer, int64_t off[2][kTensors]) {
   }
 }
 
+// Batched weight gradients (saved tensors kept, per_micro_batch_grads = 0):
+// per layer and half, each saved field, the half's output gradient, its dU
+// or dQKV and its LayerNorm partial rows, every micro-batch's copy of a field
+// back to back, so that a weight gradient is one product over mb * T rows.
+// Off when a batched operand would reach the GEMM's 2 GiB operand bound.
+bool stage_batched(const mtnlg_stage_desc* sd) {
+  if (sd->recompute || sd->per_micro_batch_grads) return false;
+  SavedSizes z;
+  if (half_saved_sizes(&sd->layer, MTNLG_ATTN, &z) != MTNLG_OK) return false;
+  const int64_t T = (int64_t)sd->layer.batch * sd->layer.seq;
+  return (int64_t)sd->micro_batches * T * (int64_t)z.widest < ((int64_t)1 << 31);
+}
+
+struct HalfBlock {  // byte offsets within one (layer, half) block of the batched region
+  size_t ln_out, mean, rstd, a, b, c, dy, g, lnp, total;
+  SavedSizes sz;
+};
+
+HalfBlock half_block(const mtnlg_stage_desc* sd, int half) {
+  HalfBlock B{};
+  half_saved_sizes(&sd->layer, half, &B.sz);
+  const size_t mb = (size_t)sd->micro_batches;
+  const size_t act = (size_t)sd->layer.batch * sd->layer.seq * sd->layer.hidden * 2;
+  size_t p = 0;
+  B.ln_out = p; p += align256(mb * B.sz.ln_out);
+  B.mean = p;   p += align256(mb * B.sz.stats);
+  B.rstd = p;   p += align256(mb * B.sz.stats);
+  B.a = p;      p += align256(mb * B.sz.a);
+  B.b = p;      p += align256(mb * B.sz.b);
+  B.c = p;      p += align256(mb * B.sz.c);
+  B.dy = p;     p += align256(mb * act);
+  B.g = p;      p += align256(mb * B.sz.g);
+  B.lnp = p;    p += align256(mb * B.sz.lnp);
+  B.total = p;
+  return B;
+}
+
 // Workspace regions, each on a 256-byte boundary.
 struct StageWs {
-  size_t adam, xin, mid, part, g1, g2, dz, saved, layer, total;
+  size_t adam, xin, mid, part, g1, g2, dz, saved, layer, wg, total;
   size_t saved_a, saved_m;  // bytes of one layer's saved tensors per half
+  size_t block[2];          // batched: bytes of one layer's block per half
 };
 
 StageWs stage_ws(const mtnlg_stage_desc* sd, const StageDims& d, int64_t n) {
@@ -93,7 +146,18 @@ StageWs stage_ws(const mtnlg_stage_desc* sd, const StageDims& d, int64_t n) {
   w.dz = p;  // the masked gradient a half's backward starts from (dropout only)
   p += sd->dropout_p > 0.0f ? act : 0;
   w.saved = p;  // every layer's saved tensors, or one scratch set when recomputing
-  p += sd->recompute ? std::max(w.saved_a, w.saved_m) : (w.saved_a + w.saved_m) * (size_t)sd->layers;
+  const bool batched = stage_batched(sd);
+  if (batched) {
+    // every layer's and micro-batch's, as per-(layer, half) blocks
+    for (int half = 0; half < 2; ++half) w.block[half] = half_block(sd, half).total;
+    p += (w.block[0] + w.block[1]) * (size_t)sd->layers;
+  } else {
+    p += sd->recompute ? std::max(w.saved_a, w.saved_m) : (w.saved_a + w.saved_m) * (size_t)sd->layers;
+  }
+  w.wg = p;  // the weight-gradient products' and column sums' scratch (batched)
+  if (batched)
+    p += align256(std::max(half_weight_grads_ws_bytes(L, MTNLG_ATTN, sd->micro_batches),
+                           half_weight_grads_ws_bytes(L, MTNLG_MLP, sd->micro_batches)));
   w.layer = p;
   const size_t lw = sd->recompute
                         ? std::max(mtnlg_recompute_workspace_bytes(L, MTNLG_ATTN),
@@ -192,7 +256,7 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
   // micro-batches; the next micro-batch's backward of that layer waits for it.
   const int nl = desc->layers, mb = desc->micro_batches;
   hipStream_t S = static_cast<hipStream_t>(stream), A = static_cast<hipStream_t>(aux_stream);
-  const bool overlap = A != nullptr && A != S && mb > 1;
+  const bool overlap = A != nullptr && A != S && mb > 1 && !stage_batched(desc);
   hipEvent_t* events = nullptr;
   if (overlap) MTNLG_HIP(t_events.get(nl, &events), "hipEventCreateWithFlags");
   hipEvent_t* const bwd_done = events;
@@ -230,6 +294,107 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
     if (desc->recompute) return base + W.saved;
     return base + W.saved + (size_t)l * (W.saved_a + W.saved_m) + (half == MTNLG_MLP ? W.saved_a : 0);
   };
+
+  if (stage_batched(desc)) {
+    // ---- batched weight gradients ----
+    const HalfBlock HB[2] = {half_block(desc, MTNLG_ATTN), half_block(desc, MTNLG_MLP)};
+    auto block = [&](int l, int half) -> char* {
+      return base + W.saved + (size_t)l * (W.block[0] + W.block[1]) + (half == MTNLG_MLP ? W.block[0] : 0);
+    };
+    auto fields = [&](int l, int half, int k) -> SavedPtrs {  // micro-batch k's saved tensors
+      const HalfBlock& B = HB[half];
+      char* b = block(l, half);
+      SavedPtrs S;
+      S.ln_out = b + B.ln_out + (size_t)k * B.sz.ln_out;
+      S.mean = reinterpret_cast<float*>(b + B.mean + (size_t)k * B.sz.stats);
+      S.rstd = reinterpret_cast<float*>(b + B.rstd + (size_t)k * B.sz.stats);
+      S.a = b + B.a + (size_t)k * B.sz.a;
+      S.b = b + B.b + (size_t)k * B.sz.b;
+      S.c = half == MTNLG_ATTN ? reinterpret_cast<float*>(b + B.c + (size_t)k * B.sz.c) : nullptr;
+      return S;
+    };
+    // the half's output gradient as its weight gradients use it (after the
+    // dropout backward); without dropout it is the residual-path gradient
+    // itself, which the previous half's partial sum writes there directly
+    // (the top layer's MLP half: the caller's dy)
+    auto dy_kept = [&](int l, int half) -> char* {
+      if (!drop && l == nl - 1 && half == MTNLG_MLP) return static_cast<char*>(const_cast<void*>(dy));
+      return block(l, half) + HB[half].dy;
+    };
+    char* wgws = base + W.wg;
+    for (int k = 0; k < mb; ++k) {
+      for (int l = 0; l < nl; ++l) {
+        int64_t o[2][kTensors];
+        layer_offsets(d, l, o);
+        const void* in[2] = {xin(l, k), mid(l)};
+        void* out[2] = {mid(l), xout(l, k)};
+        const mtnlg_layer_desc Lk = layer_of(k, l);
+        for (int half = 0; half < 2; ++half) {
+          const int64_t* t = o[half];
+          const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
+          STAGE_CALL(half_fwd(&Lk, half, &p, in[half], part, fields(l, half, k), lws, S));
+          const void* parts[1] = {part};
+          if (drop) {
+            const mtnlg_dropout dr = {desc->dropout_seed, site(k, l, half), desc->dropout_p};
+            STAGE_CALL(mtnlg_reduce_partials_dropout(d.T, d.h, MTNLG_BF16, parts, 1, in[half], wb + 2 * t[5], &dr,
+                                                     out[half], stream));
+          } else {
+            STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, in[half], wb + 2 * t[5], out[half],
+                                             stream));
+          }
+        }
+      }
+      const void* gcur = static_cast<const char*>(dy) + (size_t)k * act;
+      for (int l = nl - 1; l >= 0; --l) {
+        int64_t o[2][kTensors];
+        layer_offsets(d, l, o);
+        const void* in[2] = {xin(l, k), mid(l)};
+        const mtnlg_layer_desc Lk = layer_of(k, l);
+        for (int half = 1; half >= 0; --half) {
+          const int64_t* t = o[half];
+          const mtnlg_half_params p = {wb + 2 * t[0], wb + 2 * t[1], wb + 2 * t[2], wb + 2 * t[3], wb + 2 * t[4]};
+          const void* dyh = gcur;
+          if (drop) {
+            const mtnlg_dropout dr = {desc->dropout_seed, site(k, l, half), desc->dropout_p};
+            void* dz = dy_kept(l, half) + (size_t)k * act;
+            STAGE_CALL(mtnlg_dropout_bwd(d.T, d.h, MTNLG_BF16, gcur, &dr, dz, stream));
+            dyh = dz;
+          }
+          const HalfBlock& B = HB[half];
+          STAGE_CALL(half_bwd_data(&Lk, half, &p, in[half], fields(l, half, k), dyh, part,
+                                   block(l, half) + B.g + (size_t)k * B.sz.g,
+                                   reinterpret_cast<float*>(block(l, half) + B.lnp + (size_t)k * B.sz.lnp), lws, S));
+          // dx of the half = dy (residual path) + the slice's partial, written
+          // where the next half keeps its output gradient
+          void* dst;
+          if (half == MTNLG_MLP)
+            dst = drop ? g1 : dy_kept(l, MTNLG_ATTN) + (size_t)k * act;
+          else if (l == 0)
+            dst = static_cast<char*>(dx) + (size_t)k * act;
+          else
+            dst = drop ? g2 : dy_kept(l - 1, MTNLG_MLP) + (size_t)k * act;
+          const void* parts[1] = {part};
+          STAGE_CALL(mtnlg_reduce_partials(d.T, d.h, MTNLG_BF16, parts, 1, gcur, nullptr, dst, stream));
+          gcur = dst;
+        }
+        if (k == mb - 1) {
+          // layer l's every micro-batch is through its backward: its weight,
+          // bias and LayerNorm gradients, each over mb * T rows
+          for (int half = 1; half >= 0; --half) {
+            const int64_t* t = o[half];
+            const mtnlg_half_grads g = {gb + 2 * t[0], gb + 2 * t[1], gb + 2 * t[2],
+                                        gb + 2 * t[3], gb + 2 * t[4], gb + 2 * t[5]};
+            const HalfBlock& B = HB[half];
+            STAGE_CALL(half_weight_grads(L, half, mb, fields(l, half, 0), dy_kept(l, half), block(l, half) + B.g,
+                                         reinterpret_cast<const float*>(block(l, half) + B.lnp), &g, wgws, S));
+          }
+        }
+      }
+    }
+    STAGE_CALL(mtnlg_grad_accumulate_norm(n, MTNLG_BF16, grad, acc, true, cfg->inv_loss_scale, base + W.adam,
+                                          W.xin - W.adam, stream));
+    return mtnlg_adam_update(cfg, n, master, m, v, acc, w, stats, base + W.adam, W.xin - W.adam, stream);
+  }
 
   for (int k = 0; k < desc->micro_batches; ++k) {
     for (int l = 0; l < desc->layers; ++l) {

@@ -219,8 +219,8 @@ def test_other_entry_points_validate():
     assert L.mtnlg_attention_bwd(_lib.BF16, 1, 128, 2, 128, A, A, A, A, A, A, 0, None) == -5
 
 
-def _stage(layers=3, mb=4, recompute=0, **kw):
-    return _lib.StageDesc(desc(**kw), layers, mb, recompute)
+def _stage(layers=3, mb=4, recompute=0, per_mb=1, **kw):
+    return _lib.StageDesc(desc(**kw), layers, mb, recompute, 0.0, 0, per_mb)
 
 
 def test_stage_layout_follows_header():
@@ -260,6 +260,16 @@ def test_stage_workspace_and_validation():
     dr = _stage()
     dr.dropout_p = 0.1
     assert L.mtnlg_stage_workspace_bytes(ctypes.byref(dr)) == want + act        # the masked-gradient buffer
+    # batched weight gradients (the default): every micro-batch's saved tensors,
+    # output gradients (dy and dU or dQKV) and LayerNorm partial rows are kept
+    bt = _stage(per_mb=0)
+    mb, T, h, wl, fl = 4, 2048, 20480, 16 * 160, 10240
+    kept = 3 * mb * ((sa + sm) + 2 * act + T * (3 * wl + fl) * 2)
+    got_bt = L.mtnlg_stage_workspace_bytes(ctypes.byref(bt))
+    assert kept < got_bt < kept + want + (1 << 30), (got_bt, kept)
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(_stage(per_mb=2))) == 0
+    # recompute ignores the flag
+    assert L.mtnlg_stage_workspace_bytes(ctypes.byref(_stage(recompute=1, per_mb=0))) == want_rc
     # invalid descriptors
     bad = _stage()
     bad.dropout_p = 1.0

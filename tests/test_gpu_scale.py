@@ -393,12 +393,15 @@ def test_stage_full_shard_matches_layer_calls():
     to the same work done through the individual layer, partial-sum, accumulation
     and optimizer entry points: checks the stage's flat layout, buffer chaining
     and accumulation order at the real size (the layers themselves are checked
-    against the oracle in test_gpu_layer.py)."""
+    against the oracle in test_gpu_layer.py). The default schedule (weight
+    gradients once over both micro-batches' rows) then gives the same outputs
+    and input gradients bit for bit, and the same gradient, norm and update up
+    to the rounding of the per-micro-batch gradients to bf16."""
     w = WORKLOADS[7]
     L, MB = w.extra["layers"], 2
     dev = torch.device("cuda:0")
     ld = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, w.tp, 0, tst.BF16, 1e-5)
-    sd = tst.make_stage_desc(ld, L, MB, False)
+    sd = tst.make_stage_desc(ld, L, MB, False, per_micro_batch_grads=True)
     n = tst.stage_param_count(sd)
     assert n == 1_887_859_200
     offs = tst.stage_param_offsets(sd)
@@ -489,6 +492,32 @@ def test_stage_full_shard_matches_layer_calls():
                        ("master", res["master"], master2), ("w", res["w"], w2), ("stats", res["stats"], stats2)):
         assert torch.equal(a, b), name
     print(f"stage full shard: bit-identical; norm {res['stats'][0].item():.6g}", flush=True)
+    del saved, sav, lws, aws, y2, dx2, m2, v2, w2, g2, master2
+    torch.cuda.empty_cache()
+
+    # (3) batched weight gradients
+    sb = tst.make_stage_desc(ld, L, MB, False)
+    master = master0.clone()
+    m.zero_()
+    v.zero_()
+    wt = master0.to(torch.bfloat16)
+    yb = torch.empty_like(x)
+    dxb = torch.empty_like(x)
+    stats.zero_()
+    ws = torch.empty(tst.stage_workspace_bytes(sb), dtype=torch.uint8, device=dev)
+    tst.stage_step(sb, cfg, wt, master, m, v, grad, acc, x, dy, yb, dxb, stats, ws)
+    torch.cuda.synchronize()
+    del ws
+    assert torch.equal(yb, res["y"]) and torch.equal(dxb, res["dx"])
+    starts = sorted(o for lay in offs for half in lay for o in half.values()) + [n]
+    worst = 0.0
+    for lo, hi in zip(starts[:-1], starts[1:]):  # tensor by tensor
+        a_, b_ = acc[lo:hi], res["acc"][lo:hi]
+        worst = max(worst, float((a_ - b_).abs().max() / b_.abs().max().clamp_min(1e-30)))
+    print(f"stage full shard, batched gradients: worst tensor {worst:.3e}", flush=True)
+    assert worst < 2e-2
+    assert abs(stats[0].item() - res["stats"][0].item()) <= 1e-2 * res["stats"][0].item()
+    assert float((master - res["master"]).abs().max()) <= 2.0 * cfg.lr
 
 
 @pytest.mark.parametrize("ta", [0, 1])

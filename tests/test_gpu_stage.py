@@ -10,7 +10,12 @@ Checked:
   (delta p 1e-4, m and v 1e-5, norm 1e-6); the bf16 weights are the GPU
   master rounded to nearest even, bit for bit;
 * the recompute schedule, and the accumulation overlapped on a second
-  stream, give bit-identical results to the plain schedule;
+  stream, give bit-identical results to the schedule that keeps the saved
+  tensors with per-micro-batch gradients;
+* the default schedule (weight gradients once over all micro-batches' rows)
+  gives bit-identical stage outputs and input gradients, its accumulated
+  gradient passes the same oracle check, and the Adam step is checked on it
+  as on the other;
 * all of it without dropout, with dropout (p = 0.15) on every half's
   output, and with dropout on the attention probabilities as well (rate 0.1,
   each layer and micro-batch with its own site), the masks drawn by the GPU
@@ -53,8 +58,8 @@ def _setup():
     return w, L, MB, ld, halves, full, xs, gs
 
 
-def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0, aux=False):
-    sd = tst.make_stage_desc(ld, L, MB, recompute, p, seed)
+def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0, aux=False, per_mb=True):
+    sd = tst.make_stage_desc(ld, L, MB, recompute, p, seed, per_micro_batch_grads=per_mb)
     n = tst.stage_param_count(sd)
     offs = tst.stage_param_offsets(sd)
     flat = np.zeros(n, dtype=np.float32)
@@ -108,6 +113,11 @@ def test_stage_step_against_oracle_and_recompute(p, pa):
     ovl, *_ = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed, aux=True)
     for k in got:
         assert np.array_equal(got[k], ovl[k]), f"second stream differs in {k}"
+    # batched weight gradients: the same forward and input gradients, bit for
+    # bit; the gradients and the step are checked against the oracle below
+    bat, *_ = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed, aux=True, per_mb=False)
+    for k in ("y", "dx"):
+        assert np.array_equal(got[k], bat[k]), f"batched gradients change {k}"
 
     sh = OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=1)
     ys, dxs, flats = OS.stage_micro_batches(sh, [{k: v.astype(np.float64) for k, v in q.items()} for q in full],
@@ -119,26 +129,28 @@ def test_stage_step_against_oracle_and_recompute(p, pa):
         errs[f"dx{k}"] = rel_inf(got["dx"][k], dxs[k])
     acc_ref = OA.accumulate(flats)
     # the oracle's flat order is the documented layout: check it tensor by tensor
-    pos = 0
-    for l in range(L):
-        for h, keys in enumerate((ATTN_KEYS, MLP_KEYS)):
-            for k, fk in keys.items():
-                size = full[l][fk].size
-                assert offs[l][h][k] == pos, (l, h, k)
-                errs[f"acc{l}.{fk}"] = rel_inf(got["acc"][pos:pos + size], acc_ref[pos:pos + size])
-                pos += size
+    for tag, run in (("", got), ("batched ", bat)):
+        pos = 0
+        for l in range(L):
+            for h, keys in enumerate((ATTN_KEYS, MLP_KEYS)):
+                for k, fk in keys.items():
+                    size = full[l][fk].size
+                    assert offs[l][h][k] == pos, (l, h, k)
+                    errs[f"{tag}acc{l}.{fk}"] = rel_inf(run["acc"][pos:pos + size], acc_ref[pos:pos + size])
+                    pos += size
     worst = max(errs, key=errs.get)
     print(f"stage parity: worst {worst} {errs[worst]:.3e}", flush=True)
     for k, e in errs.items():
         assert e < 2e-2, f"{k}: {e:.3e}"
 
-    rp, rm, rv, rw, (norm, coef, inf) = OA.adam_step(flat.astype(np.float64), m0.astype(np.float64),
-                                                    v0.astype(np.float64), got["acc"].astype(np.float64), cfg)
-    assert not inf and got["stats"][2] == 0.0
-    assert coef < 1.0, "clipping should be active"
-    assert abs(got["stats"][0] - norm) <= 1e-6 * norm
-    assert abs(got["stats"][1] - coef) <= 1e-6
-    assert rel_inf(got["master"] - flat, rp - flat) < 1e-4
-    assert rel_inf(got["m"], rm) < 1e-5
-    assert rel_inf(got["v"], rv) < 1e-5
-    assert_bf16_copy(got["w"], got["master"], rw, rp)
+    for run in (got, bat):
+        rp, rm, rv, rw, (norm, coef, inf) = OA.adam_step(flat.astype(np.float64), m0.astype(np.float64),
+                                                        v0.astype(np.float64), run["acc"].astype(np.float64), cfg)
+        assert not inf and run["stats"][2] == 0.0
+        assert coef < 1.0, "clipping should be active"
+        assert abs(run["stats"][0] - norm) <= 1e-6 * norm
+        assert abs(run["stats"][1] - coef) <= 1e-6
+        assert rel_inf(run["master"] - flat, rp - flat) < 1e-4
+        assert rel_inf(run["m"], rm) < 1e-5
+        assert rel_inf(run["v"], rv) < 1e-5
+        assert_bf16_copy(run["w"], run["master"], rw, rp)
