@@ -304,14 +304,14 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
     auto fields = [&](int l, int half, int k) -> SavedPtrs {  // micro-batch k's saved tensors
       const HalfBlock& B = HB[half];
       char* b = block(l, half);
-      SavedPtrs S;
-      S.ln_out = b + B.ln_out + (size_t)k * B.sz.ln_out;
-      S.mean = reinterpret_cast<float*>(b + B.mean + (size_t)k * B.sz.stats);
-      S.rstd = reinterpret_cast<float*>(b + B.rstd + (size_t)k * B.sz.stats);
-      S.a = b + B.a + (size_t)k * B.sz.a;
-      S.b = b + B.b + (size_t)k * B.sz.b;
-      S.c = half == MTNLG_ATTN ? reinterpret_cast<float*>(b + B.c + (size_t)k * B.sz.c) : nullptr;
-      return S;
+      SavedPtrs f;
+      f.ln_out = b + B.ln_out + (size_t)k * B.sz.ln_out;
+      f.mean = reinterpret_cast<float*>(b + B.mean + (size_t)k * B.sz.stats);
+      f.rstd = reinterpret_cast<float*>(b + B.rstd + (size_t)k * B.sz.stats);
+      f.a = b + B.a + (size_t)k * B.sz.a;
+      f.b = b + B.b + (size_t)k * B.sz.b;
+      f.c = half == MTNLG_ATTN ? reinterpret_cast<float*>(b + B.c + (size_t)k * B.sz.c) : nullptr;
+      return f;
     };
     // the half's output gradient as its weight gradients use it (after the
     // dropout backward); without dropout it is the residual-path gradient
