@@ -43,9 +43,10 @@ ATTN_KEYS = {"ln_g": "ln1_g", "ln_b": "ln1_b", "w_in": "w_qkv", "b_in": "b_qkv",
 MLP_KEYS = {"ln_g": "ln2_g", "ln_b": "ln2_b", "w_in": "w_a", "b_in": "b_a", "w_out": "w_b", "b_out": "b_b"}
 
 
-def _setup():
+def _setup(L=None, MB=None):
     w = WORKLOADS[6]
-    L, MB = w.extra["layers"], w.extra["micro_batches"]
+    L = L or w.extra["layers"]
+    MB = MB or w.extra["micro_batches"]
     ld = tst.make_desc(w.batch, w.seq, w.hidden, w.heads, w.ffn, 1, 0, tst.BF16, 1e-5)
     halves = [(make_half_params(w, "attn", 0, layer=l), make_half_params(w, "mlp", 0, layer=l)) for l in range(L)]
     full = []
@@ -119,6 +120,34 @@ def test_stage_step_against_oracle_and_recompute(p, pa):
     for k in ("y", "dx"):
         assert np.array_equal(got[k], bat[k]), f"batched gradients change {k}"
 
+    _against_oracle(w, L, MB, full, xs, gs, p, seed, attn, cfg, flat, m0, v0, offs, {"": got, "batched ": bat})
+
+
+@pytest.mark.parametrize("L,MB,p", [(1, 1, 0.0), (2, 3, 0.15)])
+def test_stage_batched_gradients_edge_shapes(L, MB, p):
+    """The batched-gradient schedule at one layer and one micro-batch (the
+    gradients computed right after the only backward; the top layer is also
+    layer 0) and at two layers and three micro-batches with dropout: outputs
+    and input gradients bit-identical to the per-micro-batch schedule, both
+    against the stage and Adam oracles."""
+    w, L, MB, ld, halves, full, xs, gs = _setup(L, MB)
+    p = float(np.float32(p))
+    seed = 0xBEE5
+    print(f"stage {w.name}: {L} layers, {MB} micro-batches, dropout {p}", flush=True)
+    cfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, max_grad_norm=0.5, inv_loss_scale=1.0,
+                        step=w.extra["step"])
+    got, flat, m0, v0, offs = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed)
+    bat, *_ = _run(w, L, MB, ld, halves, xs, gs, False, cfg, p, seed, per_mb=False)
+    for k in ("y", "dx"):
+        assert np.array_equal(got[k], bat[k]), f"batched gradients change {k}"
+    _against_oracle(w, L, MB, full, xs, gs, p, seed, None, cfg, flat, m0, v0, offs, {"": got, "batched ": bat})
+
+
+def _against_oracle(w, L, MB, full, xs, gs, p, seed, attn, cfg, flat, m0, v0, offs, runs):
+    """Every run's outputs, input gradients and accumulated gradient against the
+    stage oracle (2e-2), and its Adam step against the Adam oracle applied to
+    its own accumulator."""
+    got = runs[""] if "" in runs else next(iter(runs.values()))
     sh = OL.LayerShape(batch=w.batch, seq=w.seq, hidden=w.hidden, heads=w.heads, ffn=w.ffn, tp=1)
     ys, dxs, flats = OS.stage_micro_batches(sh, [{k: v.astype(np.float64) for k, v in q.items()} for q in full],
                                             [x.astype(np.float64) for x in xs], [g.astype(np.float64) for g in gs],
@@ -129,7 +158,7 @@ def test_stage_step_against_oracle_and_recompute(p, pa):
         errs[f"dx{k}"] = rel_inf(got["dx"][k], dxs[k])
     acc_ref = OA.accumulate(flats)
     # the oracle's flat order is the documented layout: check it tensor by tensor
-    for tag, run in (("", got), ("batched ", bat)):
+    for tag, run in runs.items():
         pos = 0
         for l in range(L):
             for h, keys in enumerate((ATTN_KEYS, MLP_KEYS)):
@@ -143,7 +172,7 @@ def test_stage_step_against_oracle_and_recompute(p, pa):
     for k, e in errs.items():
         assert e < 2e-2, f"{k}: {e:.3e}"
 
-    for run in (got, bat):
+    for run in runs.values():
         rp, rm, rv, rw, (norm, coef, inf) = OA.adam_step(flat.astype(np.float64), m0.astype(np.float64),
                                                         v0.astype(np.float64), run["acc"].astype(np.float64), cfg)
         assert not inf and run["stats"][2] == 0.0
