@@ -187,8 +187,9 @@ AttnDropout attn_dropout(const mtnlg_layer_desc* desc, const Dims& d) {
   return a;
 }
 
-// The forward of one half into `saved`; the row-sliced output GEMM is
-// skipped when y_partial is NULL (a recompute needs only what is saved).
+// The forward of one half into its saved tensors S; the row-sliced output
+// GEMM is skipped when y_partial is NULL (a recompute needs only what is
+// saved).
 int forward_into(const mtnlg_layer_desc* desc, const Dims& d, int half, const mtnlg_half_params* params,
                  const void* x, void* y_partial, const SavedPtrs& S, void* gws, hipStream_t st) {
   void* ln_out = S.ln_out;
