@@ -299,6 +299,11 @@ __device__ __forceinline__ void epilogue256(const GemmArgs& p, f32x16_t (&acc)[F
                                            Mid&& mid) {
   static_assert(TN == 64, "lane columns assume 64-column wave blocks");
   constexpr int TM = FM * 32;
+  // Opaque lane id: the slab and store offsets below depend only on the lane
+  // and wave, and without this the compiler computes them once per kernel and
+  // keeps them live across every item's K loop (up to 14 of them spilled, and
+  // each reload waited for all stores in flight).
+  asm volatile("" : "+v"(lane));
   const int lrow = lane & 31, lg = lane >> 5;
   const int rr = lane >> 3, cc = (lane & 7) * 8;
   const int col = n0 + wn * TN + cc;
