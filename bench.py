@@ -166,7 +166,7 @@ def main():
     fwd_dense = shard_fwd_flops(T, h, w.local_heads, w.head_dim, fl, w.seq, w.batch, causal=False)
 
     # ---- GPU clock and power while the step runs (not part of the timed region) ----
-    clocks = None if args.no_clock else clock_sample(torch, step, ms)
+    clocks = None if args.no_clock else clock_sample(torch, step, ms, settle=1.0)
     if clocks and clocks["gfx_clock_mhz"]:
         peak_at_clock = PEAK_BF16_TFLOPS * clocks["gfx_clock_mhz"] / 2400.0
         clocks["mfma_peak_frac_at_clock"] = round(tflops / peak_at_clock, 4)
@@ -352,11 +352,17 @@ def smi_sample():
         return None
 
 
-def clock_sample(torch, step, ms_step, seconds=1.5):
+def clock_sample(torch, step, ms_step, seconds=1.5, settle=0.0):
     """Runs the step back to back for about `seconds` while amdsmi is polled from a
-    second thread; the medians of the samples taken while the GPU is busy."""
+    second thread; the medians of the samples taken while the GPU is busy. With
+    `settle` > 0 the step first runs that many seconds unsampled: the driver's
+    clock and power readings trail the load by up to about a second, so a
+    window right after a change of workload reads the previous one."""
     import threading
     samples, stop = [], threading.Event()
+    if settle > 0:
+        for _ in range(max(1, int(settle * 1e3 / ms_step))):
+            step()
 
     def poll():
         while not stop.is_set():
@@ -548,7 +554,7 @@ def gemm_power_probe(torch, tst, dev, T, h, fl, reps=20):
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / reps
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        ck = clock_sample(torch, run, ms, seconds=1.0) or {}
+        ck = clock_sample(torch, run, ms, seconds=1.0, settle=1.5) or {}
         row = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                "gfx_clock_mhz": ck.get("gfx_clock_mhz"), "socket_power_w": ck.get("socket_power_w")}
         if ck.get("gfx_clock_mhz"):
