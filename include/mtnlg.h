@@ -409,15 +409,18 @@ size_t mtnlg_stage_workspace_bytes(const mtnlg_stage_desc* desc);
  * LayerNorm partial sums; after the last micro-batch's backward of a layer,
  * that layer's weight gradients are single products over micro_batches * T
  * rows (fp32 accumulation inside the product, one bf16 rounding into grad)
- * and its bias and LayerNorm gradients single column sums; acc is then
- * overwritten by grad with the norm pass. Either way mtnlg_adam_update with
- * cfg follows.
+ * and its bias and LayerNorm gradients single column sums; the norm pass
+ * and the update then read grad as it is (no fp32 copy: 6 bytes per
+ * parameter less traffic, and the same result bit for bit as overwriting acc
+ * with grad through mtnlg_grad_accumulate_norm and updating from acc).
+ * Either way the update is mtnlg_adam_update's, with cfg.
  *   w       [n] bf16 flat weights; read by every layer and rewritten by the
  *           step as bf16(master)
  *   master, m, v  [n] f32 optimizer state (updated in place)
  *   grad    [n] bf16 scratch: one micro-batch's gradient (batched: the sum over
  *           all micro-batches)
- *   acc     [n] f32: the accumulated gradient (left holding it)
+ *   acc     [n] f32: per-micro-batch gradients: the accumulated gradient (left
+ *           holding it); batched gradients: not used (left untouched)
  *   x       [micro_batches, T, h] bf16: stage input (T = batch * seq)
  *   dy      [micro_batches, T, h] bf16: gradient of the stage output
  *   y       [micro_batches, T, h] bf16: stage output, written

@@ -240,8 +240,8 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
   STAGE_CALL(stage_dims(desc, &d));
   const int64_t n = d.per_layer * desc->layers;
   // everything is checked before the first launch
-  AdamScalars unused;
-  STAGE_CALL(adam_args(cfg, n, master, m, v, acc, w, stats, ws, ws_bytes, &unused));
+  AdamScalars sc;
+  STAGE_CALL(adam_args(cfg, n, master, m, v, acc, w, stats, ws, ws_bytes, &sc));
   CHECK_PTR(grad);
   CHECK_PTR(x);
   CHECK_PTR(dy);
@@ -391,9 +391,12 @@ int mtnlg_stage_step(const mtnlg_stage_desc* desc, const mtnlg_adam_cfg* cfg, vo
         }
       }
     }
-    STAGE_CALL(mtnlg_grad_accumulate_norm(n, MTNLG_BF16, grad, acc, true, cfg->inv_loss_scale, base + W.adam,
-                                          W.xin - W.adam, stream));
-    return mtnlg_adam_update(cfg, n, master, m, v, acc, w, stats, base + W.adam, W.xin - W.adam, stream);
+    // grad holds the whole step's gradient: the norm pass and the update read
+    // it as it is (acc is left untouched; an fp32 copy would only add 6 bytes
+    // per parameter of traffic for the same values)
+    MTNLG_HIP(grad_norm_bf16(n, grad, cfg->inv_loss_scale, base + W.adam, S), "grad_norm_bf16");
+    MTNLG_HIP(adam_update_bf16(sc, n, master, m, v, grad, w, stats, base + W.adam, S), "adam_update_bf16");
+    return MTNLG_OK;
   }
 
   for (int k = 0; k < desc->micro_batches; ++k) {

@@ -51,6 +51,16 @@ __device__ __forceinline__ float4 ld_nt(const float4* p) {
   const nf4_t v = __builtin_nontemporal_load(reinterpret_cast<const nf4_t*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
 }
+// four gradient values from a 16-byte (fp32) or 8-byte (bf16) group
+__device__ __forceinline__ float4 ld4_nt(const float* g, int64_t u) {
+  return ld_nt(reinterpret_cast<const float4*>(g) + u);
+}
+__device__ __forceinline__ float4 ld4_nt(const bf16_t* g, int64_t u) {
+  typedef unsigned int nu2_t __attribute__((ext_vector_type(2)));
+  const nu2_t w = __builtin_nontemporal_load(reinterpret_cast<const nu2_t*>(g) + u);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u));
+}
 __device__ __forceinline__ void st_nt(float4* p, const float4& v) {
   const nf4_t w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<nf4_t*>(p));
@@ -176,8 +186,10 @@ __global__ __launch_bounds__(kStreamThreads) void dropout_bwd_kernel(int64_t tot
 // acc = (overwrite ? 0 : acc) + grad. With NORM the same pass also leaves, per
 // workgroup, the fp64 sum of (acc * s)^2 over the elements it wrote and a
 // non-finite flag: the norm pass of the optimizer folded into the last
-// micro-batch's accumulation, one fewer read of the accumulator.
-template <typename T, bool NORM>
+// micro-batch's accumulation, one fewer read of the accumulator. Without
+// STORE (overwrite only) nothing is written but those partials: the norm pass
+// over a gradient that the update then reads as it is.
+template <typename T, bool NORM, bool STORE = true>
 __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, const T* __restrict__ g,
                                                                   float* __restrict__ acc, int overwrite, float s,
                                                                   double* __restrict__ part,
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, con
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[k][e] += a[k][e];
         }
-        store8(acc + u * 8, v[k]);
+        if (STORE) store8(acc + u * 8, v[k]);
         if (NORM) {
           double q[8];
 #pragma unroll
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(kStreamThreads) void grad_acc_kernel(int64_t n, con
   for (int64_t i = units * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += s1) {
     const float v = Elem<T>::to_f(g[i]);
     const float r = overwrite ? v : acc[i] + v;
-    acc[i] = r;
+    if (STORE) acc[i] = r;
     if (NORM) {
       const float t = r * s;
       bad |= !isfinite(t);
@@ -325,11 +337,13 @@ __device__ __forceinline__ void adam_one(float& p, float& m, float& v, float g, 
   p -= c.lr * mhat / (sqrtf(vhat) + c.eps);
 }
 
-// (3) the update; reads found_inf and coef written by (2) on the same stream
+// (3) the update; reads found_inf and coef written by (2) on the same stream.
+// G: the gradient's type (fp32 accumulator, or a bf16 gradient read as it is)
+template <typename G>
 __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars c, int64_t n,
                                                                      float* __restrict__ master, float* __restrict__ m,
                                                                      float* __restrict__ v,
-                                                                     const float* __restrict__ grad,
+                                                                     const G* __restrict__ grad,
                                                                      bf16_t* __restrict__ w,
                                                                      const float* __restrict__ stats) {
   if (stats[2] != 0.0f) return;
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars
     float4 p = ld_nt(reinterpret_cast<const float4*>(master) + u);
     float4 mm = ld_nt(reinterpret_cast<const float4*>(m) + u);
     float4 vv = ld_nt(reinterpret_cast<const float4*>(v) + u);
-    const float4 g = ld_nt(reinterpret_cast<const float4*>(grad) + u);
+    const float4 g = ld4_nt(grad, u);
     adam_one(p.x, mm.x, vv.x, g.x * gs, c);
     adam_one(p.y, mm.y, vv.y, g.y * gs, c);
     adam_one(p.z, mm.z, vv.z, g.z * gs, c);
@@ -355,7 +369,7 @@ __global__ __launch_bounds__(kStreamThreads) void adam_update_kernel(AdamScalars
   }
   for (int64_t i = n4 * 4 + t0; i < n; i += stride) {
     float p = master[i], mm = m[i], vv = v[i];
-    adam_one(p, mm, vv, grad[i] * gs, c);
+    adam_one(p, mm, vv, Elem<G>::to_f(grad[i]) * gs, c);
     master[i] = p;
     m[i] = mm;
     v[i] = vv;
@@ -499,7 +513,8 @@ hipError_t grad_accumulate_norm(int64_t n, int dtype, const void* grad, float* a
 
 namespace {
 // (2) + (3): the finish over nparts partials, then the update
-hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const float* grad,
+template <typename G>
+hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const G* grad,
                              void* w_bf16, float* stats, const double* part, const int* flag, int nparts,
                              hipStream_t st) {
   hipLaunchKernelGGL(adam_finish_kernel, dim3(1), dim3(kStreamThreads), 0, st, part, flag, nparts,
@@ -507,7 +522,7 @@ hipError_t finish_and_update(const AdamScalars& c, int64_t n, float* master, flo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n == 0) return e;
   const int grid = stream_grid(n / 4 + 1, kOneShotBlocks);
-  hipLaunchKernelGGL(adam_update_kernel, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
+  hipLaunchKernelGGL(adam_update_kernel<G>, dim3(grid), dim3(kStreamThreads), 0, st, c, n, master, m, v, grad,
                      static_cast<bf16_t*>(w_bf16), stats);
   return hipGetLastError();
 }
@@ -590,6 +605,23 @@ hipError_t adam_update(const AdamScalars& c, int64_t n, float* master, float* m,
   const double* part = static_cast<const double*>(ws);
   const int* flag = reinterpret_cast<const int*>(part + kOptBlocks);
   return finish_and_update(c, n, master, m, v, grad, w_bf16, stats, part, flag, acc_grid(n), st);
+}
+
+hipError_t grad_norm_bf16(int64_t n, const void* grad, float inv_loss_scale, void* ws, hipStream_t st) {
+  double* part = static_cast<double*>(ws);
+  int* flag = reinterpret_cast<int*>(part + kOptBlocks);
+  // the launch and per-thread order of grad_accumulate_norm: the same partials
+  hipLaunchKernelGGL((grad_acc_kernel<bf16_t, true, false>), dim3(acc_grid(n)), dim3(kStreamThreads), 0, st, n,
+                     static_cast<const bf16_t*>(grad), nullptr, 1, inv_loss_scale, part, flag);
+  return hipGetLastError();
+}
+
+hipError_t adam_update_bf16(const AdamScalars& c, int64_t n, float* master, float* m, float* v, const void* grad,
+                            void* w_bf16, float* stats, const void* ws, hipStream_t st) {
+  const double* part = static_cast<const double*>(ws);
+  const int* flag = reinterpret_cast<const int*>(part + kOptBlocks);
+  return finish_and_update(c, n, master, m, v, static_cast<const bf16_t*>(grad), w_bf16, stats, part, flag,
+                           acc_grid(n), st);
 }
 
 }  // namespace mtnlg

@@ -509,10 +509,13 @@ def test_stage_full_shard_matches_layer_calls():
     torch.cuda.synchronize()
     del ws
     assert torch.equal(yb, res["y"]) and torch.equal(dxb, res["dx"])
+    # batched: the update reads grad (the whole step's gradient) as it is and
+    # leaves acc untouched (still run (1)'s accumulator)
+    assert torch.equal(acc, res["acc"])
     starts = sorted(o for lay in offs for half in lay for o in half.values()) + [n]
     worst = 0.0
     for lo, hi in zip(starts[:-1], starts[1:]):  # tensor by tensor
-        a_, b_ = acc[lo:hi], res["acc"][lo:hi]
+        a_, b_ = grad[lo:hi].float(), res["acc"][lo:hi]
         worst = max(worst, float((a_ - b_).abs().max() / b_.abs().max().clamp_min(1e-30)))
     print(f"stage full shard, batched gradients: worst tensor {worst:.3e}", flush=True)
     assert worst < 2e-2

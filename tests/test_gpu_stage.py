@@ -76,7 +76,8 @@ def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0, aux=False,
     mm = torch.from_numpy(m0).to(dev)
     vv = torch.from_numpy(v0).to(dev)
     grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    # batched gradients leave acc untouched: a sentinel shows it
+    acc = torch.full((n,), 7.0, dtype=torch.float32, device=dev)
     x = torch.from_numpy(np.stack(xs)).to(dev).to(torch.bfloat16)
     dy = torch.from_numpy(np.stack(gs)).to(dev).to(torch.bfloat16)
     y = torch.empty_like(x)
@@ -88,7 +89,11 @@ def _run(w, L, MB, ld, halves, xs, gs, recompute, cfg, p=0.0, seed=0, aux=False,
     aux_stream = torch.cuda.Stream() if aux else None
     tst.stage_step(sd, c, wt, master, mm, vv, grad, acc, x, dy, y, dx, stats, ws, aux_stream=aux_stream)
     torch.cuda.synchronize()
-    out = {"y": y.float().cpu().numpy(), "dx": dx.float().cpu().numpy(), "acc": acc.cpu().numpy(),
+    if not per_mb:
+        assert bool((acc == 7.0).all()), "batched gradients wrote acc"
+    # the step's gradient: acc, or (batched) grad, which the update reads as it is
+    step_grad = acc.cpu().numpy() if per_mb else grad.float().cpu().numpy()
+    out = {"y": y.float().cpu().numpy(), "dx": dx.float().cpu().numpy(), "acc": step_grad,
            "master": master.cpu().numpy(), "m": mm.cpu().numpy(), "v": vv.cpu().numpy(),
            "w": wt.float().cpu().numpy(), "stats": stats.cpu().numpy()}
     return out, flat, m0, v0, offs
