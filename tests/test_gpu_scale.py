@@ -521,6 +521,37 @@ def test_stage_full_shard_matches_layer_calls():
     assert worst < 2e-2
     assert abs(stats[0].item() - res["stats"][0].item()) <= 1e-2 * res["stats"][0].item()
     assert float((master - res["master"]).abs().max()) <= 2.0 * cfg.lr
+    # the batched step's optimizer (a norm pass over the bf16 gradient, then the
+    # update reading it): the norm against an exact float64 pass over the GPU's
+    # own gradient on the host, and the update on sampled parameters (both ends
+    # of every tensor and 8192 seeded ones) against the Adam oracle
+    sq = 0.0
+    piece = 1 << 26
+    for s0 in range(0, n, piece):
+        xg = grad[s0:s0 + piece].float().cpu().numpy().astype(np.float64)
+        sq += float(np.dot(xg, xg))
+    ocfg = OA.AdamConfig(lr=1e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, max_grad_norm=1.0,
+                         inv_loss_scale=1.0, step=3)
+    norm = float(np.sqrt(sq))
+    coef = min(1.0, ocfg.max_grad_norm / (norm + OA.CLIP_EPS))
+    st = stats.cpu().numpy()
+    assert st[2] == 0.0 and coef < 1.0
+    assert abs(st[0] - norm) / norm < 1e-6 and abs(st[1] - coef) / coef < 1e-6
+    rng = np.random.default_rng(7300)
+    idx = np.unique(np.concatenate([rng.choice(n, 8192, replace=False), np.array(starts[:-1]),
+                                    np.array(starts[1:]) - 1]))
+    ti = torch.from_numpy(idx).to(dev)
+    p0 = master0[ti].double().cpu().numpy()
+    g0 = grad[ti].float().double().cpu().numpy()
+    rp, rm, rv, _ = OA.adam_update(p0, np.zeros_like(p0), np.zeros_like(p0), g0, ocfg, coef, False)
+    gp = master[ti].double().cpu().numpy()
+    # master is fp32: besides the update's own error, the stored value rounds to
+    # an ulp of p (6e-8 for the LayerNorm gains near 1, as large as the update)
+    tol = 1e-4 * np.max(np.abs(rp - p0)) + 2.0 ** -23 * np.abs(p0)
+    assert np.all(np.abs(gp - rp) <= tol)
+    assert np.max(np.abs(m[ti].double().cpu().numpy() - rm)) <= 1e-5 * np.max(np.abs(rm))
+    assert np.max(np.abs(v[ti].double().cpu().numpy() - rv)) <= 1e-5 * np.max(np.abs(rv))
+    assert torch.equal(wt[ti], master[ti].to(torch.bfloat16))
 
 
 @pytest.mark.parametrize("ta", [0, 1])
